@@ -1,0 +1,157 @@
+"""CPU oracle for the KDA prefill chunk solver (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path (``tril_solve_amd``)
+never imports, loads or calls it, and it imports nothing from there.
+
+It evaluates the plain definition of what LightLLM PR #1703 ("perf(kda):
+parallelize diagonal solves in Prefill", PR description) computes: for every
+64-token chunk and head, X = (I + A)^-1 with A the strictly-lower intra-chunk
+matrix, by fp64 column forward substitution (``tril_oracle.c``). Inputs in
+float32 or bfloat16 are upcast to float64 exactly before the solve.
+
+Pins (each in ``tests/test_oracle_pins.py``): exact rational Neumann series,
+the single-subdiagonal closed form, LAPACK inversion, the residual of
+(I + A) X = I, the leading-principal-block property for partial chunks,
+hand-derived chunk maps (``tests/golden/``), and RNE against torch's
+bfloat16 cast plus hand-picked ties.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tril_oracle.c")
+_LIB = os.path.join(_HERE, "libtril_oracle.so")
+CHUNK = 64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP). Returns the .so path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.oracle_chunks_packed.restype = i64
+        lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
+        lib.oracle_inv_unit_lower.restype = None
+        lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
+        lib.oracle_tril_inv_packed.restype = i64
+        lib.oracle_tril_inv_packed.argtypes = [p, p, p, i64, i64, i32, ctypes.c_int]
+        lib.oracle_tril_inv_dense.restype = i64
+        lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, i32, ctypes.c_int]
+        lib.oracle_rne_bf16.restype = None
+        lib.oracle_rne_bf16.argtypes = [p, p, i64]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the OpenMP loops use by default (OMP_NUM_THREADS or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of a materialised input to float64.
+
+    ``dtype`` is "f32" (a float32 array) or "bf16" (a uint16/int16 array of
+    bfloat16 bit patterns: the value is those 16 bits followed by 16 zero bits
+    of a binary32).
+    """
+    if dtype == "f32":
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(a).view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.ascontiguousarray(a, dtype=np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def chunks_packed(cu_seqlens) -> np.ndarray:
+    """Chunks of a packed batch: int64 array of rows (seq, start, length)."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = cu.shape[0] - 1
+    lib = _load()
+    n = lib.oracle_chunks_packed(_ptr(cu), nseq, None, None, None, 0)
+    if n < 0:
+        raise ValueError("malformed cu_seqlens")
+    seq = np.zeros(n, np.int64)
+    start = np.zeros(n, np.int64)
+    ln = np.zeros(n, np.int32)
+    lib.oracle_chunks_packed(_ptr(cu), nseq, _ptr(seq), _ptr(start), _ptr(ln), n)
+    return np.stack([seq, start, ln.astype(np.int64)], axis=1)
+
+
+def inv_unit_lower(M: np.ndarray) -> np.ndarray:
+    """(I + M)^-1 for one L x L matrix (only the strictly-lower part of M is
+    read). Returns an L x 64 float64 array: full-width output rows."""
+    M = np.ascontiguousarray(M, dtype=np.float64)
+    L = M.shape[0]
+    if M.ndim != 2 or M.shape[1] < L or L > CHUNK:
+        raise ValueError("M must be L x >=L with L <= 64")
+    X = np.zeros((L, CHUNK), np.float64)
+    _load().oracle_inv_unit_lower(_ptr(M), M.shape[1], L, _ptr(X), CHUNK)
+    return X
+
+
+def tril_inv_packed(A: np.ndarray, cu_seqlens, dtype: str = "f32", nthreads: int = 0,
+                    fill: float = np.nan) -> np.ndarray:
+    """Oracle X for a packed [T, H, 64] input. Rows outside every chunk hold
+    ``fill``."""
+    A64 = to_f64(A, dtype)
+    T, H, C = A64.shape
+    assert C == CHUNK
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    X = np.full((T, H, CHUNK), fill, np.float64)
+    r = _load().oracle_tril_inv_packed(_ptr(A64), _ptr(X), _ptr(cu), cu.shape[0] - 1, T, H,
+                                       nthreads)
+    if r < 0:
+        raise ValueError("malformed packed problem")
+    return X
+
+
+def tril_inv_dense(A: np.ndarray, dtype: str = "f32", nthreads: int = 0) -> np.ndarray:
+    """Oracle X for a dense [B, T, H, 64] input."""
+    A64 = to_f64(A, dtype)
+    B, T, H, C = A64.shape
+    assert C == CHUNK
+    X = np.full((B, T, H, CHUNK), np.nan, np.float64)
+    r = _load().oracle_tril_inv_dense(_ptr(A64), _ptr(X), B, T, H, nthreads)
+    if r < 0:
+        raise ValueError("malformed dense problem")
+    return X
+
+
+def rne_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns the
+    uint16 bit patterns."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = np.empty(bits.shape, np.uint16)
+    _load().oracle_rne_bf16(_ptr(bits), _ptr(out), bits.size)
+    return out

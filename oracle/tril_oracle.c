@@ -1,0 +1,179 @@
+/*
+ * Plain CPU oracle for the KDA prefill chunk solver.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it. It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes (LightLLM PR #1703, "perf(kda): parallelize diagonal solves
+ * in Prefill", PR description, method paragraph): for every 64-token chunk of
+ * every request and every head, the inverse X = (I + A)^-1 of the unit
+ * lower-triangular matrix I + A, where A holds the strictly-lower
+ * intra-chunk entries. The page computes it with four 16x16 diagonal inverses
+ * and a blocked merge; that is only an evaluation order of the same unique
+ * inverse (det(I + A) = 1), so this oracle evaluates the plain definition:
+ * column-by-column forward substitution of (I + A) X = I in double precision,
+ * one chunk-head at a time, with no blocking.
+ *
+ * Readings where the page is silent (each also recorded in the design notes):
+ *  - chunks restart at every request's first token, so a request of length n
+ *    has ceil(n / 64) chunks and only its last one may be partial;
+ *  - only rows i < L of a chunk with L valid tokens exist; the result is the
+ *    L x L inverse, i.e. the leading block of the zero-padded 64x64 one;
+ *  - entries of A on or above the diagonal are ignored (never read);
+ *  - every valid row of X is written in full: 1 on the diagonal, 0 above it
+ *    and in columns >= L;
+ *  - rows that belong to no chunk are not touched.
+ *
+ * Layouts: packed A and X are [T, H, 64] row-major (token, head, column);
+ * dense ones are [B, T, H, 64]. Element (token t, head h, column j) is the
+ * entry (t - chunk_start, j) of that chunk-head's matrix.
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_CHUNK 64
+
+/*
+ * Chunk enumeration of a packed batch (same PR, PR description: the solver
+ * accepts packed varlen batches described by cumulative sequence lengths).
+ * Request s covers tokens [cu[s], cu[s+1]); its chunks start at cu[s] + 64c.
+ * Writes up to `cap` entries and returns the total number of chunks, or -1
+ * when cu is not non-decreasing or cu[0] < 0.
+ */
+int64_t oracle_chunks_packed(const int32_t *cu, int64_t nseq, int64_t *seq_out,
+                             int64_t *start_out, int32_t *len_out, int64_t cap) {
+    int64_t n = 0;
+    if (nseq > 0 && cu[0] < 0) return -1;
+    for (int64_t s = 0; s < nseq; ++s) {
+        int64_t bos = cu[s], eos = cu[s + 1];
+        if (eos < bos) return -1;
+        for (int64_t p = bos; p < eos; p += ORACLE_CHUNK) {
+            int64_t len = eos - p < ORACLE_CHUNK ? eos - p : ORACLE_CHUNK;
+            if (n < cap) {
+                if (seq_out) seq_out[n] = s;
+                if (start_out) start_out[n] = p;
+                if (len_out) len_out[n] = (int32_t)len;
+            }
+            ++n;
+        }
+    }
+    return n;
+}
+
+/*
+ * X = (I + M)^-1 for one L x L matrix, L <= 64. M and X are row-major with
+ * leading dimensions ldm and ldx (in elements). Only M[i][j] with j < i is
+ * read. X is written for rows i < L and columns j < 64 (columns >= L are 0),
+ * matching a full-width output row.
+ *
+ * Column c of X solves (I + M) x = e_c: x_i = 0 for i < c, x_c = 1, and for
+ * i > c, x_i = -sum_{j=c}^{i-1} M[i][j] x_j, summed in increasing j.
+ */
+void oracle_inv_unit_lower(const double *M, int64_t ldm, int L, double *X, int64_t ldx) {
+    double col[ORACLE_CHUNK];
+    for (int i = 0; i < L; ++i)
+        for (int j = 0; j < ORACLE_CHUNK; ++j) X[(int64_t)i * ldx + j] = 0.0;
+    for (int c = 0; c < L; ++c) {
+        for (int i = 0; i < c; ++i) col[i] = 0.0;
+        col[c] = 1.0;
+        for (int i = c + 1; i < L; ++i) {
+            double s = 0.0;
+            for (int j = c; j < i; ++j) s += M[(int64_t)i * ldm + j] * col[j];
+            col[i] = -s;
+        }
+        for (int i = c; i < L; ++i) X[(int64_t)i * ldx + c] = col[i];
+    }
+}
+
+static int oracle_threads(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * Packed layout: A, X are [T, H, 64] doubles; cu has nseq + 1 entries with
+ * cu[nseq] <= T. Returns the number of chunk-head matrices solved, or -1 on a
+ * malformed cu. nthreads <= 0 uses the OpenMP default.
+ */
+int64_t oracle_tril_inv_packed(const double *A, double *X, const int32_t *cu, int64_t nseq,
+                               int64_t T, int32_t H, int nthreads) {
+    if (H <= 0 || nseq < 0) return -1;
+    int64_t nt = oracle_chunks_packed(cu, nseq, NULL, NULL, NULL, 0);
+    if (nt < 0 || (nseq > 0 && cu[nseq] > T)) return -1;
+    int64_t *start = (int64_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int64_t));
+    int32_t *len = (int32_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int32_t));
+    if (!start || !len) { free(start); free(len); return -1; }
+    oracle_chunks_packed(cu, nseq, NULL, start, len, nt);
+    const int64_t rs = (int64_t)H * ORACLE_CHUNK; /* elements between consecutive tokens */
+    const int64_t work = nt * (int64_t)H;
+#pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
+    for (int64_t w = 0; w < work; ++w) {
+        int64_t k = w / H, h = w % H;
+        int64_t off = start[k] * rs + h * ORACLE_CHUNK;
+        oracle_inv_unit_lower(A + off, rs, len[k], X + off, rs);
+    }
+    free(start);
+    free(len);
+    return work;
+}
+
+/*
+ * Dense batch layout (same PR, PR description: the solver also takes dense
+ * [B, T, H] batches): A, X are [B, T, H, 64] doubles; every batch element is
+ * one request of T tokens, so its chunks start at 64c and the last has
+ * T - 64c valid rows. Returns the number of matrices solved.
+ */
+int64_t oracle_tril_inv_dense(const double *A, double *X, int64_t B, int64_t T, int32_t H,
+                              int nthreads) {
+    if (H <= 0 || B < 0 || T < 0) return -1;
+    const int64_t rs = (int64_t)H * ORACLE_CHUNK;
+    const int64_t per_b = (T + ORACLE_CHUNK - 1) / ORACLE_CHUNK;
+    const int64_t work = B * per_b * (int64_t)H;
+#pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
+    for (int64_t w = 0; w < work; ++w) {
+        int64_t h = w % H, k = w / H;
+        int64_t b = k / per_b, c = k % per_b;
+        int64_t row0 = b * T + c * ORACLE_CHUNK;
+        int L = (int)(T - c * ORACLE_CHUNK < ORACLE_CHUNK ? T - c * ORACLE_CHUNK : ORACLE_CHUNK);
+        int64_t off = row0 * rs + h * ORACLE_CHUNK;
+        oracle_inv_unit_lower(A + off, rs, L, X + off, rs);
+    }
+    return work;
+}
+
+/*
+ * Round-to-nearest-even from binary32 to bfloat16. The same PR keeps the
+ * inverse tiles in FP32 through the merge (commit summary), so a bfloat16
+ * output is read as one rounding of the final FP32 value at the store; this is
+ * the CPU side of that rounding, used to check it. bfloat16 is
+ * the upper 16 bits of a binary32; the value is rounded to the nearer of the
+ * two representable neighbours, and a tie goes to the one whose last kept bit
+ * is 0. NaNs stay NaN (quiet bit forced). Overflow rounds to infinity, as the
+ * definition gives.
+ */
+void oracle_rne_bf16(const uint32_t *f32bits, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t b = f32bits[i];
+        if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu) != 0u) {
+            out[i] = (uint16_t)((b >> 16) | 0x0040u);
+            continue;
+        }
+        uint32_t kept = b >> 16;
+        uint32_t rest = b & 0xFFFFu;
+        if (rest > 0x8000u || (rest == 0x8000u && (kept & 1u))) kept += 1u;
+        out[i] = (uint16_t)kept;
+    }
+}
+
+int oracle_num_threads(void) { return oracle_threads(0); }

@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the KDA prefill chunk solver.
+
+This module only draws inputs; it holds none of the solver's arithmetic and
+imports neither the oracle nor the HIP library, both of which consume what it
+makes.
+
+The intra-chunk matrix follows the delta-rule shape that KDA prefill hands to
+the solver: for tokens i > j of one 64-token chunk and one head,
+
+    A[i, j] = -beta_i * sum_d k[i, d] * k[j, d] * exp(g[i, d] - g[j, d])
+
+with k a Gaussian key row L2-normalised over the key dimension (128),
+beta_i = sigmoid(N(0, 1)), and g the within-chunk running sum of
+logsigmoid(N(0, 1) + 3) per channel. Since g decreases along the chunk,
+exp(g_i - g_j) <= 1 for i > j and |A[i, j]| <= beta_i < 1.
+
+Randomness: chunk number n (counted in packed order over all requests) draws
+from ``numpy.random.default_rng([seed, n])``: first k [L, H, K], then the
+decay logits [L, H, K], then the beta logits [L, H]. Each chunk is therefore
+reproducible on its own, and chunks can be generated in parallel.
+
+The product k_i . k_j weighted by exp(g_i - g_j) is evaluated in float64 as
+(k_i * exp(g_i)) . (k_j * exp(-g_j)); with |g| below a few tens this is as
+accurate as the direct form, and A is rounded once to float32 at the end.
+bfloat16 inputs are rounded from that float32 array by torch's CPU cast.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+CHUNK = 64
+KEY_DIM = 128
+
+# The five workloads: name -> layout, request lengths (or dense B, T), heads,
+# input and output dtypes, data seed.
+CONFIGS = {
+    "c1_packed_1x64_h64_f32": dict(layout="packed", lengths=[64], H=64, a_dtype="f32",
+                                   x_dtype="f32", seed=0),
+    "c2_dense_b4_t512_h16_bf16_f32": dict(layout="dense", B=4, T=512, H=16, a_dtype="bf16",
+                                          x_dtype="f32", seed=1),
+    "c3_packed_16x512_h64_f32": dict(layout="packed", lengths=[512] * 16, H=64, a_dtype="f32",
+                                     x_dtype="f32", seed=2),
+    "c4_packed_ragged48_h64_f32_bf16": dict(layout="packed", lengths="ragged48", H=64,
+                                            a_dtype="f32", x_dtype="bf16", seed=3),
+    "c5_packed_1x131072_h64_f32": dict(layout="packed", lengths=[131072], H=64,
+                                       a_dtype="f32", x_dtype="f32", seed=4),
+}
+
+
+def ragged_lengths(n: int = 48, lo: int = 1, hi: int = 1500, seed: int = 0) -> list[int]:
+    """Request lengths uniform in [lo, hi] (seed 0 gives T = 33,139 tokens in
+    542 chunks for the 48-request workload)."""
+    return [int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, n)]
+
+
+def config_lengths(cfg: dict) -> list[int]:
+    if cfg["layout"] == "dense":
+        return [cfg["T"]] * cfg["B"]
+    if cfg["lengths"] == "ragged48":
+        return ragged_lengths()
+    return list(cfg["lengths"])
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Cumulative sequence lengths [0, n0, n0+n1, ...] as int32."""
+    cu = np.zeros(len(lengths) + 1, np.int64)
+    cu[1:] = np.cumsum(np.asarray(lengths, np.int64))
+    assert cu[-1] < 2**31
+    return cu.astype(np.int32)
+
+
+def _chunk_rows(lengths):
+    """(first token, valid rows) of every chunk, in packed order."""
+    out = []
+    bos = 0
+    for n in lengths:
+        for p in range(0, n, CHUNK):
+            out.append((bos + p, min(CHUNK, n - p)))
+        bos += n
+    return out
+
+
+def _one_chunk(seed: int, idx: int, L: int, H: int, K: int) -> np.ndarray:
+    rng = np.random.default_rng([seed, idx])
+    k = rng.standard_normal((L, H, K))
+    z = rng.standard_normal((L, H, K))
+    b = rng.standard_normal((L, H))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    g = np.cumsum(-np.logaddexp(0.0, -(z + 3.0)), axis=0)  # logsigmoid(z + 3)
+    kq = (k * np.exp(g)).transpose(1, 0, 2)          # [H, L, K]
+    kk = (k * np.exp(-g)).transpose(1, 2, 0)         # [H, K, L]
+    S = np.matmul(kq, kk)                            # [H, L, L]
+    a = -beta.T[:, :, None] * S                      # [H, L, L]
+    a = np.tril(a, -1).transpose(1, 0, 2)            # [L, H, L]
+    out = np.zeros((L, H, CHUNK), np.float32)
+    out[:, :, :L] = a
+    return out
+
+
+def delta_rule_A(lengths, H: int, seed: int, K: int = KEY_DIM, upper: str = "zero",
+                 threads: int | None = None) -> np.ndarray:
+    """Packed float32 A [T, H, 64] for requests of the given lengths.
+
+    ``upper`` fills the entries on and above the diagonal (and the columns past
+    a partial chunk's length), which the solver must ignore: "zero", "nan", or
+    "garbage" (large finite values, +-inf and NaN mixed)."""
+    chunks = _chunk_rows(lengths)
+    T = int(sum(lengths))
+    A = np.zeros((T, H, CHUNK), np.float32)
+    nthr = threads or min(16, os.cpu_count() or 1)
+
+    def work(i):
+        s, L = chunks[i]
+        A[s:s + L] = _one_chunk(seed, i, L, H, K)
+
+    if len(chunks) > 1 and nthr > 1:
+        with ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(work, range(len(chunks))))
+    else:
+        for i in range(len(chunks)):
+            work(i)
+    if upper != "zero":
+        _fill_upper(A, chunks, upper, seed)
+    return A
+
+
+def _fill_upper(A, chunks, mode, seed):
+    rng = np.random.default_rng([seed, 0x5EED])
+    col = np.arange(CHUNK)
+    for s, L in chunks:
+        rows = np.arange(L)
+        mask = col[None, :] >= rows[:, None]                  # on/above diagonal
+        blk = A[s:s + L]
+        if mode == "nan":
+            fill = np.full(blk.shape, np.nan, np.float32)
+        elif mode == "garbage":
+            fill = rng.uniform(-1e30, 1e30, blk.shape).astype(np.float32)
+            pick = rng.integers(0, 4, blk.shape)
+            fill[pick == 0] = np.inf
+            fill[pick == 1] = -np.inf
+            fill[pick == 2] = np.nan
+        else:
+            raise ValueError(mode)
+        blk[np.broadcast_to(mask[:, None, :], blk.shape)] = fill[
+            np.broadcast_to(mask[:, None, :], blk.shape)]
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of a float32 array, via torch's CPU cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make(name_or_cfg, upper: str = "zero") -> dict:
+    """Materialise one workload. Returns a dict with the input ``A`` (float32,
+    or uint16 bfloat16 bits when a_dtype is bf16) in its layout
+    ([T, H, 64] packed or [B, T, H, 64] dense), ``cu_seqlens`` (packed only),
+    the request lengths and the config fields."""
+    cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    lengths = config_lengths(cfg)
+    A = delta_rule_A(lengths, cfg["H"], cfg["seed"], upper=upper)
+    if cfg["a_dtype"] == "bf16":
+        A = to_bf16_bits(A)
+    out = dict(cfg)
+    out["lengths"] = lengths
+    out["T_total"] = int(sum(lengths))
+    out["num_chunks"] = len(_chunk_rows(lengths))
+    if cfg["layout"] == "dense":
+        out["A"] = A.reshape(cfg["B"], cfg["T"], cfg["H"], CHUNK)
+    else:
+        out["A"] = A
+        out["cu_seqlens"] = cu_seqlens(lengths)
+    return out

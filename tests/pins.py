@@ -1,0 +1,212 @@
+"""Pins of the oracle's matrix inverse against facts that do not come from the
+oracle itself. Each check takes ``inv(M) -> X``: the (I + M)^-1 of one
+L x L matrix (only the strictly-lower part of M is meaningful), returned as
+L rows of 64 columns. The same checks run on the real oracle and on copies of
+it with a planted mistake, which they must reject.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def neumann_exact(M):
+    """X = sum_{k<n} (-M)^k in exact rationals (M strictly lower, so M^n = 0)."""
+    n = len(M)
+    F = [[Fraction(M[i][j]) if j < i else Fraction(0) for j in range(n)] for i in range(n)]
+    X = [[Fraction(int(i == j)) for j in range(n)] for i in range(n)]
+    P = [row[:] for row in X]  # (-M)^k
+    for _ in range(1, n):
+        P = [[-sum(P[i][m] * F[m][j] for m in range(n) if F[m][j] != 0 and P[i][m] != 0)
+              for j in range(n)] for i in range(n)]
+        for i in range(n):
+            for j in range(n):
+                X[i][j] += P[i][j]
+    return X
+
+
+def check_neumann_integer(inv, n=12, seed=0, density=0.6):
+    """Small integer matrices: every intermediate of a correct substitution is
+    an integer below 2^53, so the fp64 result must equal the exact series."""
+    rng = np.random.default_rng(seed)
+    M = np.tril(rng.integers(-2, 3, (n, n)), -1) * (rng.random((n, n)) < density)
+    M = M.astype(np.float64)
+    ex = neumann_exact(M.astype(np.int64).tolist())
+    X = inv(M)
+    for i in range(n):
+        for j in range(n):
+            if X[i, j] != float(ex[i][j]):
+                return f"neumann mismatch at ({i},{j}): {X[i, j]} vs {ex[i][j]}"
+        for j in range(n, 64):
+            if X[i, j] != 0.0:
+                return f"column {j} >= L not zero in row {i}"
+    return None
+
+
+def check_neumann_sparse64(inv, seed=0):
+    """Sparse 64 x 64 dyadic matrix (entries +-1/2, +-1): exact series."""
+    rng = np.random.default_rng(seed)
+    n = 64
+    vals = rng.choice(np.array([-1.0, -0.5, 0.5, 1.0]), (n, n))
+    M = np.tril(vals * (rng.random((n, n)) < 0.04), -1)
+    ex = neumann_exact([[Fraction(v) for v in row] for row in M.tolist()])
+    X = inv(M)
+    for i in range(n):
+        for j in range(n):
+            if Fraction(X[i, j]) != ex[i][j]:
+                return f"sparse64 mismatch at ({i},{j})"
+    return None
+
+
+def check_subdiagonal(inv, c, n=64):
+    """Single subdiagonal M[i, i-1] = c: X[i, j] = (-c)^(i-j) for i >= j."""
+    M = np.zeros((n, n))
+    for i in range(1, n):
+        M[i, i - 1] = c
+    X = inv(M)
+    want = np.zeros((n, 64))
+    for i in range(n):
+        for j in range(i + 1):
+            want[i, j] = (-c) ** (i - j)
+    exact = float(c) in (1.0, -1.0, 0.5, -0.5, 2.0, -2.0)
+    if exact:
+        if not np.array_equal(X, want):
+            return f"subdiagonal c={c}: not bitwise (-c)^(i-j)"
+    elif not np.allclose(X, want, rtol=1e-13, atol=0):
+        return f"subdiagonal c={c}: off the closed form"
+    return None
+
+
+def check_worked_4x4(inv):
+    """Hand-derived 4x4 example in tests/golden/worked_4x4.txt."""
+    A, X = [], []
+    cur = None
+    with open(os.path.join(GOLDEN, "worked_4x4.txt")) as f:
+        for line in f:
+            s = line.strip()
+            if not s or s.startswith("#"):
+                continue
+            if s in ("A", "X"):
+                cur = A if s == "A" else X
+                continue
+            cur.append([float(v) for v in s.split()])
+    got = inv(np.array(A))
+    if not np.array_equal(got[:, :4], np.array(X)):
+        return "worked 4x4 example mismatch"
+    return None
+
+
+def check_lapack(inv, seed=0, n=64, scale=0.5):
+    """Against LAPACK's general inverse of I + M (numpy.linalg.inv)."""
+    rng = np.random.default_rng(seed)
+    M = np.tril(rng.uniform(-scale, scale, (n, n)), -1)
+    X = inv(M)[:, :n]
+    ref = np.linalg.inv(np.eye(n) + M)
+    err = np.abs(X - ref).max() / max(1.0, np.abs(ref).max())
+    if err > 1e-12:
+        return f"lapack mismatch {err:.3g}"
+    return None
+
+
+def check_residual(inv, seed=0, n=64):
+    rng = np.random.default_rng(seed)
+    M = np.tril(rng.uniform(-0.5, 0.5, (n, n)), -1)
+    X = inv(M)[:, :n]
+    r = np.abs((np.eye(n) + M) @ X - np.eye(n)).max()
+    if r > 1e-12:
+        return f"residual {r:.3g}"
+    return None
+
+
+def check_upper_ignored(inv, seed=0, n=64):
+    """Entries on and above the diagonal of M must not enter the result."""
+    rng = np.random.default_rng(seed)
+    M = np.tril(rng.uniform(-0.5, 0.5, (n, n)), -1)
+    G = M.copy()
+    iu = np.triu_indices(n)
+    G[iu] = rng.uniform(-1e3, 1e3, len(iu[0]))
+    if not np.array_equal(inv(M), inv(G)):
+        return "upper triangle leaks into the result"
+    # non-finite values on and above the diagonal must not leak either
+    G[np.diag_indices(n)] = np.nan
+    G[0, 1:] = np.inf
+    if not np.array_equal(inv(M), inv(G)):
+        return "non-finite diagonal/upper entries leak into the result"
+    return None
+
+
+def check_leading_block(inv, seed=0):
+    """For L < 64 the result is the leading L x L block of the zero-padded
+    64 x 64 inverse, and matches LAPACK on the L x L matrix."""
+    rng = np.random.default_rng(seed)
+    M = np.tril(rng.uniform(-0.5, 0.5, (64, 64)), -1)
+    full = inv(M)
+    for L in (1, 2, 15, 16, 17, 31, 33, 63):
+        X = inv(M[:L, :L])
+        if not np.array_equal(X[:, :L], full[:L, :L]):
+            return f"L={L}: not the leading block"
+        if np.any(X[:, L:] != 0):
+            return f"L={L}: columns >= L not zero"
+        ref = np.linalg.inv(np.eye(L) + M[:L, :L])
+        if np.abs(X[:, :L] - ref).max() > 1e-12:
+            return f"L={L}: lapack mismatch"
+    return None
+
+
+ALL_INV_CHECKS = [
+    ("neumann_integer", check_neumann_integer),
+    ("neumann_sparse64", check_neumann_sparse64),
+    ("subdiag_1", lambda inv: check_subdiagonal(inv, 1.0)),
+    ("subdiag_-0.5", lambda inv: check_subdiagonal(inv, -0.5)),
+    ("subdiag_2", lambda inv: check_subdiagonal(inv, 2.0, n=40)),
+    ("subdiag_0.3", lambda inv: check_subdiagonal(inv, 0.3)),
+    ("worked_4x4", check_worked_4x4),
+    ("lapack", check_lapack),
+    ("residual", check_residual),
+    ("upper_ignored", check_upper_ignored),
+    ("leading_block", check_leading_block),
+]
+
+
+def run_all(inv):
+    """Names of failed checks (empty when every pin holds)."""
+    failed = []
+    for name, fn in ALL_INV_CHECKS:
+        try:
+            msg = fn(inv)
+        except Exception as e:  # a broken build may also crash a check
+            msg = f"raised {e!r}"
+        if msg:
+            failed.append((name, msg))
+    return failed
+
+
+def read_chunk_maps():
+    cases = []
+    cu, chunks = None, []
+    with open(os.path.join(GOLDEN, "chunk_map.txt")) as f:
+        for line in f:
+            s = line.split("#")[0].split()
+            if not s:
+                continue
+            if s[0] == "cu":
+                cu, chunks = [int(v) for v in s[1:]], []
+            elif s[0] == "chunk":
+                chunks.append(tuple(int(v) for v in s[1:]))
+            elif s[0] == "end":
+                cases.append((cu, chunks))
+    return cases
+
+
+def read_rne_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "bf16_rne.txt")) as f:
+        for line in f:
+            s = line.split("#")[0].split()
+            if len(s) >= 2:
+                rows.append((int(s[0], 16), int(s[1], 16)))
+    return rows

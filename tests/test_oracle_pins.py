@@ -1,0 +1,253 @@
+"""The oracle pinned to facts that do not come from itself (CPU only).
+
+Pins: exact rational Neumann series, the single-subdiagonal closed form, a
+hand-derived 4x4 example, LAPACK's inverse, the residual of (I + A) X = I,
+the leading-block property of partial chunks, hand-derived chunk maps and
+bfloat16 rounding tables, torch's bfloat16 cast. The last test plants
+plausible mistakes in copies of the oracle's C source and checks that these
+pins reject every one of them.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+
+def _inv(M):
+    return oracle.inv_unit_lower(M)
+
+
+@pytest.mark.parametrize("name,fn", pins.ALL_INV_CHECKS, ids=[n for n, _ in pins.ALL_INV_CHECKS])
+def test_inverse_pins(name, fn):
+    assert fn(_inv) is None
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_neumann_integer_more_seeds(seed):
+    assert pins.check_neumann_integer(_inv, n=16, seed=seed + 10) is None
+    assert pins.check_neumann_integer(_inv, n=5, seed=seed + 20, density=1.0) is None
+
+
+def test_delta_rule_matrices_against_lapack():
+    """Workload-shaped matrices (the generator's) against LAPACK."""
+    import synth
+    A = synth.delta_rule_A([64, 37], H=4, seed=7)
+    for s, L in ((0, 64), (64, 37)):
+        for h in range(4):
+            M = A[s:s + L, h, :L].astype(np.float64)
+            ref = np.linalg.inv(np.eye(L) + np.tril(M, -1))
+            X = oracle.inv_unit_lower(M)
+            assert np.abs(X[:, :L] - ref).max() < 1e-13
+
+
+def test_chunk_map_golden():
+    for cu, want in pins.read_chunk_maps():
+        got = [tuple(r) for r in oracle.chunks_packed(cu).tolist()]
+        assert got == want, cu
+
+
+def test_chunk_map_rejects_decreasing():
+    with pytest.raises(ValueError):
+        oracle.chunks_packed([0, 10, 5])
+
+
+def _packed_case(seed=3, H=3):
+    cu = [0, 64, 130, 130, 131, 300]
+    T = cu[-1]
+    rng = np.random.default_rng(seed)
+    A = rng.uniform(-0.5, 0.5, (T, H, 64)).astype(np.float32)
+    return cu, A
+
+
+def test_packed_driver_against_lapack_per_chunk():
+    """The packed driver solves every (chunk, head) of the hand-derived chunk
+    map; each equals LAPACK on that chunk's strictly-lower L x L block, and
+    entries on/above the diagonal (random here) are ignored."""
+    cu, A = _packed_case()
+    X = oracle.tril_inv_packed(A, cu)
+    want = [w for c, w in pins.read_chunk_maps() if c == [0, 64, 130, 130, 131]][0]
+    want = want + [(4, 131, 64), (4, 195, 64), (4, 259, 41)]
+    assert [tuple(r) for r in oracle.chunks_packed(cu).tolist()] == want
+    for _, s, L in want:
+        for h in range(A.shape[1]):
+            M = np.tril(A[s:s + L, h, :L].astype(np.float64), -1)
+            ref = np.linalg.inv(np.eye(L) + M)
+            assert np.abs(X[s:s + L, h, :L] - ref).max() < 1e-12
+            assert np.all(X[s:s + L, h, L:] == 0)
+
+
+def test_packed_rows_outside_chunks_untouched():
+    cu = [0, 10]
+    A = np.zeros((16, 2, 64), np.float32)
+    X = oracle.tril_inv_packed(A, cu, fill=-7.0)
+    assert np.all(X[10:] == -7.0)
+    assert np.array_equal(X[:10, 0, :10], np.eye(10))
+
+
+def test_dense_driver_against_lapack():
+    rng = np.random.default_rng(5)
+    B, T, H = 2, 150, 2
+    A = rng.uniform(-0.5, 0.5, (B, T, H, 64)).astype(np.float32)
+    X = oracle.tril_inv_dense(A)
+    for b in range(B):
+        for c0 in range(0, T, 64):
+            L = min(64, T - c0)
+            for h in range(H):
+                M = np.tril(A[b, c0:c0 + L, h, :L].astype(np.float64), -1)
+                ref = np.linalg.inv(np.eye(L) + M)
+                assert np.abs(X[b, c0:c0 + L, h, :L] - ref).max() < 1e-12
+                assert np.all(X[b, c0:c0 + L, h, L:] == 0)
+
+
+def test_dense_equals_packed_with_equal_lengths():
+    rng = np.random.default_rng(6)
+    B, T, H = 3, 100, 2
+    A = rng.uniform(-0.5, 0.5, (B, T, H, 64)).astype(np.float32)
+    Xd = oracle.tril_inv_dense(A)
+    Xp = oracle.tril_inv_packed(A.reshape(B * T, H, 64), [0, 100, 200, 300])
+    assert np.array_equal(Xd.reshape(B * T, H, 64), Xp)
+
+
+def test_bf16_upcast_is_exact():
+    bits = np.array([0x3F80, 0xBF82, 0x0001, 0x7F7F], np.uint16)
+    got = oracle.to_f64(bits, "bf16")
+    want = np.array([1.0, -(1 + 2 / 128), 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127])
+    assert np.array_equal(got, want)
+
+
+def test_rne_golden():
+    table = pins.read_rne_table()
+    f = np.array([a for a, _ in table], np.uint32).view(np.float32)
+    got = oracle.rne_bf16(f)
+    assert [int(v) for v in got] == [b for _, b in table]
+
+
+def test_rne_matches_torch_cast():
+    import torch
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** rng.integers(
+        -30, 30, 200000).astype(np.float32)
+    # add exact ties and neighbours
+    ties = (rng.integers(0, 2**31, 5000, dtype=np.int64).astype(np.uint32) & 0xFFFF0000) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32)])
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.rne_bf16(x), want)
+
+
+# ---- planted mistakes: each must be rejected by the pins above ----------------
+
+_MUTANTS = {
+    "drop_first_term": ("for (int j = c; j < i; ++j) s +=", "for (int j = c + 1; j < i; ++j) s +="),
+    "wrong_sign": ("col[i] = -s;", "col[i] = s;"),
+    "transposed": ("s += M[(int64_t)i * ldm + j] * col[j];", "s += M[(int64_t)j * ldm + i] * col[j];"),
+    "reads_diagonal": ("for (int j = c; j < i; ++j) s +=", "for (int j = c; j <= i; ++j) s +="),
+    "global_chunk_alignment": ("for (int64_t p = bos; p < eos; p += ORACLE_CHUNK)",
+                               "for (int64_t p = bos - bos % ORACLE_CHUNK; p < eos; p += ORACLE_CHUNK)"),
+    "ties_away": ("(rest == 0x8000u && (kept & 1u))", "(rest == 0x8000u)"),
+    "dense_row0": ("int64_t row0 = b * T + c * ORACLE_CHUNK;",
+                   "int64_t row0 = (b * per_b + c) * ORACLE_CHUNK;"),
+}
+
+
+def _build_mutant(tmp_path, name):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "tril_oracle.c")).read()
+    old, new = _MUTANTS[name]
+    assert src.count(old) >= 1, name
+    src = src.replace(old, new)
+    if name == "reads_diagonal":  # j <= i would read col[i], so make it defined
+        src = src.replace("col[c] = 1.0;", "col[c] = 1.0;\n        for (int i = c + 1; i < 64; ++i) col[i] = 0.0;")
+    c = tmp_path / f"{name}.c"
+    c.write_text(src)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o",
+                           str(so), str(c)])
+    lib = ctypes.CDLL(str(so))
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
+    lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
+    lib.oracle_chunks_packed.restype = i64
+    lib.oracle_rne_bf16.argtypes = [p, p, i64]
+    lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int]
+    lib.oracle_tril_inv_dense.restype = i64
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _pins_fail(lib):
+    """True when at least one pin rejects this build."""
+    def inv(M):
+        M = np.ascontiguousarray(M, np.float64)
+        L = M.shape[0]
+        X = np.zeros((L, 64))
+        lib.oracle_inv_unit_lower(_ptr(M), M.shape[1], L, _ptr(X), 64)
+        return X
+
+    if pins.run_all(inv):
+        return True
+    for cu, want in pins.read_chunk_maps():
+        cu = np.array(cu, np.int32)
+        n = lib.oracle_chunks_packed(_ptr(cu), len(cu) - 1, None, None, None, 0)
+        if n != len(want):
+            return True
+        seq, st, ln = np.zeros(n, np.int64), np.zeros(n, np.int64), np.zeros(n, np.int32)
+        lib.oracle_chunks_packed(_ptr(cu), len(cu) - 1, _ptr(seq), _ptr(st), _ptr(ln), n)
+        if list(zip(seq.tolist(), st.tolist(), ln.tolist())) != want:
+            return True
+    table = pins.read_rne_table()
+    bits = np.array([a for a, _ in table], np.uint32)
+    out = np.zeros(len(bits), np.uint16)
+    lib.oracle_rne_bf16(_ptr(bits), _ptr(out), len(bits))
+    if out.tolist() != [b for _, b in table]:
+        return True
+    # dense driver on a partial-chunk shape, against LAPACK per matrix
+    rng = np.random.default_rng(5)
+    B, T, H = 2, 150, 2
+    # room past the end so a mutant that indexes rows wrongly stays in bounds
+    Abuf = rng.uniform(-0.5, 0.5, (B * T + 4 * 64, H, 64))
+    Xbuf = np.full_like(Abuf, np.nan)
+    lib.oracle_tril_inv_dense(_ptr(Abuf), _ptr(Xbuf), B, T, H, 1)
+    A = Abuf[:B * T].reshape(B, T, H, 64)
+    X = Xbuf[:B * T].reshape(B, T, H, 64)
+    for b in range(B):
+        for c0 in range(0, T, 64):
+            L = min(64, T - c0)
+            for h in range(H):
+                ref = np.linalg.inv(np.eye(L) + np.tril(A[b, c0:c0 + L, h, :L], -1))
+                got = X[b, c0:c0 + L, h, :L]
+                if not np.all(np.isfinite(got)) or np.abs(got - ref).max() > 1e-12:
+                    return True
+    return False
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    assert _pins_fail(_build_mutant(tmp_path, name)), f"pins accept the mutant {name}"
+
+
+def test_unpatched_oracle_passes_the_same_gate(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "tril_oracle.c")).read()
+    c = tmp_path / "plain.c"
+    c.write_text(src)
+    so = tmp_path / "libplain.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o",
+                           str(so), str(c)])
+    lib = ctypes.CDLL(str(so))
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
+    lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
+    lib.oracle_chunks_packed.restype = i64
+    lib.oracle_rne_bf16.argtypes = [p, p, i64]
+    lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int]
+    lib.oracle_tril_inv_dense.restype = i64
+    assert not _pins_fail(lib)
