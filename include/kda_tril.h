@@ -1,0 +1,154 @@
+/*
+ * kda_tril.h - C ABI of the MI355X (gfx950) KDA prefill chunk solver.
+ *
+ * Operation (LightLLM PR #1703, "perf(kda): parallelize diagonal solves in
+ * Prefill", PR description, method paragraph): the sequence is cut into
+ * 64-token chunks; for every chunk and every head the solver returns
+ *
+ *     X = (I + A)^-1,
+ *
+ * where A is the 64 x 64 strictly-lower-triangular intra-chunk matrix of
+ * that head. The page's scheme inverts the four 16 x 16 diagonal blocks of
+ * I + A independently and then merges them into the 64 x 64 inverse, keeping
+ * the inverse tiles in FP32 until the final store (same PR, commit summary).
+ * This library follows that scheme on CDNA4: every kernel computes in FP32;
+ * inputs and outputs may be FP32 or bfloat16.
+ *
+ * Layout (both A and X, contiguous, row-major, 64 columns innermost):
+ *   packed: [T, H, 64]; requests are concatenated along T and described by
+ *           cu_seqlens. Chunks restart at every request's first token, so the
+ *           last chunk of a request may hold fewer than 64 valid rows (L).
+ *   dense:  [B, T, H, 64]; every batch element is one request of T tokens.
+ * Element (token t, head h, column j) of A is entry (t - chunk_start, j) of
+ * that chunk-head's matrix. Entries on or above the diagonal, and columns
+ * >= L of a partial chunk, are ignored (never used in arithmetic, so NaN or
+ * Inf there cannot reach X). For each valid row i < L of a chunk, X is
+ * written in full: X[i][i] = 1, X[i][j] = 0 for j > i (including j >= L),
+ * and the inverse below the diagonal. Rows that belong to no chunk (packed
+ * tokens past cu_seqlens[num_seqs]) are not written.
+ *
+ * Memory: every pointer argument is DEVICE memory unless marked (host). The
+ * caller owns A, X, cu_seqlens, chunk_indices and the workspace. The library
+ * allocates nothing, frees nothing, keeps no pointer after a call returns,
+ * never synchronises and never copies between host and device: every call
+ * only enqueues kernels on `stream` and returns. A and X must not overlap.
+ *
+ * Errors: plain status codes; nothing is thrown across the ABI. Problems that
+ * the host can see (null pointers with nonzero sizes, H <= 0, unknown dtype,
+ * forced SPLIT with too little workspace, sizes past the int32 token range)
+ * are reported before any launch. Device-side cu_seqlens are not validated
+ * (that would need a synchronisation): they must start at 0, be
+ * non-decreasing and end at <= total_tokens; kernels clamp every row index
+ * to [0, total_tokens) so a bad cu_seqlens cannot write outside X.
+ * KDA_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ * Zero tokens, zero batch or zero requests is a no-op returning KDA_OK.
+ *
+ * Thread safety: stateless. Concurrent calls on different streams need
+ * different workspaces.
+ */
+#ifndef KDA_TRIL_H
+#define KDA_TRIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of A or X. BF16 is bfloat16 (8 exponent, 7 mantissa bits);
+ * a bfloat16 X is the round-to-nearest-even of the FP32 result. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Kernel plan.
+ *   AUTO   - pick SPLIT when it is eligible and the tuned rule prefers it,
+ *            else FUSED (same PR, PR description: splitting is selected by
+ *            the FP32 workspace budget and a minimum input length; commit
+ *            summary: by chunk occupancy, to bound scratch). An ineligible
+ *            SPLIT silently falls back to FUSED.
+ *   FUSED  - one kernel: diagonal inverses and merges of a chunk-head in one
+ *            wavefront, merge products on the FP32 matrix cores (MFMA).
+ *   SPLIT  - two kernels: the diagonal kernel writes the four FP32 16 x 16
+ *            inverse tiles of every chunk-head to the workspace, the merge
+ *            kernel reads them back with A and writes X. Needs workspace of
+ *            kda_tril_inv_workspace_size bytes; it must not exceed the FP32
+ *            input size (T x H x 64 x 4 bytes), i.e. mean chunk occupancy
+ *            T / num_chunks >= 16.
+ *   FUSED_VALU - like FUSED, but the merge products run as FP32 vector FMAs
+ *            instead of matrix-core instructions (the other precision mode:
+ *            both are IEEE FP32 products and sums, in different orders). */
+typedef enum {
+    KDA_ALGO_AUTO = 0,
+    KDA_ALGO_FUSED = 1,
+    KDA_ALGO_SPLIT = 2,
+    KDA_ALGO_FUSED_VALU = 3
+} kda_algo;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1,
+    KDA_ERR_UNSUPPORTED = -2,
+    KDA_ERR_WORKSPACE = -3,
+    KDA_ERR_HIP = -4
+} kda_status;
+
+/*
+ * Workspace query and plan choice. Host only: never touches the GPU.
+ *   total_tokens  T (packed) or B * T (dense), >= 0.
+ *   num_seqs      number of requests (packed) or B (dense), >= 0.
+ *   num_chunks    exact number of chunks if known, else 0: the bound
+ *                 floor(total_tokens / 64) + num_seqs is then used.
+ *   num_heads     H > 0.
+ *   algo          requested plan.
+ *   bytes (host out)   workspace bytes the call with this plan needs
+ *                      (0 for FUSED / FUSED_VALU).
+ *   chosen (host out, nullable)  plan that a call with a workspace of
+ *                      *bytes bytes would run (AUTO resolved).
+ * The SPLIT workspace is 4 tiles x 16 x 16 FP32 = 4096 bytes per chunk-head.
+ * Returns KDA_ERR_WORKSPACE when SPLIT is forced but ineligible (its scratch
+ * would exceed the FP32 input size).
+ */
+kda_status kda_tril_inv_workspace_size(int64_t total_tokens, int64_t num_seqs,
+                                       int64_t num_chunks, int32_t num_heads, kda_algo algo,
+                                       size_t *bytes, kda_algo *chosen);
+
+/*
+ * Dense batch: A [B, T, H, 64] of a_dtype, X [B, T, H, 64] of x_dtype.
+ * B * T must fit in int32. workspace may be NULL when workspace_bytes is 0.
+ */
+kda_status kda_tril_inv_dense(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
+                              int64_t B, int64_t T, int32_t H, void *workspace,
+                              size_t workspace_bytes, kda_algo algo, hipStream_t stream);
+
+/*
+ * Packed varlen batch: A [total_tokens, H, 64], X [total_tokens, H, 64].
+ *   cu_seqlens     int32 [num_seqs + 1] (device): 0 = cu[0] <= cu[1] <= ...
+ *                  <= cu[num_seqs] <= total_tokens.
+ *   chunk_indices  optional int32 [num_chunks][2] (device) of (request,
+ *                  chunk-within-request) pairs in packed order, as a caller
+ *                  that reuses one map across layers would keep it; NULL to
+ *                  let the kernels resolve chunks from cu_seqlens on the
+ *                  device (grid sized by the bound floor(T/64) + num_seqs).
+ *   num_chunks     length of chunk_indices (0 when it is NULL).
+ */
+kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
+                               const int32_t *cu_seqlens, int64_t num_seqs,
+                               int64_t total_tokens, int32_t H, const int32_t *chunk_indices,
+                               int64_t num_chunks, void *workspace, size_t workspace_bytes,
+                               kda_algo algo, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Plan AUTO would choose for a problem with these sizes and workspace
+ * (host only; same rule the calls apply). */
+kda_algo kda_tril_auto_plan(int64_t total_tokens, int64_t num_chunks, int32_t num_heads,
+                            size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_TRIL_H */

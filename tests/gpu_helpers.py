@@ -1,0 +1,75 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs and compare with the oracle to the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+
+# Tolerances (elementwise, X_ref from the fp64 oracle):
+#   fp32 output: |X - X_ref| <= 2e-5 * (1 + |X_ref|)
+#   bf16 output: |X - X_ref| <= 1e-2 * |X_ref| + 2e-5 * (1 + |X_ref|)
+#   residual (fp32 outputs): max |(I + A_L) X - I| <= 1e-4
+F32_TOL = 2e-5
+BF16_REL = 1e-2
+RESIDUAL_TOL = 1e-4
+
+
+def to_torch_input(A_np, a_dtype, device):
+    import torch
+    if a_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(A_np).view(np.int16)).view(
+            torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(A_np, dtype=np.float32)).to(device)
+
+
+def out_torch_dtype(x_dtype):
+    import torch
+    return torch.bfloat16 if x_dtype == "bf16" else torch.float32
+
+
+def to_numpy_f64(X):
+    """Device tensor -> float64 numpy (exact for f32 and bf16)."""
+    import torch
+    if X.dtype == torch.bfloat16:
+        bits = X.cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return X.cpu().numpy().astype(np.float64)
+
+
+def bf16_bits(X):
+    import torch
+    assert X.dtype == torch.bfloat16
+    return X.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def excess(got, ref, x_dtype):
+    """Largest amount by which |got - ref| exceeds its bound (<= 0: pass)."""
+    diff = np.abs(got - ref)
+    bound = F32_TOL * (1.0 + np.abs(ref))
+    if x_dtype == "bf16":
+        bound = bound + BF16_REL * np.abs(ref)
+    e = diff - bound
+    e = np.where(np.isnan(got) | np.isnan(ref), np.inf, e)
+    return float(e.max()) if e.size else -1.0
+
+
+def residual_chunks(A64, X64, chunks):
+    """max |(I + A_L) X_L - I| over the given (start, len, head) matrices;
+    A64, X64 packed [T, H, 64] float64."""
+    worst = 0.0
+    for s, L, h in chunks:
+        M = np.tril(A64[s:s + L, h, :L], -1)
+        Xm = X64[s:s + L, h, :L]
+        r = np.abs((np.eye(L) + M) @ Xm - np.eye(L)).max()
+        worst = max(worst, float(r))
+    return worst
+
+
+def all_chunk_heads(lengths, H):
+    out = []
+    bos = 0
+    for n in lengths:
+        for p in range(0, n, 64):
+            for h in range(H):
+                out.append((bos + p, min(64, n - p), h))
+        bos += n
+    return out

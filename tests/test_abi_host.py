@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a kernel).
+
+The library must load, export every entry point include/kda_tril.h declares,
+size workspaces and choose plans as documented, and reject bad arguments
+before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda_tril.h")
+
+
+@pytest.fixture(scope="module")
+def kt():
+    import tril_solve_amd
+    return tril_solve_amd
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(kt):
+    names = declared_functions()
+    assert names == sorted(kt.EXPORTED)
+    lib = ctypes.CDLL(kt.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(kt):
+    for code in (0, -1, -2, -3, -4):
+        s = kt.kda_status_string(code)
+        assert s.startswith("KDA_")
+    assert "UNKNOWN" in kt.kda_status_string(7)
+
+
+def test_workspace_sizes(kt):
+    # packed 16 x 512 tokens, 64 heads, exact chunk count: 4 KiB per
+    # chunk-head, 32 MiB in all; the FP32 input is 128 MiB, so split fits
+    b, c = kt.kda_tril_inv_workspace_size(8192, 16, 128, 64, "split")
+    assert (b, c) == (128 * 64 * 4096, "split") and b == 32 * 2**20
+    # without the exact count the bound floor(T/64) + N slots is used
+    b, _ = kt.kda_tril_inv_workspace_size(8192, 16, 0, 64, "split")
+    assert b == (128 + 16) * 64 * 4096
+    for algo in ("fused", "fused_valu"):
+        assert kt.kda_tril_inv_workspace_size(8192, 16, 128, 64, algo) == (0, algo)
+
+
+def test_split_budget_is_fp32_input_size(kt):
+    # scratch <= FP32 input  <=>  T / slots >= 16
+    assert kt.kda_tril_inv_workspace_size(16 * 10, 1, 10, 4, "split")[1] == "split"
+    with pytest.raises(kt.KdaError) as e:
+        kt.kda_tril_inv_workspace_size(16 * 10 - 1, 1, 10, 4, "split")
+    assert e.value.status == kt.KDA_ERR_WORKSPACE
+    # many one-token requests: occupancy 1 token per chunk
+    with pytest.raises(kt.KdaError):
+        kt.kda_tril_inv_workspace_size(100, 100, 100, 8, "split")
+
+
+def test_auto_plan_rule(kt, monkeypatch):
+    # default: no input size where split was measured faster -> fused
+    assert kt.kda_tril_auto_plan(8192, 128, 64, 2**40) == "fused"
+    monkeypatch.setenv("KDA_TRIL_SPLIT_MIN_TOKENS", "4096")
+    assert kt.kda_tril_auto_plan(8192, 128, 64, 2**40) == "split"
+    assert kt.kda_tril_auto_plan(4095, 64, 64, 2**40) == "fused"       # below min length
+    assert kt.kda_tril_auto_plan(8192, 128, 64, 128 * 64 * 4096 - 1) == "fused"  # short ws
+    assert kt.kda_tril_auto_plan(8192, 1000, 64, 2**40) == "fused"     # over budget
+    assert kt.kda_tril_inv_workspace_size(8192, 16, 128, 64, "auto") == (32 * 2**20, "split")
+    monkeypatch.setenv("KDA_TRIL_SPLIT_MIN_TOKENS", "0")
+    assert kt.kda_tril_auto_plan(64, 1, 64, 2**40) == "split"
+
+
+def test_workspace_query_errors(kt):
+    for args in [(-1, 1, 0, 4), (10, -1, 0, 4), (10, 1, -1, 4), (10, 1, 0, 0)]:
+        with pytest.raises(kt.KdaError) as e:
+            kt.kda_tril_inv_workspace_size(*args, "auto")
+        assert e.value.status == kt.KDA_ERR_INVALID_ARG
+    with pytest.raises(kt.KdaError) as e:
+        kt.kda_tril_inv_workspace_size(2**31, 1, 0, 4, "auto")
+    assert e.value.status == kt.KDA_ERR_UNSUPPORTED
+
+
+# ---- argument validation: every case returns before any launch ------------
+
+P = ctypes.c_void_p
+
+
+def _packed(kt, A=0x10000, ad=0, X=0x90000000, xd=0, cu=0x2000, nseq=1, T=64, H=2, cmap=None,
+            nch=0, ws=None, wsb=0, algo=1):
+    return kt._lib.kda_tril_inv_packed(P(A), ad, P(X), xd, P(cu), nseq, T, H, P(cmap), nch, P(ws),
+                                       wsb, algo, None)
+
+
+def _dense(kt, A=0x10000, ad=0, X=0x90000000, xd=0, B=1, T=64, H=2, ws=None, wsb=0, algo=1):
+    return kt._lib.kda_tril_inv_dense(P(A), ad, P(X), xd, B, T, H, P(ws), wsb, algo, None)
+
+
+def test_invalid_arguments_rejected_before_launch(kt):
+    E = kt.KDA_ERR_INVALID_ARG
+    assert _packed(kt, ad=2) == E                      # unknown input dtype
+    assert _packed(kt, xd=-1) == E                     # unknown output dtype
+    assert _packed(kt, algo=9) == E                    # unknown plan
+    assert _packed(kt, H=0) == E
+    assert _packed(kt, A=None) == E
+    assert _packed(kt, X=None) == E
+    assert _packed(kt, cu=None) == E
+    assert _packed(kt, A=0x10008) == E                 # misaligned
+    assert _packed(kt, X=0x10000 + 64 * 2 * 64 * 4 - 16) == E  # overlaps A
+    assert _packed(kt, cmap=0x3000, nch=0) == E        # map without a length
+    assert _packed(kt, cmap=None, nch=5) == E
+    assert _packed(kt, nseq=-1) == E
+    assert _packed(kt, T=-5) == E
+    assert _dense(kt, B=-1) == E
+    assert _dense(kt, H=-3) == E
+    assert _dense(kt, A=None) == E
+
+
+def test_unsupported_sizes(kt):
+    U = kt.KDA_ERR_UNSUPPORTED
+    assert _packed(kt, T=2**31) == U
+    assert _dense(kt, B=2**20, T=2**12) == U
+
+
+def test_forced_split_workspace_errors(kt):
+    W = kt.KDA_ERR_WORKSPACE
+    assert _packed(kt, algo=2) == W                    # no workspace
+    assert _packed(kt, algo=2, ws=0x4000, wsb=1000) == W
+    assert _dense(kt, algo=2) == W
+    # budget exceeded: 64 one-token requests
+    assert _packed(kt, algo=2, nseq=64, T=64, ws=0x4000, wsb=2**40) == W
+    # enough workspace but misaligned
+    assert _packed(kt, algo=2, ws=0x4004, wsb=2**30) == kt.KDA_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_noops(kt):
+    assert _packed(kt, T=0) == kt.KDA_OK
+    assert _packed(kt, nseq=0) == kt.KDA_OK
+    assert _packed(kt, T=0, A=None, X=None, cu=None) == kt.KDA_OK
+    assert _dense(kt, B=0) == kt.KDA_OK
+    assert _dense(kt, T=0, A=None, X=None) == kt.KDA_OK

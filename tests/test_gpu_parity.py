@@ -1,0 +1,390 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 output |X - X_ref| <= 2e-5 (1 + |X_ref|); bf16 output
+|X - X_ref| <= 1e-2 |X_ref| + 2e-5 (1 + |X_ref|); residual
+max |(I + A) X - I| <= 1e-4 on fp32 outputs. Exact cases are compared bit
+for bit. Every input is seeded; every expected value comes from the oracle
+or from a closed form.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_helpers as gh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["fused", "split", "fused_valu"]
+
+
+@pytest.fixture(scope="module")
+def kt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tril_solve_amd
+    return tril_solve_amd
+
+
+DEV = "cuda:0"
+
+
+def _run_cfg(kt, d, algo, x_dtype=None):
+    x_dtype = x_dtype or d["x_dtype"]
+    A = gh.to_torch_input(d["A"], d["a_dtype"], DEV)
+    if d["layout"] == "dense":
+        X = kt.tril_inv(A, None, out_dtype=gh.out_torch_dtype(x_dtype), algo=algo)
+    else:
+        cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+        X = kt.tril_inv(A, cu, out_dtype=gh.out_torch_dtype(x_dtype), algo=algo)
+    torch.cuda.synchronize()
+    return X
+
+
+def _oracle_cfg(d):
+    if d["layout"] == "dense":
+        return oracle.tril_inv_dense(d["A"], d["a_dtype"])
+    return oracle.tril_inv_packed(d["A"], d["cu_seqlens"], d["a_dtype"])
+
+
+_CFG_CACHE = {}
+
+
+def _cfg(name):
+    if name not in _CFG_CACHE:
+        d = synth.make(name)
+        d["ref"] = _oracle_cfg(d)
+        _CFG_CACHE[name] = d
+    return _CFG_CACHE[name]
+
+
+SMALL_CFGS = ["c1_packed_1x64_h64_f32", "c2_dense_b4_t512_h16_bf16_f32",
+              "c3_packed_16x512_h64_f32", "c4_packed_ragged48_h64_f32_bf16"]
+
+
+@pytest.mark.parametrize("algo", ALGOS + ["auto"])
+@pytest.mark.parametrize("name", SMALL_CFGS)
+def test_config_parity(kt, name, algo):
+    print(f"\n[parity] {name} algo={algo}", flush=True)
+    d = _cfg(name)
+    X = _run_cfg(kt, d, algo)
+    got = gh.to_numpy_f64(X)
+    ref = d["ref"]
+    if d["layout"] == "dense":
+        got = got.reshape(-1, d["H"], 64)
+        ref = ref.reshape(-1, d["H"], 64)
+    e = gh.excess(got, ref, d["x_dtype"])
+    assert e <= 0, f"{name}/{algo}: exceeds tolerance by {e:.3g}"
+    # residual on an fp32-output run of the same A (bf16 output alone would
+    # carry ~1e-3 of rounding)
+    if d["x_dtype"] == "f32":
+        X32 = got
+    else:
+        X32 = gh.to_numpy_f64(_run_cfg(kt, d, algo, x_dtype="f32"))
+    A64 = oracle.to_f64(d["A"], d["a_dtype"]).reshape(-1, d["H"], 64)
+    X32 = X32.reshape(-1, d["H"], 64)
+    ch = gh.all_chunk_heads(d["lengths"], d["H"])
+    rng = np.random.default_rng(0)
+    pick = [ch[i] for i in rng.choice(len(ch), min(len(ch), 400), replace=False)]
+    assert gh.residual_chunks(A64, X32, pick) <= gh.RESIDUAL_TOL
+
+
+@pytest.fixture(scope="module")
+def c5():
+    name = "c5_packed_1x131072_h64_f32"
+    print(f"\n[c5] generating {name}", flush=True)
+    return synth.make(name)
+
+
+@pytest.mark.parametrize("algo", ["fused", "split"])
+def test_long_context_sampled(kt, c5, algo):
+    """1 request x 131072 tokens, H = 64 (131072 matrices): 256 sampled
+    chunk-heads against the oracle; unit diagonal and zero upper triangle
+    on every row."""
+    d = c5
+    A = torch.from_numpy(d["A"]).to(DEV)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    print(f"[c5] solving algo={algo}", flush=True)
+    X = kt.tril_inv(A, cu, algo=algo)
+    torch.cuda.synchronize()
+    T, H = d["T_total"], d["H"]
+    diag = X.view(T // 64, 64, H, 64).permute(0, 2, 1, 3)  # [chunk, head, row, col]
+    assert bool((torch.diagonal(diag, dim1=2, dim2=3) == 1).all())
+    upper = torch.triu(torch.ones(64, 64, device=DEV, dtype=torch.bool), 1)
+    assert bool((diag[:, :, upper] == 0).all())
+    assert bool(torch.isfinite(X).all())
+    rng = np.random.default_rng(1)
+    for k in rng.choice(T // 64 * H, 256, replace=False):
+        c, h = divmod(int(k), H)
+        M = d["A"][64 * c:64 * c + 64, h, :].astype(np.float64)
+        ref = oracle.inv_unit_lower(M)
+        Xc = X[64 * c:64 * c + 64, h, :].cpu().numpy().astype(np.float64)
+        assert gh.excess(Xc, ref, "f32") <= 0, (c, h)
+        assert np.abs((np.eye(64) + np.tril(M, -1)) @ Xc - np.eye(64)).max() <= gh.RESIDUAL_TOL
+
+
+def _subdiag_input(H, lengths, c):
+    T = sum(lengths)
+    A = np.zeros((T, H, 64), np.float32)
+    bos = 0
+    for n in lengths:
+        for p in range(0, n, 64):
+            L = min(64, n - p)
+            for i in range(1, L):
+                A[bos + p + i, :, i - 1] = c
+        bos += n
+    return A
+
+
+@pytest.mark.parametrize("c", [1.0, -1.0, 0.5, -0.5, 2.0, -2.0])
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_exact_subdiagonal(kt, c, algo, x_dtype):
+    """A[i, i-1] = c: X[i, j] = (-c)^(i-j) exactly (one nonzero term per sum)."""
+    lengths = [64, 64, 23]
+    H = 3
+    A = _subdiag_input(H, lengths, c)
+    cu = synth.cu_seqlens(lengths)
+    X = kt.tril_inv(torch.from_numpy(A).to(DEV), torch.from_numpy(cu).to(DEV),
+                    out_dtype=gh.out_torch_dtype(x_dtype), algo=algo)
+    got = gh.to_numpy_f64(X)
+    bos = 0
+    for n in lengths:
+        for p in range(0, n, 64):
+            L = min(64, n - p)
+            want = np.zeros((L, 64))
+            for i in range(L):
+                for j in range(i + 1):
+                    want[i, j] = (-c) ** (i - j)
+            for h in range(H):
+                assert np.array_equal(got[bos + p:bos + p + L, h, :], want), (n, p, h)
+        bos += n
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_zero_and_single_entry(kt, algo):
+    H = 2
+    A = np.zeros((64, H, 64), np.float32)
+    cu = torch.tensor([0, 64], dtype=torch.int32, device=DEV)
+    X = kt.tril_inv(torch.from_numpy(A).to(DEV), cu, algo=algo).cpu().numpy()
+    for h in range(H):
+        assert np.array_equal(X[:, h, :], np.eye(64, dtype=np.float32))
+    # one nonzero a at (i, j): (I + a E_ij)^-1 = I - a E_ij, bit for bit
+    for (i, j) in [(1, 0), (15, 3), (17, 16), (40, 2), (63, 0), (63, 62), (33, 31), (50, 20)]:
+        A = np.zeros((64, H, 64), np.float32)
+        A[i, 1, j] = 0.375
+        X = kt.tril_inv(torch.from_numpy(A).to(DEV), cu, algo=algo).cpu().numpy()
+        want = np.eye(64, dtype=np.float32)
+        want[i, j] = -0.375
+        assert np.array_equal(X[:, 1, :], want), (i, j)
+        assert np.array_equal(X[:, 0, :], np.eye(64, dtype=np.float32))
+
+
+PARTIAL_LENGTHS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_partial_chunks_and_canaries(kt, algo, x_dtype):
+    """Ragged lengths with NaN on and above the diagonal of A. Valid rows
+    match the oracle, carry exact 1 on the diagonal and +0 above it; rows past
+    cu_seqlens[-1] and guard bands around X stay untouched."""
+    H = 4
+    lengths = PARTIAL_LENGTHS
+    T = sum(lengths)
+    tail = 37
+    A = np.zeros((T + tail, H, 64), np.float32)
+    A[:T] = synth.delta_rule_A(lengths, H, seed=21, upper="nan")
+    A[T:] = np.nan
+    cu = synth.cu_seqlens(lengths)
+    tdt = gh.out_torch_dtype(x_dtype)
+    canary = torch.tensor(-1234.5, dtype=tdt)
+    pad = 64
+    buf = torch.full((T + tail + 2 * pad, H, 64), float(canary), dtype=tdt, device=DEV)
+    X = buf[pad:pad + T + tail]
+    kt.kda_tril_inv_packed(torch.from_numpy(A).to(DEV), X, torch.from_numpy(cu).to(DEV),
+                           workspace=_workspace(kt, T + tail, len(lengths), H, algo), algo=algo)
+    torch.cuda.synchronize()
+    b = gh.to_numpy_f64(buf)
+    assert np.all(b[:pad] == float(canary)) and np.all(b[pad + T + tail:] == float(canary))
+    got = b[pad:pad + T + tail]
+    assert np.all(got[T:] == float(canary)), "rows past the last request were written"
+    ref = oracle.tril_inv_packed(A, cu, fill=np.nan)
+    assert gh.excess(got[:T], ref[:T], x_dtype) <= 0
+    raw = X.cpu()
+    if x_dtype == "bf16":
+        bits = raw.view(torch.int16).numpy().view(np.uint16)
+        one, zero = 0x3F80, 0
+    else:
+        bits = raw.view(torch.int32).numpy().view(np.uint32)
+        one, zero = 0x3F800000, 0
+    for s, L, h in gh.all_chunk_heads(lengths, H):
+        blk = bits[s:s + L, h, :]
+        for i in range(L):
+            assert blk[i, i] == one
+            assert np.all(blk[i, i + 1:] == zero)
+
+
+def _workspace(kt, T, nseq, H, algo, nchunks=0):
+    nbytes, _ = kt.kda_tril_inv_workspace_size(T, nseq, nchunks, H, algo)
+    if not nbytes:
+        return None
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+
+
+@pytest.mark.parametrize("T", [512, 300])
+def test_dense_equals_packed(kt, T):
+    B, H = 3, 5
+    A = synth.delta_rule_A([T] * B, H, seed=31)
+    Ad = torch.from_numpy(A).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens([T] * B)).to(DEV)
+    Xp = kt.tril_inv(Ad, cu, algo="fused")
+    Xd = kt.tril_inv(Ad.view(B, T, H, 64), None, algo="fused")
+    assert torch.equal(Xp.view(B, T, H, 64), Xd)
+    Xs = kt.tril_inv(Ad.view(B, T, H, 64), None, algo="split")
+    assert torch.equal(Xs, Xd)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_output_is_rne_of_fp32_output(kt, algo):
+    lengths = [512, 300, 64, 7]
+    H = 8
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=41)).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    X32 = kt.tril_inv(A, cu, out_dtype=torch.float32, algo=algo)
+    X16 = kt.tril_inv(A, cu, out_dtype=torch.bfloat16, algo=algo)
+    want = oracle.rne_bf16(X32.cpu().numpy())
+    assert np.array_equal(gh.bf16_bits(X16), want)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_bf16_input(kt, x_dtype):
+    lengths = [200, 64, 1]
+    H = 6
+    A = synth.to_bf16_bits(synth.delta_rule_A(lengths, H, seed=51))
+    cu = synth.cu_seqlens(lengths)
+    Ad = gh.to_torch_input(A, "bf16", DEV)
+    for algo in ALGOS:
+        X = kt.tril_inv(Ad, torch.from_numpy(cu).to(DEV), out_dtype=gh.out_torch_dtype(x_dtype),
+                        algo=algo)
+        ref = oracle.tril_inv_packed(A, cu, "bf16")
+        assert gh.excess(gh.to_numpy_f64(X), ref, x_dtype) <= 0, algo
+
+
+def test_split_equals_fused_bitwise(kt):
+    """The split path runs the same diagonal and merge arithmetic in the same
+    order, so it matches the fused kernel bit for bit."""
+    d = _cfg("c4_packed_ragged48_h64_f32_bf16")
+    A = torch.from_numpy(d["A"]).to(DEV)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    for dt in (torch.float32, torch.bfloat16):
+        Xf = kt.tril_inv(A, cu, out_dtype=dt, algo="fused")
+        Xs = kt.tril_inv(A, cu, out_dtype=dt, algo="split")
+        assert torch.equal(Xf, Xs)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_garbage_above_diagonal_is_ignored(kt, algo):
+    lengths = [64, 100, 5]
+    H = 4
+    clean = synth.delta_rule_A(lengths, H, seed=61)
+    dirty = synth.delta_rule_A(lengths, H, seed=61, upper="garbage")
+    assert np.isnan(dirty).any() and np.isinf(dirty).any()
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    Xc = kt.tril_inv(torch.from_numpy(clean).to(DEV), cu, algo=algo)
+    Xd = kt.tril_inv(torch.from_numpy(dirty).to(DEV), cu, algo=algo)
+    assert torch.equal(Xc, Xd)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_deterministic(kt, algo):
+    d = _cfg("c3_packed_16x512_h64_f32")
+    A = torch.from_numpy(d["A"]).to(DEV)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    X0 = kt.tril_inv(A, cu, algo=algo)
+    for _ in range(20):
+        assert torch.equal(kt.tril_inv(A, cu, algo=algo), X0)
+
+
+def _host_chunk_map(lengths):
+    m = []
+    for s, n in enumerate(lengths):
+        for c in range((n + 63) // 64):
+            m.append((s, c))
+    return np.array(m, np.int32).reshape(-1, 2)
+
+
+@pytest.mark.parametrize("algo", ["fused", "split"])
+def test_chunk_map_matches_device_scan(kt, algo):
+    rng = np.random.default_rng(71)
+    lengths = [int(v) for v in rng.integers(0, 300, 200)]  # includes empty requests
+    H = 3
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=71)).to(DEV)
+    cu_np = synth.cu_seqlens(lengths)
+    cu = torch.from_numpy(cu_np).to(DEV)
+    cmap = torch.from_numpy(_host_chunk_map(lengths)).to(DEV)
+    X0 = kt.tril_inv(A, cu, algo=algo)
+    X1 = kt.tril_inv(A, cu, algo=algo, chunk_indices=cmap)
+    assert torch.equal(X0, X1)
+    ref = oracle.tril_inv_packed(A.cpu().numpy(), cu_np)
+    assert gh.excess(gh.to_numpy_f64(X0), ref, "f32") <= 0
+
+
+def test_split_workspace_guard_bands(kt):
+    lengths = [512, 77]
+    H = 4
+    T = sum(lengths)
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=81)).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    nbytes, chosen = kt.kda_tril_inv_workspace_size(T, len(lengths), 0, H, "split")
+    assert chosen == "split" and nbytes == (T // 64 + len(lengths)) * H * 4096
+    pad = 1024
+    wbuf = torch.full((nbytes // 4 + 2 * pad,), 777.0, device=DEV)
+    ws = wbuf[pad:pad + nbytes // 4]
+    X = torch.empty_like(A)
+    kt.kda_tril_inv_packed(A, X, cu, workspace=ws, algo="split")
+    torch.cuda.synchronize()
+    assert bool((wbuf[:pad] == 777.0).all()) and bool((wbuf[pad + nbytes // 4:] == 777.0).all())
+    assert torch.equal(X, kt.tril_inv(A, cu, algo="fused"))
+
+
+def test_non_default_stream(kt):
+    lengths = [512] * 4
+    H = 16
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=91)).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    ref = kt.tril_inv(A, cu)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        X = kt.tril_inv(A, cu)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(X, ref)
+
+
+def test_empty_problems_are_noops(kt):
+    A = torch.zeros((0, 4, 64), device=DEV)
+    X = torch.zeros((0, 4, 64), device=DEV)
+    kt.kda_tril_inv_packed(A, X, torch.zeros(1, dtype=torch.int32, device=DEV))
+    A = torch.zeros((64, 4, 64), device=DEV)
+    X = torch.full((64, 4, 64), 5.0, device=DEV)
+    kt.kda_tril_inv_packed(A, X, torch.tensor([0, 0, 0], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert bool((X == 5.0).all())
+    kt.kda_tril_inv_dense(torch.zeros((0, 64, 4, 64), device=DEV),
+                          torch.zeros((0, 64, 4, 64), device=DEV))
+
+
+def test_forced_split_without_workspace_fails(kt):
+    A = torch.zeros((128, 2, 64), device=DEV)
+    X = torch.empty_like(A)
+    cu = torch.tensor([0, 128], dtype=torch.int32, device=DEV)
+    with pytest.raises(kt.KdaError) as e:
+        kt.kda_tril_inv_packed(A, X, cu, algo="split")
+    assert e.value.status == kt.KDA_ERR_WORKSPACE
+    # AUTO without workspace falls back to the fused kernel
+    kt.kda_tril_inv_packed(A, X, cu, algo="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(X[:, 0, :], torch.eye(64, device=DEV).repeat(2, 1))

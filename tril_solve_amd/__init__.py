@@ -1,0 +1,164 @@
+"""Python binding of the MI355X KDA chunk solver (libkda_tril.so).
+
+Argument marshalling only: every step of the solve runs in the HIP kernels
+behind the C ABI of ``include/kda_tril.h``. torch supplies device memory and
+the current stream. There is no CPU fallback: if the library is missing or
+fails to load, importing this package raises.
+
+The functions named like the C entry points take torch tensors and forward
+their data pointers; ``tril_inv`` is the convenience form that allocates X
+(and the split workspace when needed) with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda_tril.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_ALGO_AUTO, KDA_ALGO_FUSED, KDA_ALGO_SPLIT, KDA_ALGO_FUSED_VALU = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = 0, -1, -2, -3, -4
+
+ALGOS = {"auto": KDA_ALGO_AUTO, "fused": KDA_ALGO_FUSED, "split": KDA_ALGO_SPLIT,
+         "fused_valu": KDA_ALGO_FUSED_VALU}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m tril_solve_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+_lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_status_string.argtypes = [ctypes.c_int]
+_lib.kda_tril_inv_workspace_size.restype = ctypes.c_int
+_lib.kda_tril_inv_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.c_int,
+                                             ctypes.POINTER(_sz), ctypes.POINTER(ctypes.c_int)]
+_lib.kda_tril_inv_dense.restype = ctypes.c_int
+_lib.kda_tril_inv_dense.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i32, _p, _sz,
+                                    ctypes.c_int, _p]
+_lib.kda_tril_inv_packed.restype = ctypes.c_int
+_lib.kda_tril_inv_packed.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64, _i32, _p,
+                                     _i64, _p, _sz, ctypes.c_int, _p]
+_lib.kda_tril_auto_plan.restype = ctypes.c_int
+_lib.kda_tril_auto_plan.argtypes = [_i64, _i64, _i32, _sz]
+
+EXPORTED = ("kda_tril_inv_workspace_size", "kda_tril_inv_dense", "kda_tril_inv_packed",
+            "kda_status_string", "kda_tril_auto_plan")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(kda_status_string(status))
+
+
+def kda_status_string(status: int) -> str:
+    return _lib.kda_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        raise KdaError(status)
+
+
+def _algo(a) -> int:
+    return ALGOS[a] if isinstance(a, str) else int(a)
+
+
+def kda_tril_inv_workspace_size(total_tokens: int, num_seqs: int, num_chunks: int,
+                                num_heads: int, algo="auto"):
+    """(workspace bytes, chosen algo name). Host only."""
+    b = _sz(0)
+    c = ctypes.c_int(0)
+    _check(_lib.kda_tril_inv_workspace_size(total_tokens, num_seqs, num_chunks, num_heads,
+                                            _algo(algo), ctypes.byref(b), ctypes.byref(c)))
+    return int(b.value), ALGO_NAMES[c.value]
+
+
+def kda_tril_auto_plan(total_tokens: int, num_chunks: int, num_heads: int,
+                       workspace_bytes: int) -> str:
+    return ALGO_NAMES[_lib.kda_tril_auto_plan(total_tokens, num_chunks, num_heads,
+                                              workspace_bytes)]
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def kda_tril_inv_dense(A, X, workspace=None, algo="auto", stream=None) -> None:
+    """A [B, T, H, 64] -> X [B, T, H, 64] (both cuda, contiguous)."""
+    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 4 and A.shape == X.shape
+    B, T, H, C = A.shape
+    assert C == 64
+    _check(_lib.kda_tril_inv_dense(_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H,
+                                   _ptr(workspace), _ws_bytes(workspace), _algo(algo),
+                                   _stream_ptr(stream)))
+
+
+def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, algo="auto",
+                        stream=None) -> None:
+    """A [T, H, 64] -> X [T, H, 64] for requests given by int32 cu_seqlens."""
+    import torch
+    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 3 and A.shape == X.shape
+    assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    T, H, C = A.shape
+    assert C == 64
+    nch = 0
+    if chunk_indices is not None:
+        assert chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous()
+        nch = chunk_indices.numel() // 2
+    _check(_lib.kda_tril_inv_packed(_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X),
+                                    _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, H,
+                                    _ptr(chunk_indices), nch, _ptr(workspace),
+                                    _ws_bytes(workspace), _algo(algo), _stream_ptr(stream)))
+
+
+def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None, out=None,
+             stream=None):
+    """X = (I + A)^-1 per 64-token chunk and head.
+
+    A: cuda tensor, [T, H, 64] packed (with int32 ``cu_seqlens``) or
+    [B, T, H, 64] dense, float32 or bfloat16. Returns X of ``out_dtype``
+    (default float32), same shape. The split workspace, when the plan needs
+    one, is allocated here with torch.
+    """
+    import torch
+    out_dtype = out_dtype or torch.float32
+    X = out if out is not None else torch.empty(A.shape, dtype=out_dtype, device=A.device)
+    if cu_seqlens is None:
+        B, T, H, _ = A.shape
+        nbytes, _chosen = kda_tril_inv_workspace_size(B * T, B, B * ((T + 63) // 64), H, algo)
+    else:
+        T, H, _ = A.shape
+        nch = 0 if chunk_indices is None else chunk_indices.numel() // 2
+        nbytes, _chosen = kda_tril_inv_workspace_size(T, cu_seqlens.numel() - 1, nch, H, algo)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=A.device) if nbytes else None
+    if cu_seqlens is None:
+        kda_tril_inv_dense(A, X, workspace=ws, algo=algo, stream=stream)
+    else:
+        kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=chunk_indices, workspace=ws,
+                            algo=algo, stream=stream)
+    return X

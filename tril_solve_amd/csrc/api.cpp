@@ -1,0 +1,184 @@
+// C ABI of the KDA chunk solver (declared in include/kda_tril.h).
+//
+// Validates arguments on the host, resolves the plan, fills the kernels'
+// Problem and enqueues them on the caller's stream. Never allocates, copies
+// or synchronises.
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_tril.h"
+#include "plan.h"
+#include "tril_launch.h"
+
+using namespace kda;
+
+namespace {
+
+// Token counts are int32 inside the kernels; keep room for +64 arithmetic.
+constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 64;
+
+bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+bool valid_algo(kda_algo a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_FUSED_VALU; }
+size_t dtype_bytes(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
+
+// One wavefront of 64 lanes per chunk slot and head; the launch must stay
+// below 2^32 threads.
+bool grid_fits(int64_t slots, int32_t H) {
+    return slots <= kMaxTokens && slots * (int64_t)H * 64 < (int64_t)UINT32_MAX;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+kda_status run(const Problem &p, kda_algo algo, int a_bf16, int x_bf16, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    switch (algo) {
+        case KDA_ALGO_FUSED:
+            e = launch_fused_mfma(p, a_bf16, x_bf16, stream);
+            break;
+        case KDA_ALGO_SPLIT:
+            e = launch_split(p, a_bf16, x_bf16, stream);
+            break;
+        case KDA_ALGO_FUSED_VALU:
+            e = launch_fused_valu(p, a_bf16, x_bf16, stream);
+            break;
+        default:
+            return KDA_ERR_INVALID_ARG;
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Checks shared by both layouts; rows = tokens covered by A and X.
+kda_status check_common(const void *A, kda_dtype a_dtype, const void *X, kda_dtype x_dtype,
+                        int64_t rows, int32_t H, kda_algo algo) {
+    if (!valid_dtype(a_dtype) || !valid_dtype(x_dtype) || !valid_algo(algo))
+        return KDA_ERR_INVALID_ARG;
+    if (H <= 0) return KDA_ERR_INVALID_ARG;
+    if (rows > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    if (rows == 0) return KDA_OK;
+    if (A == nullptr || X == nullptr) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(X)) return KDA_ERR_INVALID_ARG;
+    const size_t elems = (size_t)rows * (size_t)H * 64;
+    if (overlap(A, elems * dtype_bytes(a_dtype), X, elems * dtype_bytes(x_dtype)))
+        return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+kda_status plan_call(int64_t rows, int64_t slots, int32_t H, kda_algo algo, void *workspace,
+                     size_t workspace_bytes, kda_algo *chosen) {
+    const size_t offered = workspace ? workspace_bytes : 0;
+    kda_status st = resolve_plan(rows, slots, H, algo, offered, chosen);
+    if (st != KDA_OK) return st;
+    if (*chosen == KDA_ALGO_SPLIT && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK:
+            return "KDA_OK";
+        case KDA_ERR_INVALID_ARG:
+            return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED:
+            return "KDA_ERR_UNSUPPORTED: unsupported size or configuration";
+        case KDA_ERR_WORKSPACE:
+            return "KDA_ERR_WORKSPACE: split path not allowed or workspace too small";
+        case KDA_ERR_HIP:
+            return "KDA_ERR_HIP: kernel launch failed";
+    }
+    return "KDA_ERR_UNKNOWN: unknown status code";
+}
+
+kda_algo kda_tril_auto_plan(int64_t total_tokens, int64_t num_chunks, int32_t num_heads,
+                            size_t workspace_bytes) {
+    kda_algo chosen = KDA_ALGO_FUSED;
+    if (total_tokens <= 0 || num_chunks <= 0 || num_heads <= 0) return KDA_ALGO_FUSED;
+    if (resolve_plan(total_tokens, num_chunks, num_heads, KDA_ALGO_AUTO, workspace_bytes,
+                     &chosen) != KDA_OK)
+        return KDA_ALGO_FUSED;
+    return chosen;
+}
+
+kda_status kda_tril_inv_workspace_size(int64_t total_tokens, int64_t num_seqs,
+                                       int64_t num_chunks, int32_t num_heads, kda_algo algo,
+                                       size_t *bytes, kda_algo *chosen) {
+    if (bytes == nullptr || !valid_algo(algo)) return KDA_ERR_INVALID_ARG;
+    if (total_tokens < 0 || num_seqs < 0 || num_chunks < 0 || num_heads <= 0)
+        return KDA_ERR_INVALID_ARG;
+    if (total_tokens > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks);
+    kda_algo c = KDA_ALGO_FUSED;
+    kda_status st = resolve_plan(total_tokens, slots, num_heads, algo, SIZE_MAX, &c);
+    if (st != KDA_OK) return st;
+    *bytes = (c == KDA_ALGO_SPLIT) ? (size_t)split_workspace_bytes(slots, num_heads) : 0;
+    if (chosen) *chosen = c;
+    return KDA_OK;
+}
+
+kda_status kda_tril_inv_dense(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
+                              int64_t B, int64_t T, int32_t H, void *workspace,
+                              size_t workspace_bytes, kda_algo algo, hipStream_t stream) {
+    if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+    if (B > 0 && T > kMaxTokens / B) return KDA_ERR_UNSUPPORTED;
+    const int64_t rows = B * T;
+    kda_status st = check_common(A, a_dtype, X, x_dtype, rows, H, algo);
+    if (st != KDA_OK || rows == 0) return st;
+    const int64_t slots = B * ((T + 63) / 64);
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    kda_algo chosen = KDA_ALGO_FUSED;
+    st = plan_call(rows, slots, H, algo, workspace, workspace_bytes, &chosen);
+    if (st != KDA_OK) return st;
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    p.A = A;
+    p.X = X;
+    p.ws = static_cast<float *>(workspace);
+    p.num_seqs = (int32_t)B;
+    p.seq_len = (int32_t)T;
+    p.total_tokens = (int32_t)rows;
+    p.heads = H;
+    p.slots = (int32_t)slots;
+    return run(p, chosen, a_dtype == KDA_BF16, x_dtype == KDA_BF16, stream);
+}
+
+kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
+                               const int32_t *cu_seqlens, int64_t num_seqs,
+                               int64_t total_tokens, int32_t H, const int32_t *chunk_indices,
+                               int64_t num_chunks, void *workspace, size_t workspace_bytes,
+                               kda_algo algo, hipStream_t stream) {
+    if (num_seqs < 0 || total_tokens < 0 || num_chunks < 0) return KDA_ERR_INVALID_ARG;
+    if ((chunk_indices == nullptr) != (num_chunks == 0)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs > kMaxTokens || num_chunks > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    kda_status st = check_common(A, a_dtype, X, x_dtype, total_tokens, H, algo);
+    if (st != KDA_OK) return st;
+    if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+    if (cu_seqlens == nullptr) return KDA_ERR_INVALID_ARG;
+    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks);
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    kda_algo chosen = KDA_ALGO_FUSED;
+    st = plan_call(total_tokens, slots, H, algo, workspace, workspace_bytes, &chosen);
+    if (st != KDA_OK) return st;
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    p.A = A;
+    p.X = X;
+    p.cu = cu_seqlens;
+    p.cmap = chunk_indices;
+    p.ws = static_cast<float *>(workspace);
+    p.num_seqs = (int32_t)num_seqs;
+    p.total_tokens = (int32_t)total_tokens;
+    p.heads = H;
+    p.slots = (int32_t)slots;
+    return run(p, chosen, a_dtype == KDA_BF16, x_dtype == KDA_BF16, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Split variant of the KDA chunk solver for gfx950: two kernels in stream
+// order with an FP32 workspace between them.
+//
+// LightLLM PR #1703 ("perf(kda): parallelize diagonal solves in Prefill",
+// commit summary and PR description) keeps FP32 inverse tiles through the
+// merge and bounds the extra scratch by the FP32 input size, choosing the
+// split path by chunk occupancy. Here the diagonal kernel writes the four
+// FP32 16x16 inverse tiles of every chunk-head (4 KiB) to the workspace
+// [slots * H, 4, 16, 16], each tile column-major; the merge kernel reads them
+// with the off-diagonal blocks of A and writes X. Per full chunk-head this
+// moves 8 KiB more than the fused kernel (tiles written once, read once).
+#include "tril_device.h"
+#include "tril_launch.h"
+
+namespace kda {
+
+constexpr int kWsTile = 256;   // floats per 16x16 tile
+constexpr int kWsCol = 16;     // column stride inside a tile (column-major)
+
+template <class EI>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) {
+    __shared__ float lds_all[kFusedWaves * kLdsPerWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    float *lds = lds_all + wid * kLdsPerWave;
+    const long w = (long)blockIdx.x * kFusedWaves + wid;
+    const int slot = (int)(w / p.heads);
+    const int h = (int)(w - (long)slot * p.heads);
+    if (slot >= p.slots) return;
+    const Chunk ch = resolve_chunk(p, slot, lane);
+    if (ch.len <= 0) return;
+
+    const long rstride = (long)p.heads * kChunk;
+    const long base = ((long)ch.start * p.heads + h) * kChunk;
+    const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
+    f4 blk[4][4];
+    load_lower_blocks<EI>(blk, A, rstride, ch.len, lane, true, false);
+    const f4 dA[4] = {blk[0][0], blk[1][1], blk[2][2], blk[3][3]};
+    diag_inverses(lds, dA, lane);
+
+    // lane (b, c) copies column c of tile b: 64 contiguous bytes per lane,
+    // 4 KiB contiguous per wavefront.
+    const int b = lane >> 4, c = lane & 15;
+    float *tile = p.ws + (((long)slot * p.heads + h) * 4 + b) * kWsTile + c * kWsCol;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f4 *>(tile + 4 * q) =
+            *reinterpret_cast<const f4 *>(&lds[b * kXsBlock + c * kXsCol + 4 * q]);
+}
+
+template <class EI, class EO>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const long w = (long)blockIdx.x * kFusedWaves + wid;
+    const int slot = (int)(w / p.heads);
+    const int h = (int)(w - (long)slot * p.heads);
+    if (slot >= p.slots) return;
+    const Chunk ch = resolve_chunk(p, slot, lane);
+    if (ch.len <= 0) return;
+
+    const long rstride = (long)p.heads * kChunk;
+    const long base = ((long)ch.start * p.heads + h) * kChunk;
+    const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
+    typename EO::T *X = static_cast<typename EO::T *>(p.X) + base;
+    const float *tiles = p.ws + ((long)slot * p.heads + h) * 4 * kWsTile;
+
+    f4 blk[4][4];
+    load_lower_blocks<EI>(blk, A, rstride, ch.len, lane, false, true);
+    const MergeOut o = merge_mfma<kWsTile, kWsCol>(tiles, blk[1][0], blk[2][0], blk[2][1],
+                                                   blk[3][0], blk[3][1], blk[3][2], lane);
+    store_x<EO, kWsTile, kWsCol>(X, rstride, ch.len, o, tiles, lane);
+}
+
+template <class EI, class EO>
+static hipError_t launch_split_t(const Problem &p, hipStream_t stream) {
+    const long waves = (long)p.slots * p.heads;
+    const long blocks = (waves + kFusedWaves - 1) / kFusedWaves;
+    hipLaunchKernelGGL((tril_inv_split_diag<EI>), dim3((unsigned)blocks), dim3(kFusedThreads), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tril_inv_split_merge<EI, EO>), dim3((unsigned)blocks),
+                       dim3(kFusedThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_split(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream) {
+    if (!a_bf16 && !x_bf16) return launch_split_t<F32, F32>(p, stream);
+    if (!a_bf16 && x_bf16) return launch_split_t<F32, BF16>(p, stream);
+    if (a_bf16 && !x_bf16) return launch_split_t<BF16, F32>(p, stream);
+    return launch_split_t<BF16, BF16>(p, stream);
+}
+
+}  // namespace kda
