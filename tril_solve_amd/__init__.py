@@ -136,6 +136,26 @@ def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, al
                                     _ws_bytes(workspace), _algo(algo), _stream_ptr(stream)))
 
 
+def prepare_packed(A, X, cu_seqlens, workspace=None, algo="auto", stream=None):
+    """Marshal the arguments of one packed call once and return a function
+    that issues exactly that call (for launch loops that should not pay the
+    per-call Python checks). The tensors must stay alive while it is used."""
+    import torch
+    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 3 and A.shape == X.shape
+    assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    T, H, _ = A.shape
+    args = (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), _ptr(cu_seqlens),
+            cu_seqlens.numel() - 1, T, H, None, 0, _ptr(workspace), _ws_bytes(workspace),
+            _algo(algo), _stream_ptr(stream))
+    fn = _lib.kda_tril_inv_packed
+
+    def call():
+        st = fn(*args)
+        if st != KDA_OK:
+            raise KdaError(st)
+    return call
+
+
 def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None, out=None,
              stream=None):
     """X = (I + A)^-1 per 64-token chunk and head.

@@ -38,14 +38,15 @@ constexpr int kWave = 64;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// LDS per wave (floats). The diagonal A blocks (row-major, block stride
-// kDiagStride) and, after the substitution, the diagonal inverses
-// (column-major: column c of block K at K * kXsBlock + c * kXsCol) share it.
-constexpr int kDiagStride = 16 * 16 + 4;
+// LDS per wave (floats): the diagonal inverses, column-major (column c of
+// block K at K * kXsBlock + c * kXsCol), then a staging tile for the stores.
 constexpr int kXsCol = 20;
 constexpr int kXsBlock = 16 * kXsCol;
-constexpr int kLdsPerWave = 4 * kXsBlock;  // 1280 floats = 5 KiB
-static_assert(4 * kDiagStride <= kLdsPerWave, "diag A must fit in the wave's LDS");
+constexpr int kXsFloats = 4 * kXsBlock;  // 1280 floats = 5 KiB
+// Output staging: one 16-row block row of X, row-major, padded row stride.
+constexpr int kStageRow = 64 + 4;
+constexpr int kStageFloats = 16 * kStageRow;
+constexpr int kLdsPerWave = kXsFloats + kStageFloats;  // 2368 floats = 9.25 KiB
 
 // Orders LDS traffic between lanes of one wavefront (no s_barrier: LDS is
 // processed in order per wave; this stops the compiler from moving accesses).
@@ -70,41 +71,62 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
     return __builtin_bit_cast(float, b << 16);
 }
 
-// Four consecutive elements -> float4 (bf16 -> f32 is exact).
+// Tile I/O goes through buffer resources: a 128-bit descriptor (kept in
+// SGPRs) whose num_records ends right after the last valid row of the
+// chunk-head. The hardware range check then returns 0 for loads of rows past
+// the chunk and drops stores to them, so loads and stores need no per-row
+// branches (and the wave's memory-counter waits stay exact).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access, gfx9-family layout
+
+// Descriptor over rows 0..len-1 (len >= 1) of a chunk-head whose row r
+// starts at base + r * rstride elements.
 template <class E>
-__device__ __forceinline__ f4 load4(const typename E::T *p);
-template <>
-__device__ __forceinline__ f4 load4<F32>(const float *p) {
-    return *reinterpret_cast<const f4 *>(p);
-}
-template <>
-__device__ __forceinline__ f4 load4<BF16>(const uint16_t *p) {
-    uint2 v = *reinterpret_cast<const uint2 *>(p);
-    f4 r;
-    r[0] = bf16_to_f32(v.x & 0xFFFFu);
-    r[1] = bf16_to_f32(v.x >> 16);
-    r[2] = bf16_to_f32(v.y & 0xFFFFu);
-    r[3] = bf16_to_f32(v.y >> 16);
-    return r;
+__device__ __forceinline__ Rsrc tile_rsrc(const typename E::T *base, int rstride, int len) {
+    const uint32_t n = (uint32_t)((len - 1) * rstride + kChunk) * E::kBytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<typename E::T *>(base), 0, n, kRsrcWord3);
 }
 
-// float4 -> four consecutive elements. bf16 uses the hardware round to
-// nearest even (v_cvt_pk_bf16_f32).
+// Four consecutive elements at byte offset `off` -> float4 (bf16 -> f32 is
+// exact); 0 past the descriptor's range.
 template <class E>
-__device__ __forceinline__ void store4(typename E::T *p, f4 v);
+__device__ __forceinline__ f4 load4(Rsrc r, uint32_t off);
 template <>
-__device__ __forceinline__ void store4<F32>(float *p, f4 v) {
-    *reinterpret_cast<f4 *>(p) = v;
+__device__ __forceinline__ f4 load4<F32>(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 template <>
-__device__ __forceinline__ void store4<BF16>(uint16_t *p, f4 v) {
+__device__ __forceinline__ f4 load4<BF16>(Rsrc r, uint32_t off) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    f4 o;
+    o[0] = bf16_to_f32(v[0] & 0xFFFFu);
+    o[1] = bf16_to_f32(v[0] >> 16);
+    o[2] = bf16_to_f32(v[1] & 0xFFFFu);
+    o[3] = bf16_to_f32(v[1] >> 16);
+    return o;
+}
+
+// float4 -> four consecutive elements at byte offset `off`, as a nontemporal
+// store (X is written once and not read again here, so it should not displace
+// cached lines); dropped past the descriptor's range. bf16 uses the hardware
+// round to nearest even (v_cvt_pk_bf16_f32).
+constexpr int kNontemporal = 2;  // cache-policy bit of buffer stores
+template <class E>
+__device__ __forceinline__ void store4(Rsrc r, uint32_t off, f4 v);
+template <>
+__device__ __forceinline__ void store4<F32>(Rsrc r, uint32_t off, f4 v) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kNontemporal);
+}
+template <>
+__device__ __forceinline__ void store4<BF16>(Rsrc r, uint32_t off, f4 v) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    b2 lo = {(__bf16)v[0], (__bf16)v[1]};
-    b2 hi = {(__bf16)v[2], (__bf16)v[3]};
-    uint2 o;
-    o.x = __builtin_bit_cast(uint32_t, lo);
-    o.y = __builtin_bit_cast(uint32_t, hi);
-    *reinterpret_cast<uint2 *>(p) = o;
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const b2 lo = {(__bf16)v[0], (__bf16)v[1]};
+    const b2 hi = {(__bf16)v[2], (__bf16)v[3]};
+    const u2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    __builtin_amdgcn_raw_buffer_store_b64(o, r, off, 0, kNontemporal);
 }
 
 // ------------------------------------------------------------ chunk resolution
@@ -181,40 +203,15 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
     return ch;
 }
 
-// ------------------------------------------------------------ small helpers
+// The chunk is the same for every lane of the wave: keep it in SGPRs so the
+// tile's base pointers and row arithmetic stay scalar.
+__device__ __forceinline__ Chunk uniform(Chunk c) {
+    c.start = __builtin_amdgcn_readfirstlane(c.start);
+    c.len = __builtin_amdgcn_readfirstlane(c.len);
+    return c;
+}
 
-// 4 x 4 transpose inside each lane quad: in reg r of lane t (t = l % 4) the
-// value V[t][r]; out reg r of lane t holds V[r][t]. Two DPP swap stages.
-__device__ __forceinline__ float dpp_swap1(float v) {  // quad_perm [1,0,3,2]
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
-                                                              0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_swap2(float v) {  // quad_perm [2,3,0,1]
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
-                                                              0xF, 0xF, false));
-}
-__device__ __forceinline__ f4 quad_transpose(f4 v, int lane) {
-    const bool t0 = lane & 1, t1 = lane & 2;
-    f4 u;
-    {
-        const float a0 = dpp_swap1(v[0]), a1 = dpp_swap1(v[1]);
-        const float a2 = dpp_swap1(v[2]), a3 = dpp_swap1(v[3]);
-        u[0] = t0 ? a1 : v[0];
-        u[1] = t0 ? v[1] : a0;
-        u[2] = t0 ? a3 : v[2];
-        u[3] = t0 ? v[3] : a2;
-    }
-    f4 w;
-    {
-        const float b0 = dpp_swap2(u[0]), b1 = dpp_swap2(u[1]);
-        const float b2 = dpp_swap2(u[2]), b3 = dpp_swap2(u[3]);
-        w[0] = t1 ? b2 : u[0];
-        w[1] = t1 ? b3 : u[1];
-        w[2] = t1 ? u[2] : b0;
-        w[3] = t1 ? u[3] : b1;
-    }
-    return w;
-}
+// ------------------------------------------------------------ small helpers
 
 // 16 x 16 x 16 product on the matrix cores: acc + P * Q with P in OPND_A and
 // Q in OPND_O layout (reduction index k = 4g + s at step s).
@@ -228,50 +225,72 @@ __device__ __forceinline__ f4 mma16(f4 P, f4 Q, f4 acc) {
 
 // --------------------------------------------------- diagonal block inverses
 
-// Input: lane (g, i) holds row i, columns 4g..4g+3 of each diagonal block
-// A_KK (OPND_A layout, rows past the chunk already zero). Stores the strictly
-// lower part (others forced to 0 by select, so NaN/Inf there cannot leak) to
-// LDS, runs the four 16-step forward substitutions, one lane per
-// (block b = lane / 16, column c = lane % 16), and leaves X_KK column-major in
-// LDS: column c of block K at lds[K * kXsBlock + c * kXsCol + row].
-__device__ __forceinline__ void diag_inverses(float *lds, const f4 dA[4], int lane) {
-    const int g = lane >> 4, m = lane & 15;
+// Value of v in lane I of this lane's 16-lane row (DPP row_newbcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x150 + I, 0xF, 0xF, false));
+}
+
+// Row I of the substitution: x_I = -sum_{j<I} A[I][j] x_j (j increasing),
+// kept only below the diagonal (x_I stays 0 above it and 1 on it).
+template <int I>
+__device__ __forceinline__ void subst_row(const float (&arow)[16], float (&x)[16], int c) {
+    float acc = 0.0f;
 #pragma unroll
-    for (int K = 0; K < 4; ++K) {
-        f4 v;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) v[s] = (4 * g + s < m) ? dA[K][s] : 0.0f;
-        *reinterpret_cast<f4 *>(&lds[K * kDiagStride + m * 16 + 4 * g]) = v;
-    }
-    wave_sync();
-    const int b = g, c = m;
-    const float *row = lds + b * kDiagStride;
+    for (int j = 0; j < I; ++j) acc = __builtin_fmaf(row_bcast<I>(arow[j]), x[j], acc);
+    x[I] = (I > c) ? -acc : x[I];
+}
+
+// Four 16x16 forward substitutions at once, one lane per (block b, column
+// c), b = lane / 16, c = lane % 16. Input: lane (b, i) holds row i of the
+// diagonal block A_bb (16 floats, rows past the chunk already 0); entry
+// A_bb[i][j] reaches the lanes of row b through a DPP broadcast from lane i,
+// and only j < i is ever broadcast, so whatever is stored on or above the
+// diagonal of A never enters the arithmetic. Output: X_bb column-major in
+// LDS, column c of block b at xs[b * kXsBlock + c * kXsCol + row].
+__device__ __forceinline__ void diag_inverses(float *xs, const float (&arow)[16], int lane) {
+    const int b = lane >> 4, c = lane & 15;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int q = 0; q < (i + 3) / 4; ++q) {
-            const f4 a = *reinterpret_cast<const f4 *>(&row[i * 16 + 4 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * q + e < i) acc = __builtin_fmaf(a[e], x[4 * q + e], acc);
-        }
-        x[i] = (i > c) ? -acc : x[i];
-    }
-    wave_sync();
+    subst_row<1>(arow, x, c);
+    subst_row<2>(arow, x, c);
+    subst_row<3>(arow, x, c);
+    subst_row<4>(arow, x, c);
+    subst_row<5>(arow, x, c);
+    subst_row<6>(arow, x, c);
+    subst_row<7>(arow, x, c);
+    subst_row<8>(arow, x, c);
+    subst_row<9>(arow, x, c);
+    subst_row<10>(arow, x, c);
+    subst_row<11>(arow, x, c);
+    subst_row<12>(arow, x, c);
+    subst_row<13>(arow, x, c);
+    subst_row<14>(arow, x, c);
+    subst_row<15>(arow, x, c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         f4 v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-        *reinterpret_cast<f4 *>(&lds[b * kXsBlock + c * kXsCol + 4 * q]) = v;
+        *reinterpret_cast<f4 *>(&xs[b * kXsBlock + c * kXsCol + 4 * q]) = v;
     }
     wave_sync();
 }
 
-// X_KK from a column-major copy (LDS or the split workspace) in the three
-// register layouts. Column c of block K starts at K * BS + c * CS.
+// Lane (b, i) loads row 16b + i, columns 16b..16b+15 (the row of diagonal
+// block b); rows past the chunk read as 0.
+template <class E>
+__device__ __forceinline__ void load_diag_rows(float (&arow)[16], Rsrc A, int rstride, int lane) {
+    const int b = lane >> 4, i = lane & 15;
+    const uint32_t off = (uint32_t)((16 * b + i) * rstride + 16 * b) * E::kBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f4 v = load4<E>(A, off + 4 * q * E::kBytes);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) arow[4 * q + e] = v[e];
+    }
+}
+
 template <int BS, int CS>
 __device__ __forceinline__ f4 xs_opnd_o(const float *xs, int K, int lane) {
     const int g = lane >> 4, n = lane & 15;
@@ -285,112 +304,115 @@ __device__ __forceinline__ f4 xs_opnd_a_neg(const float *xs, int K, int lane) {
     for (int s = 0; s < 4; ++s) r[s] = -xs[K * BS + (4 * g + s) * CS + m];
     return r;
 }
-template <int BS, int CS>
-__device__ __forceinline__ f4 xs_store(const float *xs, int K, int lane) {
-    const int g = lane >> 4, q = (lane >> 2) & 3, t = lane & 3;
-    f4 r;
+// Loads of the six blocks below the diagonal: lane (g, m) takes row
+// 16I + m, columns 16K + 4g..+3 of block (I, K), K < I (OPND_A layout).
+// Rows past the chunk read as 0.
+template <class E>
+__device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], Rsrc A, int rstride, int lane) {
+    const int g = lane >> 4, m = lane & 15;
+    const uint32_t off = (uint32_t)(m * rstride + 4 * g) * E::kBytes;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r[s] = xs[K * BS + (4 * q + s) * CS + 4 * g + t];
-    return r;
+    for (int I = 1; I < 4; ++I)
+#pragma unroll
+        for (int K = 0; K < I; ++K)
+            blk[I][K] = load4<E>(A, off + (uint32_t)(16 * I * rstride + 16 * K) * E::kBytes);
 }
 
-// Merge products on the matrix cores: A blocks in OPND_A layout, diagonal
-// inverses from a column-major copy; results X_IJ (I > J) in OPND_O layout.
-struct MergeOut {
-    f4 x10, x21, x32, x20, x31, x30;
+// Registers of one chunk-head's input tile: the rows of the diagonal blocks
+// (load_diag_rows layout) and the six blocks below the diagonal (OPND_A).
+struct Tile {
+    float arow[16];
+    f4 blk[4][4];  // blk[I][K] for K < I
 };
 
-template <int BS, int CS>
-__device__ __forceinline__ MergeOut merge_mfma(const float *xs, const f4 a10, const f4 a20,
-                                               const f4 a21, const f4 a30, const f4 a31,
-                                               const f4 a32, int lane) {
-    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f4 x00 = xs_opnd_o<BS, CS>(xs, 0, lane);
-    const f4 x11 = xs_opnd_o<BS, CS>(xs, 1, lane);
-    const f4 x22 = xs_opnd_o<BS, CS>(xs, 2, lane);
-    const f4 n11 = xs_opnd_a_neg<BS, CS>(xs, 1, lane);
-    const f4 n22 = xs_opnd_a_neg<BS, CS>(xs, 2, lane);
-    const f4 n33 = xs_opnd_a_neg<BS, CS>(xs, 3, lane);
-    MergeOut o;
-    // level 1, plus the first terms of levels 2 and 3 (they need only X_KK)
-    const f4 s10 = mma16(a10, x00, z);
-    const f4 s21 = mma16(a21, x11, z);
-    const f4 s32 = mma16(a32, x22, z);
-    f4 s20 = mma16(a20, x00, z);
-    f4 s31 = mma16(a31, x11, z);
-    f4 s30 = mma16(a30, x00, z);
-    o.x10 = mma16(n11, s10, z);
-    o.x21 = mma16(n22, s21, z);
-    o.x32 = mma16(n33, s32, z);
-    // level 2
-    s20 = mma16(a21, o.x10, s20);
-    s31 = mma16(a32, o.x21, s31);
-    s30 = mma16(a31, o.x10, s30);
-    o.x20 = mma16(n22, s20, z);
-    o.x31 = mma16(n33, s31, z);
-    // level 3
-    s30 = mma16(a32, o.x20, s30);
-    o.x30 = mma16(n33, s30, z);
-    return o;
-}
-
-// Loads of the blocks on and below the diagonal: lane (g, m) takes row
-// 16I + m, columns 16K + 4g..+3 of block (I, K), K <= I (and K >= kmin).
-// Rows at or past `len` read as 0.
 template <class E>
-__device__ __forceinline__ void load_lower_blocks(f4 blk[4][4], const typename E::T *A, long rstride,
-                                                  int len, int lane, bool diag, bool offdiag) {
-    const int g = lane >> 4, m = lane & 15;
-    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const int r = 16 * I + m;
-        const bool ok = r < len;
-        const typename E::T *row = A + (long)r * rstride + 4 * g;
-#pragma unroll
-        for (int K = 0; K <= I; ++K) {
-            const bool want = (K == I) ? diag : offdiag;
-            blk[I][K] = (want && ok) ? load4<E>(row + 16 * K) : z;
-        }
-    }
+__device__ __forceinline__ void load_tile(Tile &t, Rsrc A, int rstride, int lane) {
+    load_diag_rows<E>(t.arow, A, rstride, lane);
+    load_offdiag_blocks<E>(t.blk, A, rstride, lane);
 }
 
-// Writes the 64 rows of X for one chunk-head: row-block I gets X_IJ (J < I)
-// from OPND_O registers, X_II from the column-major copy, zeros for J > I.
-// Lane (g, 4q + t) writes row 16I + 4g + t, columns 16J + 4q..+3; rows at or
-// past `len` are not written.
-template <class E, int BS, int CS>
-__device__ __forceinline__ void store_x(typename E::T *X, long rstride, int len, const MergeOut &o,
-                                        const float *xs, int lane) {
-    const int g = lane >> 4, q = (lane >> 2) & 3, t = lane & 3;
-    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f4 xo[4][4] = {
-        {z, z, z, z},
-        {o.x10, z, z, z},
-        {o.x20, o.x21, z, z},
-        {o.x30, o.x31, o.x32, z},
-    };
+// Writes rows 16I..16I+15 of X (those inside the descriptor) through the LDS staging
+// tile so that every store instruction covers four whole 64-column rows
+// (16 lanes x 16 bytes per row for fp32): X_IJ (J < I) from OPND_O
+// registers xo[J], X_II from the column-major copy xs, and the zero upper
+// triangle (columns past 16(I + 1)) without touching LDS.
+template <class E, int BS, int CS, int I>
+__device__ __forceinline__ void store_block_row(Rsrc X, int rstride, const f4 (&xo)[4],
+                                                const float *xs, float *stage, int lane) {
+    const int g = lane >> 4, n = lane & 15;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        // DPP transposes read neighbouring lanes, so they run with every lane
-        // active; only the stores are masked by row.
-        f4 v[4];
+    for (int J = 0; J <= I; ++J) {
+        const f4 v = (J < I) ? xo[J] : xs_opnd_o<BS, CS>(xs, I, lane);
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            if (J < I)
-                v[J] = quad_transpose(xo[I][J], lane);
-            else if (J == I)
-                v[J] = xs_store<BS, CS>(xs, I, lane);
-            else
-                v[J] = z;
-        }
-        const int r = 16 * I + 4 * g + t;
-        if (r < len) {
-            typename E::T *row = X + (long)r * rstride + 4 * q;
-#pragma unroll
-            for (int J = 0; J < 4; ++J) store4<E>(row + 16 * J, v[J]);
-        }
+        for (int r = 0; r < 4; ++r) stage[(4 * g + r) * kStageRow + 16 * J + n] = v[r];
     }
+    wave_sync();
+    const int r4 = lane >> 4, c4 = (lane & 15) * 4;
+    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t off = (uint32_t)(r4 * rstride + c4) * E::kBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + r4;
+        f4 v = z;
+        if (c4 < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * kStageRow + c4]);
+        store4<E>(X, off + (uint32_t)((16 * I + 4 * i) * rstride) * E::kBytes, v);
+    }
+    wave_sync();
+}
+
+// Merge products on the matrix cores: mm(P, Q, acc) = acc + P Q with P in
+// OPND_A and Q in OPND_O; negx(I, S) = -X_II S with X_II read (negated, in
+// OPND_A) from the column-major copy xs.
+template <int BS, int CS>
+struct MfmaEngine {
+    const float *xs;
+    int lane;
+    __device__ __forceinline__ f4 mm(f4 P, f4 Q, f4 acc) const { return mma16(P, Q, acc); }
+    __device__ __forceinline__ f4 negx(int I, f4 S) const {
+        const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        return mma16(xs_opnd_a_neg<BS, CS>(xs, I, lane), S, z);
+    }
+};
+
+// Block merge and stores, one block row at a time (the rows of block row I
+// are written as soon as X_I0..X_II are known):
+//   X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ,  I > J,
+// FP32 throughout. X_KK come from the column-major copy xs (LDS in the fused
+// kernel, the workspace in the split path); the products run in the same
+// order in both, so their results agree bit for bit.
+template <class E, int BS, int CS, class Eng>
+__device__ __forceinline__ void merge_and_store(const Eng &eng, const f4 (&blk)[4][4],
+                                                const float *xs, float *stage, Rsrc X,
+                                                int rstride, int len, int lane) {
+    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4 xo[4] = {z, z, z, z};
+    store_block_row<E, BS, CS, 0>(X, rstride, xo, xs, stage, lane);
+    if (len <= 16) return;
+    // block row 1
+    const f4 x00 = xs_opnd_o<BS, CS>(xs, 0, lane);
+    const f4 x10 = eng.negx(1, eng.mm(blk[1][0], x00, z));
+    xo[0] = x10;
+    store_block_row<E, BS, CS, 1>(X, rstride, xo, xs, stage, lane);
+    if (len <= 32) return;
+    // block row 2
+    const f4 x11 = xs_opnd_o<BS, CS>(xs, 1, lane);
+    const f4 s21 = eng.mm(blk[2][1], x11, z);
+    const f4 s20 = eng.mm(blk[2][1], x10, eng.mm(blk[2][0], x00, z));
+    const f4 x21 = eng.negx(2, s21);
+    const f4 x20 = eng.negx(2, s20);
+    xo[0] = x20;
+    xo[1] = x21;
+    store_block_row<E, BS, CS, 2>(X, rstride, xo, xs, stage, lane);
+    if (len <= 48) return;
+    // block row 3
+    const f4 x22 = xs_opnd_o<BS, CS>(xs, 2, lane);
+    const f4 s32 = eng.mm(blk[3][2], x22, z);
+    const f4 s31 = eng.mm(blk[3][2], x21, eng.mm(blk[3][1], x11, z));
+    const f4 s30 = eng.mm(blk[3][2], x20, eng.mm(blk[3][1], x10, eng.mm(blk[3][0], x00, z)));
+    xo[0] = eng.negx(3, s30);
+    xo[1] = eng.negx(3, s31);
+    xo[2] = eng.negx(3, s32);
+    store_block_row<E, BS, CS, 3>(X, rstride, xo, xs, stage, lane);
 }
 
 }  // namespace kda

@@ -25,6 +25,10 @@ struct Problem {
 constexpr int kFusedWaves = 4;  // independent wavefronts per workgroup
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
+// Workgroups of `threads` threads of kernel `fn` that the current device
+// holds at once (occupancy x compute units); 0 when unknown. Cached.
+long resident_blocks(const void *fn, int threads);
+
 hipError_t launch_fused_mfma(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);
 hipError_t launch_split(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);
 hipError_t launch_fused_valu(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);

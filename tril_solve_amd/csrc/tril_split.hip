@@ -19,24 +19,23 @@ constexpr int kWsCol = 16;     // column stride inside a tile (column-major)
 
 template <class EI>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) {
-    __shared__ float lds_all[kFusedWaves * kLdsPerWave];
+    __shared__ float lds_all[kFusedWaves * kXsFloats];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    float *lds = lds_all + wid * kLdsPerWave;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float *lds = lds_all + wid * kXsFloats;
     const long w = (long)blockIdx.x * kFusedWaves + wid;
     const int slot = (int)(w / p.heads);
     const int h = (int)(w - (long)slot * p.heads);
     if (slot >= p.slots) return;
-    const Chunk ch = resolve_chunk(p, slot, lane);
+    const Chunk ch = uniform(resolve_chunk(p, slot, lane));
     if (ch.len <= 0) return;
 
-    const long rstride = (long)p.heads * kChunk;
+    const int rstride = p.heads * kChunk;
     const long base = ((long)ch.start * p.heads + h) * kChunk;
     const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
-    f4 blk[4][4];
-    load_lower_blocks<EI>(blk, A, rstride, ch.len, lane, true, false);
-    const f4 dA[4] = {blk[0][0], blk[1][1], blk[2][2], blk[3][3]};
-    diag_inverses(lds, dA, lane);
+    float arow[16];
+    load_diag_rows<EI>(arow, tile_rsrc<EI>(A, rstride, ch.len), rstride, lane);
+    diag_inverses(lds, arow, lane);
 
     // lane (b, c) copies column c of tile b: 64 contiguous bytes per lane,
     // 4 KiB contiguous per wavefront.
@@ -50,26 +49,28 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) 
 
 template <class EI, class EO>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p) {
+    __shared__ float stage_all[kFusedWaves * kStageFloats];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float *stage = stage_all + wid * kStageFloats;
     const long w = (long)blockIdx.x * kFusedWaves + wid;
     const int slot = (int)(w / p.heads);
     const int h = (int)(w - (long)slot * p.heads);
     if (slot >= p.slots) return;
-    const Chunk ch = resolve_chunk(p, slot, lane);
+    const Chunk ch = uniform(resolve_chunk(p, slot, lane));
     if (ch.len <= 0) return;
 
-    const long rstride = (long)p.heads * kChunk;
+    const int rstride = p.heads * kChunk;
     const long base = ((long)ch.start * p.heads + h) * kChunk;
     const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
     typename EO::T *X = static_cast<typename EO::T *>(p.X) + base;
     const float *tiles = p.ws + ((long)slot * p.heads + h) * 4 * kWsTile;
 
     f4 blk[4][4];
-    load_lower_blocks<EI>(blk, A, rstride, ch.len, lane, false, true);
-    const MergeOut o = merge_mfma<kWsTile, kWsCol>(tiles, blk[1][0], blk[2][0], blk[2][1],
-                                                   blk[3][0], blk[3][1], blk[3][2], lane);
-    store_x<EO, kWsTile, kWsCol>(X, rstride, ch.len, o, tiles, lane);
+    load_offdiag_blocks<EI>(blk, tile_rsrc<EI>(A, rstride, ch.len), rstride, lane);
+    const MfmaEngine<kWsTile, kWsCol> eng{tiles, lane};
+    merge_and_store<EO, kWsTile, kWsCol>(eng, blk, tiles, stage, tile_rsrc<EO>(X, rstride, ch.len),
+                                         rstride, ch.len, lane);
 }
 
 template <class EI, class EO>
