@@ -27,10 +27,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
-# Pages' H200 time for the same workload (8192 tokens, 64 heads) after the
-# change they describe: 0.476 ms per solve -> inverses per second.
-H200_INV_PER_S = 8192 / 0.476e-3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_c3.json")
+# The pages' H200 solver times after the change they describe (context: a
+# different GPU, dtypes not stated), as inverses per second:
+#   8192 tokens x 64 heads (8192 matrices): 0.476 ms;  64 tokens x 64 heads: 0.0254 ms.
+H200_INV_PER_S = {"packed_16x512_h64_f32": 8192 / 0.476e-3, "packed_1x64_h64_f32": 64 / 0.0254e-3}
+WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_16x512_h64_f32",
+             "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32"]
+MAIN_WORKLOAD = "packed_16x512_h64_f32"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_packed16x512.json")
 KERNEL_SOURCES = ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
 
 
@@ -89,16 +93,30 @@ def cpu_baseline(d, budget_s=12.0):
                       f"by the fp64 oracle in {el:.1f} s"}
 
 
+def describe(d) -> str:
+    if d["layout"] == "dense":
+        shape = f"dense B={d['B']} x T={d['T']}"
+    elif len(set(d["lengths"])) == 1:
+        shape = f"packed {len(d['lengths'])} x {d['lengths'][0]} tokens"
+    else:
+        shape = f"packed {len(d['lengths'])} ragged requests, {d['T_total']} tokens"
+    return (f"{shape}, {d['H']} heads, {d['a_dtype']} A -> {d['x_dtype']} X "
+            f"({d['num_chunks'] * d['H']} chunk-head 64x64 matrices)")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "split", "fused_valu"])
-    ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--workload", default=MAIN_WORKLOAD, choices=WORKLOADS,
+                    help="the default is the metric's workload; the others are diagnostics")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating input/output buffer sets (default: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", choices=["copy"], default=None,
-                    help="run only a torch copy of the same byte count (counter calibration)")
+                    help="run only a plain copy of A's byte count (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -106,54 +124,80 @@ def main() -> int:
             "chunk-heads with no communication and is not part of this build.")
         return 2
 
-    import numpy as np
+    import numpy as np  # noqa: F401
     import torch
 
     import synth
     import tril_solve_amd as kt
 
     dev = torch.device("cuda:0")
-    name = "c3_packed_16x512_h64_f32"
-    cfg = synth.CONFIGS[name]
-    sets = []
-    for i in range(args.sets):
-        c = dict(cfg)
-        c["seed"] = cfg["seed"] + 100 * i
-        d = synth.make(c)
-        A = torch.from_numpy(d["A"]).to(dev)
-        X = torch.empty(A.shape, dtype=torch.float32, device=dev)
-        sets.append((A, X))
-        if i == 0:
-            d0 = d
-    cu = torch.from_numpy(d0["cu_seqlens"]).to(dev)
+    cfg = synth.CONFIGS[args.workload]
+    d0 = synth.make(cfg)
+    a_bytes = 2 if cfg["a_dtype"] == "bf16" else 4
+    x_bytes = 2 if cfg["x_dtype"] == "bf16" else 4
     H = cfg["H"]
     T = d0["T_total"]
     mats = d0["num_chunks"] * H
-    bytes_alg = algorithmic_bytes(d0["lengths"], H, 4, 4)
-    nbytes, chosen = kt.kda_tril_inv_workspace_size(T, len(d0["lengths"]), 0, H, args.algo)
+    bytes_alg = algorithmic_bytes(d0["lengths"], H, a_bytes, x_bytes)
+    nsets = args.sets or max(1, min(4, -(-(1 << 30) // bytes_alg)))
+    x_dt = torch.bfloat16 if cfg["x_dtype"] == "bf16" else torch.float32
+
+    def to_dev(d):
+        if cfg["a_dtype"] == "bf16":
+            return torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(d["A"]).to(dev)
+
+    sets = []
+    for i in range(nsets):
+        d = d0
+        if i:
+            c = dict(cfg)
+            c["seed"] = cfg["seed"] + 100 * i
+            d = synth.make(c)
+        A = to_dev(d)
+        sets.append((A, torch.empty(A.shape, dtype=x_dt, device=dev)))
+    dense = cfg["layout"] == "dense"
+    cu = None if dense else torch.from_numpy(d0["cu_seqlens"]).to(dev)
+    if dense:
+        nbytes, chosen = kt.kda_tril_inv_workspace_size(T, cfg["B"], d0["num_chunks"], H,
+                                                        args.algo)
+    else:
+        nbytes, chosen = kt.kda_tril_inv_workspace_size(T, len(d0["lengths"]), 0, H, args.algo)
     ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=dev) if nbytes else None
     torch.cuda.synchronize()
 
+    stream = torch.cuda.current_stream()
     probe = load_copy_probe()
 
-    def copy(A, X):
-        st = probe.kda_probe_copy_f32(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(X.data_ptr()),
-                                      A.numel(), ctypes.c_void_p(stream.cuda_stream))
+    # The copy probe has destinations of its own, each exactly the byte size of
+    # its source (X may be narrower than A, e.g. bf16 X from fp32 A).
+    copy_dst = {}
+
+    def copy(A, _X=None):
+        nbytes = A.numel() * A.element_size()
+        D = copy_dst.get(A.data_ptr())
+        if D is None:
+            D = copy_dst[A.data_ptr()] = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        if nbytes % 16 or D.numel() * 4 != nbytes:
+            raise RuntimeError("copy probe: source and destination sizes differ")
+        st = probe.kda_probe_copy_f32(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()),
+                                      nbytes // 4, ctypes.c_void_p(stream.cuda_stream))
         if st != 0:
             raise RuntimeError(f"copy probe failed ({st})")
 
-    stream = torch.cuda.current_stream()
     if args.probe == "copy":
         for _ in range(args.warmup + args.steps):
             for A, X in sets:
                 copy(A, X)
         torch.cuda.synchronize()
         log(f"copy probe: {args.warmup + args.steps} x {len(sets)} copies of "
-            f"{A.numel() * 4} bytes read + written")
+            f"{A.numel() * A.element_size()} bytes read + written")
         return 0
 
-    calls = [kt.prepare_packed(A, X, cu, workspace=ws, algo=args.algo, stream=None)
-             for A, X in sets]
+    if dense:
+        calls = [kt.prepare_dense(A, X, workspace=ws, algo=args.algo) for A, X in sets]
+    else:
+        calls = [kt.prepare_packed(A, X, cu, workspace=ws, algo=args.algo) for A, X in sets]
 
     for i in range(args.warmup):
         calls[i % len(calls)]()
@@ -173,24 +217,29 @@ def main() -> int:
     el = time.perf_counter() - t0
     k_avg = e0.elapsed_time(e1) * 1e-3 / args.steps  # seconds per launch
 
-    # measured copy roofline: a plain streaming copy of the same byte count
-    # (A's size read + written), same buffer rotation, events over the region
-    for i in range(4):
-        copy(*sets[i % len(sets)])
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    ncopy = 40
-    c0.record(stream)
-    for i in range(ncopy):
-        copy(*sets[i % len(sets)])
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_s = c0.elapsed_time(c1) * 1e-3 / ncopy
-    copy_gbs = 2 * sets[0][0].numel() * 4 / copy_s / 1e9
+    # measured copy roofline: a plain streaming copy of A's byte count, read
+    # and written, same buffer rotation, events over the region
+    if a_bytes == 4:
+        for i in range(4):
+            copy(*sets[i % len(sets)])
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        ncopy = 40
+        c0.record(stream)
+        for i in range(ncopy):
+            copy(*sets[i % len(sets)])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_s = c0.elapsed_time(c1) * 1e-3 / ncopy
+        copy_gbs = 2 * sets[0][0].numel() * 4 / copy_s / 1e9
+    else:
+        copy_gbs = None
 
     value = mats * args.steps / el
     achieved = bytes_alg / k_avg / 1e9
-    traffic = load_traffic(bytes_alg)
+    traffic = load_traffic(bytes_alg) if args.workload == MAIN_WORKLOAD and args.algo in (
+        "auto", "fused") and chosen == "fused" else None
+    h200 = H200_INV_PER_S.get(args.workload)
     out = {
         "metric": "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads",
         "value": value,
@@ -201,12 +250,12 @@ def main() -> int:
         "ms_per_step": el / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": value / H200_INV_PER_S,
+        "vs_baseline": (value / h200) if h200 else None,
         "dtype": "f32",
-        "data": "synthetic (seeded delta-rule generator, 4 rotating buffer sets)",
-        "config": {"workload": "packed 16 requests x 512 tokens, 64 heads, fp32 A -> fp32 X "
-                               "(8192 chunk-head 64x64 matrices)",
-                   "tokens": T, "heads": H, "requests": len(d0["lengths"]), "matrices": mats,
+        "data": f"synthetic (seeded delta-rule generator, {len(sets)} rotating buffer sets)",
+        "config": {"workload": describe(d0), "tokens": T, "heads": H,
+                   "requests": len(d0["lengths"]), "matrices": mats,
+                   "a_dtype": cfg["a_dtype"], "x_dtype": cfg["x_dtype"],
                    "algo": args.algo, "plan": chosen},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
@@ -214,7 +263,7 @@ def main() -> int:
         "algorithmic_bytes_per_launch": bytes_alg,
         "copy_roofline_gbs": copy_gbs,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == MAIN_WORKLOAD:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(d0)
     else:

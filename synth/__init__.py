@@ -34,18 +34,19 @@ import numpy as np
 CHUNK = 64
 KEY_DIM = 128
 
-# The five workloads: name -> layout, request lengths (or dense B, T), heads,
-# input and output dtypes, data seed.
+# The five workloads, each named by its layout, request lengths, heads and
+# dtypes. Fields: layout, request lengths (or dense B, T), heads, input and
+# output dtypes, data seed.
 CONFIGS = {
-    "c1_packed_1x64_h64_f32": dict(layout="packed", lengths=[64], H=64, a_dtype="f32",
+    "packed_1x64_h64_f32": dict(layout="packed", lengths=[64], H=64, a_dtype="f32",
                                    x_dtype="f32", seed=0),
-    "c2_dense_b4_t512_h16_bf16_f32": dict(layout="dense", B=4, T=512, H=16, a_dtype="bf16",
+    "dense_b4_t512_h16_bf16_f32": dict(layout="dense", B=4, T=512, H=16, a_dtype="bf16",
                                           x_dtype="f32", seed=1),
-    "c3_packed_16x512_h64_f32": dict(layout="packed", lengths=[512] * 16, H=64, a_dtype="f32",
+    "packed_16x512_h64_f32": dict(layout="packed", lengths=[512] * 16, H=64, a_dtype="f32",
                                      x_dtype="f32", seed=2),
-    "c4_packed_ragged48_h64_f32_bf16": dict(layout="packed", lengths="ragged48", H=64,
+    "packed_ragged48_h64_f32_bf16": dict(layout="packed", lengths="ragged48", H=64,
                                             a_dtype="f32", x_dtype="bf16", seed=3),
-    "c5_packed_1x131072_h64_f32": dict(layout="packed", lengths=[131072], H=64,
+    "packed_1x131072_h64_f32": dict(layout="packed", lengths=[131072], H=64,
                                        a_dtype="f32", x_dtype="f32", seed=4),
 }
 

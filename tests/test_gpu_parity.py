@@ -59,8 +59,8 @@ def _cfg(name):
     return _CFG_CACHE[name]
 
 
-SMALL_CFGS = ["c1_packed_1x64_h64_f32", "c2_dense_b4_t512_h16_bf16_f32",
-              "c3_packed_16x512_h64_f32", "c4_packed_ragged48_h64_f32_bf16"]
+SMALL_CFGS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32",
+              "packed_16x512_h64_f32", "packed_ragged48_h64_f32_bf16"]
 
 
 @pytest.mark.parametrize("algo", ALGOS + ["auto"])
@@ -92,7 +92,7 @@ def test_config_parity(kt, name, algo):
 
 @pytest.fixture(scope="module")
 def c5():
-    name = "c5_packed_1x131072_h64_f32"
+    name = "packed_1x131072_h64_f32"
     print(f"\n[c5] generating {name}", flush=True)
     return synth.make(name)
 
@@ -275,7 +275,7 @@ def test_bf16_input(kt, x_dtype):
 def test_split_equals_fused_bitwise(kt):
     """The split path runs the same diagonal and merge arithmetic in the same
     order, so it matches the fused kernel bit for bit."""
-    d = _cfg("c4_packed_ragged48_h64_f32_bf16")
+    d = _cfg("packed_ragged48_h64_f32_bf16")
     A = torch.from_numpy(d["A"]).to(DEV)
     cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
     for dt in (torch.float32, torch.bfloat16):
@@ -299,7 +299,7 @@ def test_garbage_above_diagonal_is_ignored(kt, algo):
 
 @pytest.mark.parametrize("algo", ALGOS)
 def test_deterministic(kt, algo):
-    d = _cfg("c3_packed_16x512_h64_f32")
+    d = _cfg("packed_16x512_h64_f32")
     A = torch.from_numpy(d["A"]).to(DEV)
     cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
     X0 = kt.tril_inv(A, cu, algo=algo)

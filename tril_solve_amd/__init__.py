@@ -156,6 +156,21 @@ def prepare_packed(A, X, cu_seqlens, workspace=None, algo="auto", stream=None):
     return call
 
 
+def prepare_dense(A, X, workspace=None, algo="auto", stream=None):
+    """Dense counterpart of prepare_packed: A, X [B, T, H, 64]."""
+    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 4 and A.shape == X.shape
+    B, T, H, _ = A.shape
+    args = (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H, _ptr(workspace),
+            _ws_bytes(workspace), _algo(algo), _stream_ptr(stream))
+    fn = _lib.kda_tril_inv_dense
+
+    def call():
+        st = fn(*args)
+        if st != KDA_OK:
+            raise KdaError(st)
+    return call
+
+
 def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None, out=None,
              stream=None):
     """X = (I + A)^-1 per 64-token chunk and head.

@@ -39,14 +39,16 @@ constexpr int kWave = 64;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // LDS per wave (floats): the diagonal inverses, column-major (column c of
-// block K at K * kXsBlock + c * kXsCol), then a staging tile for the stores.
+// block K at K * kXsBlock + c * kXsCol). The output staging of block row I
+// (16 rows x 16(I + 1) columns, row stride 16(I + 1) + 4) reuses the same
+// region: by the time block row I is staged, every value of blocks 0..I that
+// is still needed has been read into registers.
 constexpr int kXsCol = 20;
 constexpr int kXsBlock = 16 * kXsCol;
 constexpr int kXsFloats = 4 * kXsBlock;  // 1280 floats = 5 KiB
-// Output staging: one 16-row block row of X, row-major, padded row stride.
-constexpr int kStageRow = 64 + 4;
-constexpr int kStageFloats = 16 * kStageRow;
-constexpr int kLdsPerWave = kXsFloats + kStageFloats;  // 2368 floats = 9.25 KiB
+constexpr int kLdsPerWave = kXsFloats;
+__host__ __device__ constexpr int stage_row(int I) { return 16 * (I + 1) + 4; }
+static_assert(16 * stage_row(3) <= kXsFloats, "the staging of a block row must fit");
 
 // Orders LDS traffic between lanes of one wavefront (no s_barrier: LDS is
 // processed in order per wave; this stops the compiler from moving accesses).
@@ -79,13 +81,27 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access, gfx9-family layout
 
-// Descriptor over rows 0..len-1 (len >= 1) of a chunk-head whose row r
-// starts at base + r * rstride elements.
+// Rows 0..len-1 (len >= 1) of one chunk-head, row r at base + r * rstride
+// elements. Descriptors are made per group of rows at the point of use (a
+// few scalar instructions) so the row part of every address lives in SGPRs
+// and a single per-lane offset VGPR serves all loads or stores of a tile.
 template <class E>
-__device__ __forceinline__ Rsrc tile_rsrc(const typename E::T *base, int rstride, int len) {
-    const uint32_t n = (uint32_t)((len - 1) * rstride + kChunk) * E::kBytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<typename E::T *>(base), 0, n, kRsrcWord3);
-}
+struct TileView {
+    const typename E::T *base;
+    int rstride;  // elements between consecutive rows
+    int len;      // valid rows
+
+    // Descriptor whose byte 0 is row r0; its range ends after row len-1, so
+    // rows at or past len (relative offsets from row r0 onward) are out of
+    // range: loads return 0, stores are dropped.
+    __device__ __forceinline__ Rsrc rows_from(int r0) const {
+        const int valid = len - r0;  // rows from r0 on that exist
+        const uint32_t n =
+            valid > 0 ? (uint32_t)((valid - 1) * rstride + kChunk) * E::kBytes : 0u;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<typename E::T *>(base + (long)r0 * rstride), 0, n, kRsrcWord3);
+    }
+};
 
 // Four consecutive elements at byte offset `off` -> float4 (bf16 -> f32 is
 // exact); 0 past the descriptor's range.
@@ -211,6 +227,14 @@ __device__ __forceinline__ Chunk uniform(Chunk c) {
     return c;
 }
 
+// The lane index made opaque to the optimiser: values derived from it are
+// then recomputed where used instead of being hoisted out of the persistent
+// loop and held in registers for the kernel's lifetime.
+__device__ __forceinline__ int opaque_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 // ------------------------------------------------------------ small helpers
 
 // 16 x 16 x 16 product on the matrix cores: acc + P * Q with P in OPND_A and
@@ -280,12 +304,13 @@ __device__ __forceinline__ void diag_inverses(float *xs, const float (&arow)[16]
 // Lane (b, i) loads row 16b + i, columns 16b..16b+15 (the row of diagonal
 // block b); rows past the chunk read as 0.
 template <class E>
-__device__ __forceinline__ void load_diag_rows(float (&arow)[16], Rsrc A, int rstride, int lane) {
+__device__ __forceinline__ void load_diag_rows(float (&arow)[16], const TileView<E> &A, int lane) {
     const int b = lane >> 4, i = lane & 15;
-    const uint32_t off = (uint32_t)((16 * b + i) * rstride + 16 * b) * E::kBytes;
+    const Rsrc r = A.rows_from(0);
+    const uint32_t off = (uint32_t)((16 * b + i) * A.rstride + 16 * b) * E::kBytes;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const f4 v = load4<E>(A, off + 4 * q * E::kBytes);
+        const f4 v = load4<E>(r, off + 4 * q * E::kBytes);
 #pragma unroll
         for (int e = 0; e < 4; ++e) arow[4 * q + e] = v[e];
     }
@@ -308,14 +333,16 @@ __device__ __forceinline__ f4 xs_opnd_a_neg(const float *xs, int K, int lane) {
 // 16I + m, columns 16K + 4g..+3 of block (I, K), K < I (OPND_A layout).
 // Rows past the chunk read as 0.
 template <class E>
-__device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], Rsrc A, int rstride, int lane) {
+__device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], const TileView<E> &A,
+                                                    int lane) {
     const int g = lane >> 4, m = lane & 15;
-    const uint32_t off = (uint32_t)(m * rstride + 4 * g) * E::kBytes;
+    const uint32_t off = (uint32_t)(m * A.rstride + 4 * g) * E::kBytes;
 #pragma unroll
-    for (int I = 1; I < 4; ++I)
+    for (int I = 1; I < 4; ++I) {
+        const Rsrc r = A.rows_from(16 * I);
 #pragma unroll
-        for (int K = 0; K < I; ++K)
-            blk[I][K] = load4<E>(A, off + (uint32_t)(16 * I * rstride + 16 * K) * E::kBytes);
+        for (int K = 0; K < I; ++K) blk[I][K] = load4<E>(r, off + 16 * K * E::kBytes);
+    }
 }
 
 // Registers of one chunk-head's input tile: the rows of the diagonal blocks
@@ -326,36 +353,36 @@ struct Tile {
 };
 
 template <class E>
-__device__ __forceinline__ void load_tile(Tile &t, Rsrc A, int rstride, int lane) {
-    load_diag_rows<E>(t.arow, A, rstride, lane);
-    load_offdiag_blocks<E>(t.blk, A, rstride, lane);
+__device__ __forceinline__ void load_tile(Tile &t, const TileView<E> &A, int lane) {
+    load_diag_rows<E>(t.arow, A, lane);
+    load_offdiag_blocks<E>(t.blk, A, lane);
 }
 
-// Writes rows 16I..16I+15 of X (those inside the descriptor) through the LDS staging
-// tile so that every store instruction covers four whole 64-column rows
-// (16 lanes x 16 bytes per row for fp32): X_IJ (J < I) from OPND_O
-// registers xo[J], X_II from the column-major copy xs, and the zero upper
-// triangle (columns past 16(I + 1)) without touching LDS.
-template <class E, int BS, int CS, int I>
-__device__ __forceinline__ void store_block_row(Rsrc X, int rstride, const f4 (&xo)[4],
-                                                const float *xs, float *stage, int lane) {
+// Writes rows 16I..16I+15 of X (those inside the descriptor) through the LDS
+// staging tile so that every store instruction covers four whole 64-column
+// rows (16 lanes x 16 bytes per row for fp32): X_IJ (J <= I) come in OPND_O
+// registers xo[J]; the zero upper triangle (columns past 16(I + 1)) is
+// stored without touching LDS.
+template <class E, int I>
+__device__ __forceinline__ void store_block_row(const TileView<E> &X, const f4 (&xo)[4],
+                                                float *stage, int lane) {
+    constexpr int S = stage_row(I);
     const int g = lane >> 4, n = lane & 15;
+    wave_sync();  // every earlier read of this LDS region has completed
 #pragma unroll
-    for (int J = 0; J <= I; ++J) {
-        const f4 v = (J < I) ? xo[J] : xs_opnd_o<BS, CS>(xs, I, lane);
+    for (int J = 0; J <= I; ++J)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) stage[(4 * g + r) * kStageRow + 16 * J + n] = v[r];
-    }
+        for (int r = 0; r < 4; ++r) stage[(4 * g + r) * S + 16 * J + n] = xo[J][r];
     wave_sync();
     const int r4 = lane >> 4, c4 = (lane & 15) * 4;
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t off = (uint32_t)(r4 * rstride + c4) * E::kBytes;
+    const uint32_t off = (uint32_t)(r4 * X.rstride + c4) * E::kBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * i + r4;
         f4 v = z;
-        if (c4 < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * kStageRow + c4]);
-        store4<E>(X, off + (uint32_t)((16 * I + 4 * i) * rstride) * E::kBytes, v);
+        if (c4 < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * S + c4]);
+        store4<E>(X.rows_from(16 * I + 4 * i), off, v);
     }
     wave_sync();
 }
@@ -379,40 +406,50 @@ struct MfmaEngine {
 //   X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ,  I > J,
 // FP32 throughout. X_KK come from the column-major copy xs (LDS in the fused
 // kernel, the workspace in the split path); the products run in the same
-// order in both, so their results agree bit for bit.
+// order in both, so their results agree bit for bit. `stage` may alias xs
+// (the fused kernel): everything block row I needs from blocks 0..I of xs is
+// read before block row I is staged, and block row I's staging covers at most
+// the first 16 * stage_row(I) floats, which ends inside block I.
 template <class E, int BS, int CS, class Eng>
 __device__ __forceinline__ void merge_and_store(const Eng &eng, const f4 (&blk)[4][4],
-                                                const float *xs, float *stage, Rsrc X,
-                                                int rstride, int len, int lane) {
+                                                const float *xs, float *stage,
+                                                const TileView<E> &X, int lane) {
+    const int len = X.len;
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     f4 xo[4] = {z, z, z, z};
-    store_block_row<E, BS, CS, 0>(X, rstride, xo, xs, stage, lane);
+    // block row 0
+    const f4 x00 = xs_opnd_o<BS, CS>(xs, 0, lane);
+    xo[0] = x00;
+    store_block_row<E, 0>(X, xo, stage, lane);
     if (len <= 16) return;
     // block row 1
-    const f4 x00 = xs_opnd_o<BS, CS>(xs, 0, lane);
+    const f4 x11 = xs_opnd_o<BS, CS>(xs, 1, lane);
     const f4 x10 = eng.negx(1, eng.mm(blk[1][0], x00, z));
     xo[0] = x10;
-    store_block_row<E, BS, CS, 1>(X, rstride, xo, xs, stage, lane);
+    xo[1] = x11;
+    store_block_row<E, 1>(X, xo, stage, lane);
     if (len <= 32) return;
     // block row 2
-    const f4 x11 = xs_opnd_o<BS, CS>(xs, 1, lane);
+    const f4 x22 = xs_opnd_o<BS, CS>(xs, 2, lane);
     const f4 s21 = eng.mm(blk[2][1], x11, z);
     const f4 s20 = eng.mm(blk[2][1], x10, eng.mm(blk[2][0], x00, z));
     const f4 x21 = eng.negx(2, s21);
     const f4 x20 = eng.negx(2, s20);
     xo[0] = x20;
     xo[1] = x21;
-    store_block_row<E, BS, CS, 2>(X, rstride, xo, xs, stage, lane);
+    xo[2] = x22;
+    store_block_row<E, 2>(X, xo, stage, lane);
     if (len <= 48) return;
     // block row 3
-    const f4 x22 = xs_opnd_o<BS, CS>(xs, 2, lane);
+    const f4 x33 = xs_opnd_o<BS, CS>(xs, 3, lane);
     const f4 s32 = eng.mm(blk[3][2], x22, z);
     const f4 s31 = eng.mm(blk[3][2], x21, eng.mm(blk[3][1], x11, z));
     const f4 s30 = eng.mm(blk[3][2], x20, eng.mm(blk[3][1], x10, eng.mm(blk[3][0], x00, z)));
     xo[0] = eng.negx(3, s30);
     xo[1] = eng.negx(3, s31);
     xo[2] = eng.negx(3, s32);
-    store_block_row<E, BS, CS, 3>(X, rstride, xo, xs, stage, lane);
+    xo[3] = x33;
+    store_block_row<E, 3>(X, xo, stage, lane);
 }
 
 }  // namespace kda

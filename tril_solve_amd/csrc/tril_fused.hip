@@ -9,10 +9,8 @@
 // the inverse goes VGPRs -> LDS staging -> HBM as whole rows.
 //
 // The grid is sized to what the GPU holds at once and every wavefront walks
-// chunk-heads with a stride of the grid size, loading the next tile before
-// it solves the current one, so that a wavefront's HBM reads overlap its own
-// arithmetic (the solve of one tile has no memory traffic of its own besides
-// the stores).
+// chunk-heads with a stride of the grid size, so consecutive wavefronts work
+// on neighbouring heads of the same chunk (adjacent 256-byte rows in HBM).
 //
 // Traffic per full chunk-head: the ten blocks on or below the diagonal of A
 // are read (the six upper blocks are never needed, so never loaded) and all
@@ -35,10 +33,10 @@ __device__ __forceinline__ Item fetch(const Problem &p, long w, Tile &t, int lan
     it.h = (int)(w - (long)slot * p.heads);
     it.ch = uniform(resolve_chunk(p, slot, lane));
     if (it.ch.len > 0) {
-        const typename EI::T *A = static_cast<const typename EI::T *>(p.A) +
-                                  ((long)it.ch.start * p.heads + it.h) * kChunk;
-        const int rs = p.heads * kChunk;
-        load_tile<EI>(t, tile_rsrc<EI>(A, rs, it.ch.len), rs, lane);
+        const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
+                                 ((long)it.ch.start * p.heads + it.h) * kChunk,
+                             p.heads * kChunk, it.ch.len};
+        load_tile<EI>(t, A, opaque_lane(lane));
     }
     return it;
 }
@@ -47,36 +45,27 @@ template <class EI, class EO, class Eng>
 __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Tile &t, float *xs,
                                       float *stage, const Eng &eng, int lane) {
     if (it.ch.len <= 0) return;
-    const int rs = p.heads * kChunk;
-    typename EO::T *X = static_cast<typename EO::T *>(p.X) +
-                        ((long)it.ch.start * p.heads + it.h) * kChunk;
+    lane = opaque_lane(lane);
+    const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
+                             ((long)it.ch.start * p.heads + it.h) * kChunk,
+                         p.heads * kChunk, it.ch.len};
     diag_inverses(xs, t.arow, lane);
-    merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, tile_rsrc<EO>(X, rs, it.ch.len),
-                                          rs, it.ch.len, lane);
+    merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
 }
 
-// Grid-stride walk over the work items with a one-tile prefetch; two tile
-// register sets alternate so no copy is needed between iterations.
+// Grid-stride walk over the work items. (Loading the next tile before
+// solving the current one was measured too: the second register tile costs
+// more occupancy than the overlap gains on MI355X, so each item is loaded
+// when its wavefront reaches it, and other wavefronts cover the latency.)
 template <class EI, class EO, class Eng>
 __device__ __forceinline__ void walk(const Problem &p, float *xs, float *stage, const Eng &eng,
                                      long w, int lane) {
     const long total = (long)p.slots * p.heads;
     const long G = (long)gridDim.x * kFusedWaves;
-    if (w >= total) return;
-    Tile ta, tb;
-    Item ia = fetch<EI>(p, w, ta, lane);
-    for (;;) {
-        Item ib;
-        ib.ch.len = 0;
-        if (w + G < total) ib = fetch<EI>(p, w + G, tb, lane);
-        solve<EI, EO>(p, ia, ta, xs, stage, eng, lane);
-        w += G;
-        if (w >= total) break;
-        if (w + G < total) ia = fetch<EI>(p, w + G, ta, lane);
-        else ia.ch.len = 0;
-        solve<EI, EO>(p, ib, tb, xs, stage, eng, lane);
-        w += G;
-        if (w >= total) break;
+    for (; w < total; w += G) {
+        Tile t;
+        const Item it = fetch<EI>(p, w, t, lane);
+        solve<EI, EO>(p, it, t, xs, stage, eng, lane);
     }
 }
 
@@ -86,7 +75,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *xs = lds_all + wid * kLdsPerWave;
-    float *stage = xs + kXsFloats;
+    float *stage = xs;  // the staging reuses the diagonal-inverse region
     const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
     walk<EI, EO>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
 }
@@ -159,7 +148,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *xs = lds_all + wid * kLdsPerWaveValu;
-    float *stage = xs + kXsFloats;
+    float *stage = xs;
     float *ps = xs + kLdsPerWave;
     const ValuEngine eng{xs, ps, ps + 16 * kScr, lane};
     walk<EI, EO>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) 
     const long base = ((long)ch.start * p.heads + h) * kChunk;
     const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
     float arow[16];
-    load_diag_rows<EI>(arow, tile_rsrc<EI>(A, rstride, ch.len), rstride, lane);
+    load_diag_rows<EI>(arow, TileView<EI>{A, rstride, ch.len}, lane);
     diag_inverses(lds, arow, lane);
 
     // lane (b, c) copies column c of tile b: 64 contiguous bytes per lane,
@@ -49,10 +49,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) 
 
 template <class EI, class EO>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p) {
-    __shared__ float stage_all[kFusedWaves * kStageFloats];
+    __shared__ float stage_all[kFusedWaves * kLdsPerWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    float *stage = stage_all + wid * kStageFloats;
+    float *stage = stage_all + wid * kLdsPerWave;
     const long w = (long)blockIdx.x * kFusedWaves + wid;
     const int slot = (int)(w / p.heads);
     const int h = (int)(w - (long)slot * p.heads);
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p)
     const float *tiles = p.ws + ((long)slot * p.heads + h) * 4 * kWsTile;
 
     f4 blk[4][4];
-    load_offdiag_blocks<EI>(blk, tile_rsrc<EI>(A, rstride, ch.len), rstride, lane);
+    load_offdiag_blocks<EI>(blk, TileView<EI>{A, rstride, ch.len}, lane);
     const MfmaEngine<kWsTile, kWsCol> eng{tiles, lane};
-    merge_and_store<EO, kWsTile, kWsCol>(eng, blk, tiles, stage, tile_rsrc<EO>(X, rstride, ch.len),
-                                         rstride, ch.len, lane);
+    merge_and_store<EO, kWsTile, kWsCol>(eng, blk, tiles, stage,
+                                         TileView<EO>{X, rstride, ch.len}, lane);
 }
 
 template <class EI, class EO>
