@@ -249,11 +249,13 @@ __device__ __forceinline__ f4 mma16(f4 P, f4 Q, f4 acc) {
 
 // --------------------------------------------------- diagonal block inverses
 
-// Value of v in lane I of this lane's 16-lane row (DPP row_newbcast).
+// Value of v in lane I of this lane's 16-lane row (DPP row_newbcast). Every
+// lane's source lane exists, so no "old" value is needed (an explicit one
+// costs a move and a hazard wait per broadcast).
 template <int I>
 __device__ __forceinline__ float row_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                 0x150 + I, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              0x150 + I, 0xF, 0xF, true));
 }
 
 // Row I of the substitution: x_I = -sum_{j<I} A[I][j] x_j (j increasing),
