@@ -12,7 +12,7 @@
  * I + A independently and then merges them into the 64 x 64 inverse, keeping
  * the inverse tiles in FP32 until the final store (same PR, commit summary).
  * This library follows that scheme on CDNA4: every kernel computes in FP32;
- * inputs and outputs may be FP32 or bfloat16.
+ * inputs and outputs may be FP32, bfloat16 or binary16.
  *
  * Layout (both A and X, contiguous, row-major, 64 columns innermost):
  *   packed: [T, H, 64]; requests are concatenated along T and described by
@@ -31,7 +31,9 @@
  * caller owns A, X, cu_seqlens, chunk_indices and the workspace. The library
  * allocates nothing, frees nothing, keeps no pointer after a call returns,
  * never synchronises and never copies between host and device: every call
- * only enqueues kernels on `stream` and returns. A and X must not overlap.
+ * only enqueues kernels on `stream` and returns. A and X must not overlap,
+ * and A, X and the workspace must be 16-byte aligned (KDA_ERR_INVALID_ARG
+ * otherwise).
  *
  * Errors: plain status codes; nothing is thrown across the ABI. Problems that
  * the host can see (null pointers with nonzero sizes, H <= 0, unknown dtype,
@@ -58,9 +60,11 @@
 extern "C" {
 #endif
 
-/* Element type of A or X. BF16 is bfloat16 (8 exponent, 7 mantissa bits);
- * a bfloat16 X is the round-to-nearest-even of the FP32 result. */
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* Element type of A or X. BF16 is bfloat16 (8 exponent, 7 mantissa bits),
+ * F16 is IEEE binary16 (5 exponent, 10 mantissa bits); a 16-bit X is the
+ * round-to-nearest-even of the FP32 result (binary16 overflows to +-inf past
+ * 65504 and keeps subnormals). 16-bit inputs are widened to FP32 exactly. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_F16 = 2 } kda_dtype;
 
 /* Kernel plan.
  *   AUTO   - pick SPLIT when it is eligible and the tuned rule prefers it,

@@ -8,13 +8,13 @@ It evaluates the plain definition of what LightLLM PR #1703 ("perf(kda):
 parallelize diagonal solves in Prefill", PR description) computes: for every
 64-token chunk and head, X = (I + A)^-1 with A the strictly-lower intra-chunk
 matrix, by fp64 column forward substitution (``tril_oracle.c``). Inputs in
-float32 or bfloat16 are upcast to float64 exactly before the solve.
+float32, bfloat16 or binary16 are upcast to float64 exactly before the solve.
 
 Pins (each in ``tests/test_oracle_pins.py``): exact rational Neumann series,
 the single-subdiagonal closed form, LAPACK inversion, the residual of
 (I + A) X = I, the leading-principal-block property for partial chunks,
-hand-derived chunk maps (``tests/golden/``), and RNE against torch's
-bfloat16 cast plus hand-picked ties.
+hand-derived chunk maps (``tests/golden/``), and the bfloat16 and binary16
+roundings against tables worked out by hand (plus torch's bfloat16 cast).
 """
 from __future__ import annotations
 
@@ -79,15 +79,17 @@ def num_threads() -> int:
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact upcast of a materialised input to float64.
 
-    ``dtype`` is "f32" (a float32 array) or "bf16" (a uint16/int16 array of
+    ``dtype`` is "f32" (a float32 array), "bf16" (a uint16/int16 array of
     bfloat16 bit patterns: the value is those 16 bits followed by 16 zero bits
-    of a binary32).
+    of a binary32) or "f16" (IEEE binary16 values or bit patterns).
     """
     if dtype == "f32":
         return np.ascontiguousarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         bits = np.ascontiguousarray(a).view(np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(a).view(np.float16).astype(np.float64)
     if dtype == "f64":
         return np.ascontiguousarray(a, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -155,3 +157,11 @@ def rne_bf16(x: np.ndarray) -> np.ndarray:
     out = np.empty(bits.shape, np.uint16)
     _load().oracle_rne_bf16(_ptr(bits), _ptr(out), bits.size)
     return out
+
+
+def rne_f16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest, ties to even,
+    overflow to infinity, gradual underflow); returns the uint16 bit
+    patterns. numpy's float32 -> float16 conversion is this IEEE rounding;
+    it is pinned against a table worked out by hand."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)

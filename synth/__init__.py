@@ -157,9 +157,16 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) of a float32 array, via torch's CPU cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def make(name_or_cfg, upper: str = "zero") -> dict:
     """Materialise one workload. Returns a dict with the input ``A`` (float32,
-    or uint16 bfloat16 bits when a_dtype is bf16) in its layout
+    or uint16 bit patterns when a_dtype is bf16 or f16) in its layout
     ([T, H, 64] packed or [B, T, H, 64] dense), ``cu_seqlens`` (packed only),
     the request lengths and the config fields."""
     cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
@@ -167,6 +174,8 @@ def make(name_or_cfg, upper: str = "zero") -> dict:
     A = delta_rule_A(lengths, cfg["H"], cfg["seed"], upper=upper)
     if cfg["a_dtype"] == "bf16":
         A = to_bf16_bits(A)
+    elif cfg["a_dtype"] == "f16":
+        A = to_f16_bits(A)
     out = dict(cfg)
     out["lengths"] = lengths
     out["T_total"] = int(sum(lengths))

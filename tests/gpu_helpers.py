@@ -7,23 +7,27 @@ import numpy as np
 # Tolerances (elementwise, X_ref from the fp64 oracle):
 #   fp32 output: |X - X_ref| <= 2e-5 * (1 + |X_ref|)
 #   bf16 output: |X - X_ref| <= 1e-2 * |X_ref| + 2e-5 * (1 + |X_ref|)
+#   f16 output:  |X - X_ref| <= 1e-3 * |X_ref| + 2e-5 * (1 + |X_ref|)
+#                (binary16 rounding is at most 2^-11 relative; subnormal
+#                 outputs are within 2^-25 absolute)
 #   residual (fp32 outputs): max |(I + A_L) X - I| <= 1e-4
 F32_TOL = 2e-5
 BF16_REL = 1e-2
+F16_REL = 1e-3
 RESIDUAL_TOL = 1e-4
 
 
 def to_torch_input(A_np, a_dtype, device):
     import torch
-    if a_dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(A_np).view(np.int16)).view(
-            torch.bfloat16).to(device)
+    if a_dtype in ("bf16", "f16"):
+        dt = torch.bfloat16 if a_dtype == "bf16" else torch.float16
+        return torch.from_numpy(np.ascontiguousarray(A_np).view(np.int16)).view(dt).to(device)
     return torch.from_numpy(np.ascontiguousarray(A_np, dtype=np.float32)).to(device)
 
 
 def out_torch_dtype(x_dtype):
     import torch
-    return torch.bfloat16 if x_dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16}.get(x_dtype, torch.float32)
 
 
 def to_numpy_f64(X):
@@ -32,12 +36,15 @@ def to_numpy_f64(X):
     if X.dtype == torch.bfloat16:
         bits = X.cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
+    if X.dtype == torch.float16:
+        return X.cpu().view(torch.int16).numpy().view(np.float16).astype(np.float64)
     return X.cpu().numpy().astype(np.float64)
 
 
-def bf16_bits(X):
+def bits16(X):
+    """uint16 bit patterns of a bfloat16 or float16 tensor."""
     import torch
-    assert X.dtype == torch.bfloat16
+    assert X.dtype in (torch.bfloat16, torch.float16)
     return X.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
@@ -47,6 +54,8 @@ def excess(got, ref, x_dtype):
     bound = F32_TOL * (1.0 + np.abs(ref))
     if x_dtype == "bf16":
         bound = bound + BF16_REL * np.abs(ref)
+    elif x_dtype == "f16":
+        bound = bound + F16_REL * np.abs(ref)
     e = diff - bound
     e = np.where(np.isnan(got) | np.isnan(ref), np.inf, e)
     return float(e.max()) if e.size else -1.0

@@ -104,7 +104,7 @@ def _dense(kt, A=0x10000, ad=0, X=0x90000000, xd=0, B=1, T=64, H=2, ws=None, wsb
 
 def test_invalid_arguments_rejected_before_launch(kt):
     E = kt.KDA_ERR_INVALID_ARG
-    assert _packed(kt, ad=2) == E                      # unknown input dtype
+    assert _packed(kt, ad=3) == E                      # unknown input dtype
     assert _packed(kt, xd=-1) == E                     # unknown output dtype
     assert _packed(kt, algo=9) == E                    # unknown plan
     assert _packed(kt, H=0) == E

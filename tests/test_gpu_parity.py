@@ -255,7 +255,36 @@ def test_bf16_output_is_rne_of_fp32_output(kt, algo):
     X32 = kt.tril_inv(A, cu, out_dtype=torch.float32, algo=algo)
     X16 = kt.tril_inv(A, cu, out_dtype=torch.bfloat16, algo=algo)
     want = oracle.rne_bf16(X32.cpu().numpy())
-    assert np.array_equal(gh.bf16_bits(X16), want)
+    assert np.array_equal(gh.bits16(X16), want)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_f16_output_is_rne_of_fp32_output(kt, algo):
+    lengths = [512, 300, 64, 7]
+    H = 8
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=43)).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    X32 = kt.tril_inv(A, cu, out_dtype=torch.float32, algo=algo)
+    X16 = kt.tril_inv(A, cu, out_dtype=torch.float16, algo=algo)
+    assert np.array_equal(gh.bits16(X16), oracle.rne_f16(X32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("a_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16", "f16"])
+def test_dtype_matrix(kt, a_dtype, x_dtype):
+    """Every input x output element type, each plan, against the oracle on
+    the materialised (rounded) input."""
+    lengths = [300, 64, 17, 1]
+    H = 5
+    A32 = synth.delta_rule_A(lengths, H, seed=47)
+    A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
+    cu = synth.cu_seqlens(lengths)
+    ref = oracle.tril_inv_packed(A, cu, a_dtype)
+    Ad = gh.to_torch_input(A, a_dtype, DEV)
+    for algo in ALGOS:
+        X = kt.tril_inv(Ad, torch.from_numpy(cu).to(DEV), out_dtype=gh.out_torch_dtype(x_dtype),
+                        algo=algo)
+        assert gh.excess(gh.to_numpy_f64(X), ref, x_dtype) <= 0, algo
 
 
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
@@ -388,3 +417,39 @@ def test_forced_split_without_workspace_fails(kt):
     kt.kda_tril_inv_packed(A, X, cu, algo="auto")
     torch.cuda.synchronize()
     assert torch.equal(X[:, 0, :], torch.eye(64, device=DEV).repeat(2, 1))
+
+
+@pytest.mark.parametrize("algo", ["fused", "split"])
+def test_graph_capture_replay(kt, algo):
+    """One call captured in a HIP graph with a caller-kept chunk map (as a
+    layer loop would reuse it) and a fixed workspace, replayed on new inputs
+    with eager work and synchronisation between replays; every replay equals
+    the eager result bit for bit."""
+    lengths = [512, 300, 64, 9]
+    H = 8
+    T = sum(lengths)
+    inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (101, 102, 103)]
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    cmap = torch.from_numpy(_host_chunk_map(lengths)).to(DEV)
+    A = torch.from_numpy(inputs[0]).to(DEV)
+    X = torch.empty_like(A)
+    nbytes, _ = kt.kda_tril_inv_workspace_size(T, len(lengths), cmap.shape[0], H, algo)
+    ws = torch.empty(max(nbytes // 4, 1), device=DEV) if nbytes else None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kt.kda_tril_inv_packed(A, X, cu, chunk_indices=cmap, workspace=ws, algo=algo)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kt.kda_tril_inv_packed(A, X, cu, chunk_indices=cmap, workspace=ws, algo=algo)
+    for i in range(6):
+        A.copy_(torch.from_numpy(inputs[i % 3]))
+        X.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = kt.tril_inv(A, cu, algo=algo)
+        torch.cuda.synchronize()
+        assert torch.equal(X, ref), i

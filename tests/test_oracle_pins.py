@@ -128,6 +128,24 @@ def test_rne_golden():
     assert [int(v) for v in got] == [b for _, b in table]
 
 
+def test_f16_rne_golden():
+    rows = []
+    for line in open(os.path.join(pins.GOLDEN, "f16_rne.txt")):
+        t = line.split("#")[0].split()
+        if len(t) >= 2:
+            rows.append((int(t[0], 16), int(t[1], 16)))
+    f = np.array([a for a, _ in rows], np.uint32).view(np.float32)
+    with np.errstate(over="ignore"):
+        got = oracle.rne_f16(f)
+    assert [int(v) for v in got] == [b for _, b in rows]
+
+
+def test_f16_upcast_is_exact():
+    bits = np.array([0x3C00, 0xC000, 0x0001, 0x7BFF, 0x0400], np.uint16)
+    got = oracle.to_f64(bits, "f16")
+    assert np.array_equal(got, np.array([1.0, -2.0, 2.0 ** -24, 65504.0, 2.0 ** -14]))
+
+
 def test_rne_matches_torch_cast():
     import torch
     rng = np.random.default_rng(0)

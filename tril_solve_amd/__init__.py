@@ -17,7 +17,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkda_tril.so")
 
-KDA_F32, KDA_BF16 = 0, 1
+KDA_F32, KDA_BF16, KDA_F16 = 0, 1, 2
 KDA_ALGO_AUTO, KDA_ALGO_FUSED, KDA_ALGO_SPLIT, KDA_ALGO_FUSED_VALU = 0, 1, 2, 3
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = 0, -1, -2, -3, -4
 
@@ -91,7 +91,9 @@ def _dtype_code(t) -> int:
         return KDA_F32
     if t.dtype == torch.bfloat16:
         return KDA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return KDA_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _stream_ptr(stream):

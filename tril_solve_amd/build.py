@@ -26,7 +26,7 @@ ARCH = "gfx950"
 # Packed FP32 VALU instructions are disabled for all device code: hipcc would
 # otherwise form v_pk_{add,mul,fma}_f32 from scalar float code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
 

@@ -18,7 +18,7 @@ namespace {
 // Token counts are int32 inside the kernels; keep room for +64 arithmetic.
 constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 64;
 
-bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16 || d == KDA_F16; }
 bool valid_algo(kda_algo a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_FUSED_VALU; }
 size_t dtype_bytes(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
 
@@ -35,17 +35,17 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-kda_status run(const Problem &p, kda_algo algo, int a_bf16, int x_bf16, hipStream_t stream) {
+kda_status run(const Problem &p, kda_algo algo, int a_dt, int x_dt, hipStream_t stream) {
     hipError_t e = hipSuccess;
     switch (algo) {
         case KDA_ALGO_FUSED:
-            e = launch_fused_mfma(p, a_bf16, x_bf16, stream);
+            e = launch_fused_mfma(p, a_dt, x_dt, stream);
             break;
         case KDA_ALGO_SPLIT:
-            e = launch_split(p, a_bf16, x_bf16, stream);
+            e = launch_split(p, a_dt, x_dt, stream);
             break;
         case KDA_ALGO_FUSED_VALU:
-            e = launch_fused_valu(p, a_bf16, x_bf16, stream);
+            e = launch_fused_valu(p, a_dt, x_dt, stream);
             break;
         default:
             return KDA_ERR_INVALID_ARG;
@@ -147,7 +147,7 @@ kda_status kda_tril_inv_dense(const void *A, kda_dtype a_dtype, void *X, kda_dty
     p.total_tokens = (int32_t)rows;
     p.heads = H;
     p.slots = (int32_t)slots;
-    return run(p, chosen, a_dtype == KDA_BF16, x_dtype == KDA_BF16, stream);
+    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
 }
 
 kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
@@ -178,7 +178,7 @@ kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dt
     p.total_tokens = (int32_t)total_tokens;
     p.heads = H;
     p.slots = (int32_t)slots;
-    return run(p, chosen, a_dtype == KDA_BF16, x_dtype == KDA_BF16, stream);
+    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
 }
 
 }  // extern "C"

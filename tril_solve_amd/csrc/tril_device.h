@@ -68,6 +68,10 @@ struct BF16 {
     typedef uint16_t T;
     static constexpr int kBytes = 2;
 };
+struct F16 {
+    typedef uint16_t T;
+    static constexpr int kBytes = 2;
+};
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
     return __builtin_bit_cast(float, b << 16);
@@ -123,10 +127,21 @@ __device__ __forceinline__ f4 load4<BF16>(Rsrc r, uint32_t off) {
     return o;
 }
 
+template <>
+__device__ __forceinline__ f4 load4<F16>(Rsrc r, uint32_t off) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 v = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    f4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)v[e];  // exact widening
+    return o;
+}
+
 // float4 -> four consecutive elements at byte offset `off`, as a nontemporal
 // store (X is written once and not read again here, so it should not displace
 // cached lines); dropped past the descriptor's range. bf16 uses the hardware
-// round to nearest even (v_cvt_pk_bf16_f32).
+// round to nearest even (v_cvt_pk_bf16_f32), binary16 the IEEE conversion in
+// the default round-to-nearest-even mode.
 constexpr int kNontemporal = 2;  // cache-policy bit of buffer stores
 template <class E>
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, f4 v);
@@ -143,6 +158,15 @@ __device__ __forceinline__ void store4<BF16>(Rsrc r, uint32_t off, f4 v) {
     const b2 hi = {(__bf16)v[2], (__bf16)v[3]};
     const u2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     __builtin_amdgcn_raw_buffer_store_b64(o, r, off, 0, kNontemporal);
+}
+template <>
+__device__ __forceinline__ void store4<F16>(Rsrc r, uint32_t off, f4 v) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    h4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];  // v_cvt_f16_f32, round to nearest even
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, h), r, off, 0, kNontemporal);
 }
 
 // ------------------------------------------------------------ chunk resolution

@@ -166,18 +166,16 @@ static hipError_t launch_walk(K kernel, const Problem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_fused_mfma(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream) {
-    if (!a_bf16 && !x_bf16) return launch_walk(tril_inv_fused_mfma<F32, F32>, p, stream);
-    if (!a_bf16 && x_bf16) return launch_walk(tril_inv_fused_mfma<F32, BF16>, p, stream);
-    if (a_bf16 && !x_bf16) return launch_walk(tril_inv_fused_mfma<BF16, F32>, p, stream);
-    return launch_walk(tril_inv_fused_mfma<BF16, BF16>, p, stream);
+hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
+    return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
+        return launch_walk(tril_inv_fused_mfma<EI, EO>, p, stream);
+    });
 }
 
-hipError_t launch_fused_valu(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream) {
-    if (!a_bf16 && !x_bf16) return launch_walk(tril_inv_fused_valu<F32, F32>, p, stream);
-    if (!a_bf16 && x_bf16) return launch_walk(tril_inv_fused_valu<F32, BF16>, p, stream);
-    if (a_bf16 && !x_bf16) return launch_walk(tril_inv_fused_valu<BF16, F32>, p, stream);
-    return launch_walk(tril_inv_fused_valu<BF16, BF16>, p, stream);
+hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
+    return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
+        return launch_walk(tril_inv_fused_valu<EI, EO>, p, stream);
+    });
 }
 
 }  // namespace kda

@@ -29,8 +29,29 @@ constexpr int kFusedThreads = 64 * kFusedWaves;
 // holds at once (occupancy x compute units); 0 when unknown. Cached.
 long resident_blocks(const void *fn, int threads);
 
-hipError_t launch_fused_mfma(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);
-hipError_t launch_split(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);
-hipError_t launch_fused_valu(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream);
+// Element-type codes of A and X: the kda_dtype values (0 f32, 1 bf16, 2 f16).
+hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
+hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
+hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
+
+// Calls f.template operator()<EI, EO>() for the element types of the codes.
+template <class EF32, class EBF16, class EF16, class F>
+hipError_t dispatch_dtypes(int a_dt, int x_dt, F &&f) {
+    auto with_out = [&](auto ein) -> hipError_t {
+        using EI = decltype(ein);
+        switch (x_dt) {
+            case 0: return f.template operator()<EI, EF32>();
+            case 1: return f.template operator()<EI, EBF16>();
+            case 2: return f.template operator()<EI, EF16>();
+        }
+        return hipErrorInvalidValue;
+    };
+    switch (a_dt) {
+        case 0: return with_out(EF32{});
+        case 1: return with_out(EBF16{});
+        case 2: return with_out(EF16{});
+    }
+    return hipErrorInvalidValue;
+}
 
 }  // namespace kda

@@ -86,11 +86,10 @@ static hipError_t launch_split_t(const Problem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_split(const Problem &p, int a_bf16, int x_bf16, hipStream_t stream) {
-    if (!a_bf16 && !x_bf16) return launch_split_t<F32, F32>(p, stream);
-    if (!a_bf16 && x_bf16) return launch_split_t<F32, BF16>(p, stream);
-    if (a_bf16 && !x_bf16) return launch_split_t<BF16, F32>(p, stream);
-    return launch_split_t<BF16, BF16>(p, stream);
+hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
+    return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
+        return launch_split_t<EI, EO>(p, stream);
+    });
 }
 
 }  // namespace kda
