@@ -51,14 +51,15 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
-        lib.oracle_chunks_packed.restype = i64
-        lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
-        lib.oracle_inv_unit_lower.restype = None
-        lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
-        lib.oracle_tril_inv_packed.restype = i64
-        lib.oracle_tril_inv_packed.argtypes = [p, p, p, i64, i64, i32, ctypes.c_int]
-        lib.oracle_tril_inv_dense.restype = i64
-        lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, i32, ctypes.c_int]
+        ci = ctypes.c_int
+        lib.oracle_chunks_packed_c.restype = i64
+        lib.oracle_chunks_packed_c.argtypes = [p, i64, ci, p, p, p, i64]
+        lib.oracle_inv_unit_lower_w.restype = None
+        lib.oracle_inv_unit_lower_w.argtypes = [p, i64, ci, ci, p, i64]
+        lib.oracle_tril_inv_packed_c.restype = i64
+        lib.oracle_tril_inv_packed_c.argtypes = [p, p, p, i64, i64, i32, ci, ci]
+        lib.oracle_tril_inv_dense_c.restype = i64
+        lib.oracle_tril_inv_dense_c.argtypes = [p, p, i64, i64, i32, ci, ci]
         lib.oracle_rne_bf16.restype = None
         lib.oracle_rne_bf16.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -95,56 +96,55 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def chunks_packed(cu_seqlens) -> np.ndarray:
+def chunks_packed(cu_seqlens, chunk: int = CHUNK) -> np.ndarray:
     """Chunks of a packed batch: int64 array of rows (seq, start, length)."""
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     nseq = cu.shape[0] - 1
     lib = _load()
-    n = lib.oracle_chunks_packed(_ptr(cu), nseq, None, None, None, 0)
+    n = lib.oracle_chunks_packed_c(_ptr(cu), nseq, chunk, None, None, None, 0)
     if n < 0:
         raise ValueError("malformed cu_seqlens")
     seq = np.zeros(n, np.int64)
     start = np.zeros(n, np.int64)
     ln = np.zeros(n, np.int32)
-    lib.oracle_chunks_packed(_ptr(cu), nseq, _ptr(seq), _ptr(start), _ptr(ln), n)
+    lib.oracle_chunks_packed_c(_ptr(cu), nseq, chunk, _ptr(seq), _ptr(start), _ptr(ln), n)
     return np.stack([seq, start, ln.astype(np.int64)], axis=1)
 
 
-def inv_unit_lower(M: np.ndarray) -> np.ndarray:
+def inv_unit_lower(M: np.ndarray, width: int = CHUNK) -> np.ndarray:
     """(I + M)^-1 for one L x L matrix (only the strictly-lower part of M is
-    read). Returns an L x 64 float64 array: full-width output rows."""
+    read). Returns an L x width float64 array: full-width output rows of a
+    chunk of ``width`` tokens (L <= width <= 64)."""
     M = np.ascontiguousarray(M, dtype=np.float64)
     L = M.shape[0]
-    if M.ndim != 2 or M.shape[1] < L or L > CHUNK:
-        raise ValueError("M must be L x >=L with L <= 64")
-    X = np.zeros((L, CHUNK), np.float64)
-    _load().oracle_inv_unit_lower(_ptr(M), M.shape[1], L, _ptr(X), CHUNK)
+    if M.ndim != 2 or M.shape[1] < L or L > width or width > CHUNK:
+        raise ValueError("M must be L x >=L with L <= width <= 64")
+    X = np.zeros((L, width), np.float64)
+    _load().oracle_inv_unit_lower_w(_ptr(M), M.shape[1], L, width, _ptr(X), width)
     return X
 
 
 def tril_inv_packed(A: np.ndarray, cu_seqlens, dtype: str = "f32", nthreads: int = 0,
                     fill: float = np.nan) -> np.ndarray:
-    """Oracle X for a packed [T, H, 64] input. Rows outside every chunk hold
-    ``fill``."""
+    """Oracle X for a packed [T, H, C] input (chunks of C = A.shape[-1]
+    tokens). Rows outside every chunk hold ``fill``."""
     A64 = to_f64(A, dtype)
     T, H, C = A64.shape
-    assert C == CHUNK
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
-    X = np.full((T, H, CHUNK), fill, np.float64)
-    r = _load().oracle_tril_inv_packed(_ptr(A64), _ptr(X), _ptr(cu), cu.shape[0] - 1, T, H,
-                                       nthreads)
+    X = np.full((T, H, C), fill, np.float64)
+    r = _load().oracle_tril_inv_packed_c(_ptr(A64), _ptr(X), _ptr(cu), cu.shape[0] - 1, T, H, C,
+                                         nthreads)
     if r < 0:
         raise ValueError("malformed packed problem")
     return X
 
 
 def tril_inv_dense(A: np.ndarray, dtype: str = "f32", nthreads: int = 0) -> np.ndarray:
-    """Oracle X for a dense [B, T, H, 64] input."""
+    """Oracle X for a dense [B, T, H, C] input (chunks of C = A.shape[-1])."""
     A64 = to_f64(A, dtype)
     B, T, H, C = A64.shape
-    assert C == CHUNK
-    X = np.full((B, T, H, CHUNK), np.nan, np.float64)
-    r = _load().oracle_tril_inv_dense(_ptr(A64), _ptr(X), B, T, H, nthreads)
+    X = np.full((B, T, H, C), np.nan, np.float64)
+    r = _load().oracle_tril_inv_dense_c(_ptr(A64), _ptr(X), B, T, H, C, nthreads)
     if r < 0:
         raise ValueError("malformed dense problem")
     return X

@@ -8,7 +8,8 @@
  *
  * What it computes (LightLLM PR #1703, "perf(kda): parallelize diagonal solves
  * in Prefill", PR description, method paragraph): for every 64-token chunk of
- * every request and every head, the inverse X = (I + A)^-1 of the unit
+ * every request and every head (and, for the shared solver's other branches,
+ * every 16- or 32-token chunk), the inverse X = (I + A)^-1 of the unit
  * lower-triangular matrix I + A, where A holds the strictly-lower
  * intra-chunk entries. The page computes it with four 16x16 diagonal inverses
  * and a blocked merge; that is only an evaluation order of the same unique
@@ -26,9 +27,9 @@
  *    and in columns >= L;
  *  - rows that belong to no chunk are not touched.
  *
- * Layouts: packed A and X are [T, H, 64] row-major (token, head, column);
- * dense ones are [B, T, H, 64]. Element (token t, head h, column j) is the
- * entry (t - chunk_start, j) of that chunk-head's matrix.
+ * Layouts: packed A and X are [T, H, C] row-major (token, head, column) for
+ * chunks of C tokens; dense ones are [B, T, H, C]. Element (token t, head h,
+ * column j) is the entry (t - chunk_start, j) of that chunk-head's matrix.
  */
 #include <stddef.h>
 #include <stdint.h>
@@ -43,19 +44,19 @@
 /*
  * Chunk enumeration of a packed batch (same PR, PR description: the solver
  * accepts packed varlen batches described by cumulative sequence lengths).
- * Request s covers tokens [cu[s], cu[s+1]); its chunks start at cu[s] + 64c.
- * Writes up to `cap` entries and returns the total number of chunks, or -1
- * when cu is not non-decreasing or cu[0] < 0.
+ * Request s covers tokens [cu[s], cu[s+1]); its chunks of C tokens start at
+ * cu[s] + C*c. Writes up to `cap` entries and returns the total number of
+ * chunks, or -1 when cu is not non-decreasing, cu[0] < 0 or C < 1.
  */
-int64_t oracle_chunks_packed(const int32_t *cu, int64_t nseq, int64_t *seq_out,
-                             int64_t *start_out, int32_t *len_out, int64_t cap) {
+int64_t oracle_chunks_packed_c(const int32_t *cu, int64_t nseq, int C, int64_t *seq_out,
+                               int64_t *start_out, int32_t *len_out, int64_t cap) {
     int64_t n = 0;
-    if (nseq > 0 && cu[0] < 0) return -1;
+    if (C < 1 || (nseq > 0 && cu[0] < 0)) return -1;
     for (int64_t s = 0; s < nseq; ++s) {
         int64_t bos = cu[s], eos = cu[s + 1];
         if (eos < bos) return -1;
-        for (int64_t p = bos; p < eos; p += ORACLE_CHUNK) {
-            int64_t len = eos - p < ORACLE_CHUNK ? eos - p : ORACLE_CHUNK;
+        for (int64_t p = bos; p < eos; p += C) {
+            int64_t len = eos - p < C ? eos - p : C;
             if (n < cap) {
                 if (seq_out) seq_out[n] = s;
                 if (start_out) start_out[n] = p;
@@ -67,19 +68,24 @@ int64_t oracle_chunks_packed(const int32_t *cu, int64_t nseq, int64_t *seq_out,
     return n;
 }
 
+int64_t oracle_chunks_packed(const int32_t *cu, int64_t nseq, int64_t *seq_out,
+                             int64_t *start_out, int32_t *len_out, int64_t cap) {
+    return oracle_chunks_packed_c(cu, nseq, ORACLE_CHUNK, seq_out, start_out, len_out, cap);
+}
+
 /*
- * X = (I + M)^-1 for one L x L matrix, L <= 64. M and X are row-major with
- * leading dimensions ldm and ldx (in elements). Only M[i][j] with j < i is
- * read. X is written for rows i < L and columns j < 64 (columns >= L are 0),
- * matching a full-width output row.
+ * X = (I + M)^-1 for one L x L matrix, L <= W <= 64. M and X are row-major
+ * with leading dimensions ldm and ldx (in elements). Only M[i][j] with j < i
+ * is read. X is written for rows i < L and columns j < W (columns >= L are
+ * 0), matching a full output row of a W-wide chunk.
  *
  * Column c of X solves (I + M) x = e_c: x_i = 0 for i < c, x_c = 1, and for
  * i > c, x_i = -sum_{j=c}^{i-1} M[i][j] x_j, summed in increasing j.
  */
-void oracle_inv_unit_lower(const double *M, int64_t ldm, int L, double *X, int64_t ldx) {
+void oracle_inv_unit_lower_w(const double *M, int64_t ldm, int L, int W, double *X, int64_t ldx) {
     double col[ORACLE_CHUNK];
     for (int i = 0; i < L; ++i)
-        for (int j = 0; j < ORACLE_CHUNK; ++j) X[(int64_t)i * ldx + j] = 0.0;
+        for (int j = 0; j < W; ++j) X[(int64_t)i * ldx + j] = 0.0;
     for (int c = 0; c < L; ++c) {
         for (int i = 0; i < c; ++i) col[i] = 0.0;
         col[c] = 1.0;
@@ -92,6 +98,10 @@ void oracle_inv_unit_lower(const double *M, int64_t ldm, int L, double *X, int64
     }
 }
 
+void oracle_inv_unit_lower(const double *M, int64_t ldm, int L, double *X, int64_t ldx) {
+    oracle_inv_unit_lower_w(M, ldm, L, ORACLE_CHUNK, X, ldx);
+}
+
 static int oracle_threads(int nthreads) {
 #ifdef _OPENMP
     return nthreads > 0 ? nthreads : omp_get_max_threads();
@@ -102,54 +112,65 @@ static int oracle_threads(int nthreads) {
 }
 
 /*
- * Packed layout: A, X are [T, H, 64] doubles; cu has nseq + 1 entries with
- * cu[nseq] <= T. Returns the number of chunk-head matrices solved, or -1 on a
- * malformed cu. nthreads <= 0 uses the OpenMP default.
+ * Packed layout with chunks of C tokens (C in 1..64): A, X are [T, H, C]
+ * doubles; cu has nseq + 1 entries with cu[nseq] <= T. Returns the number of
+ * chunk-head matrices solved, or -1 on a malformed problem. nthreads <= 0
+ * uses the OpenMP default.
  */
-int64_t oracle_tril_inv_packed(const double *A, double *X, const int32_t *cu, int64_t nseq,
-                               int64_t T, int32_t H, int nthreads) {
-    if (H <= 0 || nseq < 0) return -1;
-    int64_t nt = oracle_chunks_packed(cu, nseq, NULL, NULL, NULL, 0);
+int64_t oracle_tril_inv_packed_c(const double *A, double *X, const int32_t *cu, int64_t nseq,
+                                 int64_t T, int32_t H, int C, int nthreads) {
+    if (H <= 0 || nseq < 0 || C < 1 || C > ORACLE_CHUNK) return -1;
+    int64_t nt = oracle_chunks_packed_c(cu, nseq, C, NULL, NULL, NULL, 0);
     if (nt < 0 || (nseq > 0 && cu[nseq] > T)) return -1;
     int64_t *start = (int64_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int64_t));
     int32_t *len = (int32_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int32_t));
     if (!start || !len) { free(start); free(len); return -1; }
-    oracle_chunks_packed(cu, nseq, NULL, start, len, nt);
-    const int64_t rs = (int64_t)H * ORACLE_CHUNK; /* elements between consecutive tokens */
+    oracle_chunks_packed_c(cu, nseq, C, NULL, start, len, nt);
+    const int64_t rs = (int64_t)H * C; /* elements between consecutive tokens */
     const int64_t work = nt * (int64_t)H;
 #pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
     for (int64_t w = 0; w < work; ++w) {
         int64_t k = w / H, h = w % H;
-        int64_t off = start[k] * rs + h * ORACLE_CHUNK;
-        oracle_inv_unit_lower(A + off, rs, len[k], X + off, rs);
+        int64_t off = start[k] * rs + h * C;
+        oracle_inv_unit_lower_w(A + off, rs, len[k], C, X + off, rs);
     }
     free(start);
     free(len);
     return work;
 }
 
+int64_t oracle_tril_inv_packed(const double *A, double *X, const int32_t *cu, int64_t nseq,
+                               int64_t T, int32_t H, int nthreads) {
+    return oracle_tril_inv_packed_c(A, X, cu, nseq, T, H, ORACLE_CHUNK, nthreads);
+}
+
 /*
  * Dense batch layout (same PR, PR description: the solver also takes dense
- * [B, T, H] batches): A, X are [B, T, H, 64] doubles; every batch element is
- * one request of T tokens, so its chunks start at 64c and the last has
- * T - 64c valid rows. Returns the number of matrices solved.
+ * [B, T, H] batches) with chunks of C tokens: A, X are [B, T, H, C] doubles;
+ * every batch element is one request of T tokens, so its chunks start at Cc
+ * and the last has T - Cc valid rows. Returns the number of matrices solved.
  */
-int64_t oracle_tril_inv_dense(const double *A, double *X, int64_t B, int64_t T, int32_t H,
-                              int nthreads) {
-    if (H <= 0 || B < 0 || T < 0) return -1;
-    const int64_t rs = (int64_t)H * ORACLE_CHUNK;
-    const int64_t per_b = (T + ORACLE_CHUNK - 1) / ORACLE_CHUNK;
+int64_t oracle_tril_inv_dense_c(const double *A, double *X, int64_t B, int64_t T, int32_t H,
+                                int C, int nthreads) {
+    if (H <= 0 || B < 0 || T < 0 || C < 1 || C > ORACLE_CHUNK) return -1;
+    const int64_t rs = (int64_t)H * C;
+    const int64_t per_b = (T + C - 1) / C;
     const int64_t work = B * per_b * (int64_t)H;
 #pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
     for (int64_t w = 0; w < work; ++w) {
         int64_t h = w % H, k = w / H;
         int64_t b = k / per_b, c = k % per_b;
-        int64_t row0 = b * T + c * ORACLE_CHUNK;
-        int L = (int)(T - c * ORACLE_CHUNK < ORACLE_CHUNK ? T - c * ORACLE_CHUNK : ORACLE_CHUNK);
-        int64_t off = row0 * rs + h * ORACLE_CHUNK;
-        oracle_inv_unit_lower(A + off, rs, L, X + off, rs);
+        int64_t row0 = b * T + c * C;
+        int L = (int)(T - c * C < C ? T - c * C : C);
+        int64_t off = row0 * rs + h * C;
+        oracle_inv_unit_lower_w(A + off, rs, L, C, X + off, rs);
     }
     return work;
+}
+
+int64_t oracle_tril_inv_dense(const double *A, double *X, int64_t B, int64_t T, int32_t H,
+                              int nthreads) {
+    return oracle_tril_inv_dense_c(A, X, B, T, H, ORACLE_CHUNK, nthreads);
 }
 
 /*

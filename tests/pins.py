@@ -210,3 +210,24 @@ def read_rne_table():
             if len(s) >= 2:
                 rows.append((int(s[0], 16), int(s[1], 16)))
     return rows
+
+
+def read_chunk_maps_sized():
+    """(C, cu, chunks) cases of tests/golden/chunk_map_16_32.txt."""
+    cases = []
+    size, cu, chunks = None, None, []
+    with open(os.path.join(GOLDEN, "chunk_map_16_32.txt")) as f:
+        for line in f:
+            s = line.split("#")[0].split()
+            if not s:
+                continue
+            if s[0] == "size":
+                size = int(s[1])
+            elif s[0] == "cu":
+                cu, chunks = [int(v) for v in s[1:]], []
+            elif s[0] == "chunk":
+                chunks.append(tuple(int(v) for v in s[1:]))
+            elif s[0] == "end":
+                cases.append((size, cu, chunks))
+    return cases
+

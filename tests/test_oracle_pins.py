@@ -166,11 +166,11 @@ _MUTANTS = {
     "wrong_sign": ("col[i] = -s;", "col[i] = s;"),
     "transposed": ("s += M[(int64_t)i * ldm + j] * col[j];", "s += M[(int64_t)j * ldm + i] * col[j];"),
     "reads_diagonal": ("for (int j = c; j < i; ++j) s +=", "for (int j = c; j <= i; ++j) s +="),
-    "global_chunk_alignment": ("for (int64_t p = bos; p < eos; p += ORACLE_CHUNK)",
-                               "for (int64_t p = bos - bos % ORACLE_CHUNK; p < eos; p += ORACLE_CHUNK)"),
+    "global_chunk_alignment": ("for (int64_t p = bos; p < eos; p += C)",
+                               "for (int64_t p = bos - bos % C; p < eos; p += C)"),
     "ties_away": ("(rest == 0x8000u && (kept & 1u))", "(rest == 0x8000u)"),
-    "dense_row0": ("int64_t row0 = b * T + c * ORACLE_CHUNK;",
-                   "int64_t row0 = (b * per_b + c) * ORACLE_CHUNK;"),
+    "dense_row0": ("int64_t row0 = b * T + c * C;",
+                   "int64_t row0 = (b * per_b + c) * C;"),
 }
 
 
@@ -269,3 +269,47 @@ def test_unpatched_oracle_passes_the_same_gate(tmp_path):
     lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int]
     lib.oracle_tril_inv_dense.restype = i64
     assert not _pins_fail(lib)
+
+
+# ---- the 16- and 32-token branches -------------------------------------------
+
+def test_chunk_map_golden_16_32():
+    for C, cu, want in pins.read_chunk_maps_sized():
+        got = [tuple(r) for r in oracle.chunks_packed(cu, C).tolist()]
+        assert got == want, (C, cu)
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_small_chunk_drivers_against_lapack(C):
+    """Packed and dense drivers with C-token chunks: every chunk-head equals
+    LAPACK's inverse of its strictly-lower L x L block, columns L..C-1 are 0,
+    and entries on/above the diagonal (random here) are ignored."""
+    rng = np.random.default_rng(C)
+    lengths = [C, C + 5, 1, 3 * C - 1]
+    H = 3
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    A = rng.uniform(-0.5, 0.5, (T, H, C)).astype(np.float32)
+    X = oracle.tril_inv_packed(A, cu)
+    for _, s, L in oracle.chunks_packed(cu, C).tolist():
+        for h in range(H):
+            M = np.tril(A[s:s + L, h, :L].astype(np.float64), -1)
+            ref = np.linalg.inv(np.eye(L) + M)
+            assert np.abs(X[s:s + L, h, :L] - ref).max() < 1e-12
+            assert np.all(X[s:s + L, h, L:] == 0)
+    B, Td = 2, 2 * C + 3
+    Ad = rng.uniform(-0.5, 0.5, (B, Td, H, C)).astype(np.float32)
+    Xd = oracle.tril_inv_dense(Ad)
+    Xp = oracle.tril_inv_packed(Ad.reshape(B * Td, H, C), [0, Td, 2 * Td])
+    assert np.array_equal(Xd.reshape(B * Td, H, C), Xp)
+
+
+def test_small_chunk_is_leading_block_of_64():
+    """A 16- or 32-token chunk's inverse is the leading block of the 64-token
+    solver's on the same (zero-padded) rows."""
+    rng = np.random.default_rng(9)
+    M = np.tril(rng.uniform(-0.5, 0.5, (64, 64)), -1)
+    full = oracle.inv_unit_lower(M)
+    for C in (16, 32):
+        X = oracle.inv_unit_lower(M[:C, :C], width=C)
+        assert np.array_equal(X, full[:C, :C])
