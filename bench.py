@@ -32,8 +32,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 #   8192 tokens x 64 heads (8192 matrices): 0.476 ms;  64 tokens x 64 heads: 0.0254 ms.
 H200_INV_PER_S = {"packed_16x512_h64_f32": 8192 / 0.476e-3, "packed_1x64_h64_f32": 64 / 0.0254e-3}
 WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_16x512_h64_f32",
-             "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32"]
+             "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32",
+             "packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"]
 MAIN_WORKLOAD = "packed_16x512_h64_f32"
+METRIC = "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_packed16x512.json")
 KERNEL_SOURCES = ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
 
@@ -58,9 +60,9 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(lengths, H, a_bytes, x_bytes) -> int:
-    """Full 64-wide rows of A read and X written: rows x H x 64 x (in + out)."""
-    return int(sum(lengths)) * H * 64 * (a_bytes + x_bytes)
+def algorithmic_bytes(lengths, H, a_bytes, x_bytes, C=64) -> int:
+    """Full C-wide rows of A read and X written: rows x H x C x (in + out)."""
+    return int(sum(lengths)) * H * C * (a_bytes + x_bytes)
 
 
 def load_traffic(bytes_alg):
@@ -100,8 +102,9 @@ def describe(d) -> str:
         shape = f"packed {len(d['lengths'])} x {d['lengths'][0]} tokens"
     else:
         shape = f"packed {len(d['lengths'])} ragged requests, {d['T_total']} tokens"
+    C = d.get("chunk", 64)
     return (f"{shape}, {d['H']} heads, {d['a_dtype']} A -> {d['x_dtype']} X "
-            f"({d['num_chunks'] * d['H']} chunk-head 64x64 matrices)")
+            f"({d['num_chunks'] * d['H']} chunk-head {C}x{C} matrices)")
 
 
 def main() -> int:
@@ -133,18 +136,23 @@ def main() -> int:
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.workload]
     d0 = synth.make(cfg)
-    a_bytes = 2 if cfg["a_dtype"] == "bf16" else 4
-    x_bytes = 2 if cfg["x_dtype"] == "bf16" else 4
+    C = d0["chunk"]
+    if C != 64 and args.algo not in ("auto", "fused"):
+        log(f"bench.py: the {C}-token branch has a single kernel (algo auto or fused)")
+        return 2
+    a_bytes = 2 if cfg["a_dtype"] in ("bf16", "f16") else 4
+    x_bytes = 2 if cfg["x_dtype"] in ("bf16", "f16") else 4
     H = cfg["H"]
     T = d0["T_total"]
     mats = d0["num_chunks"] * H
-    bytes_alg = algorithmic_bytes(d0["lengths"], H, a_bytes, x_bytes)
+    bytes_alg = algorithmic_bytes(d0["lengths"], H, a_bytes, x_bytes, C)
     nsets = args.sets or max(1, min(4, -(-(1 << 30) // bytes_alg)))
-    x_dt = torch.bfloat16 if cfg["x_dtype"] == "bf16" else torch.float32
+    x_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["x_dtype"], torch.float32)
 
     def to_dev(d):
-        if cfg["a_dtype"] == "bf16":
-            return torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+        if cfg["a_dtype"] in ("bf16", "f16"):
+            dt = torch.bfloat16 if cfg["a_dtype"] == "bf16" else torch.float16
+            return torch.from_numpy(d["A"].view(np.int16)).view(dt).to(dev)
         return torch.from_numpy(d["A"]).to(dev)
 
     sets = []
@@ -158,7 +166,9 @@ def main() -> int:
         sets.append((A, torch.empty(A.shape, dtype=x_dt, device=dev)))
     dense = cfg["layout"] == "dense"
     cu = None if dense else torch.from_numpy(d0["cu_seqlens"]).to(dev)
-    if dense:
+    if C != 64:
+        nbytes, chosen = 0, "fused"
+    elif dense:
         nbytes, chosen = kt.kda_tril_inv_workspace_size(T, cfg["B"], d0["num_chunks"], H,
                                                         args.algo)
     else:
@@ -241,7 +251,8 @@ def main() -> int:
         "auto", "fused") and chosen == "fused" else None
     h200 = H200_INV_PER_S.get(args.workload)
     out = {
-        "metric": "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads",
+        "metric": METRIC if C == 64 else f"{C}x{C} tril inverses/sec + achieved HBM GB/s "
+                                         f"(% peak)",
         "value": value,
         "unit": "inverses/s",
         "n_gpus": 1,

@@ -37,11 +37,12 @@
  *
  * Errors: plain status codes; nothing is thrown across the ABI. Problems that
  * the host can see (null pointers with nonzero sizes, H <= 0, unknown dtype,
- * forced SPLIT with too little workspace, sizes past the int32 token range)
- * are reported before any launch. Device-side cu_seqlens are not validated
- * (that would need a synchronisation): they must start at 0, be
- * non-decreasing and end at <= total_tokens; kernels clamp every row index
- * to [0, total_tokens) so a bad cu_seqlens cannot write outside X.
+ * forced SPLIT with too little workspace; KDA_ERR_UNSUPPORTED for sizes past
+ * the int32 token range or H > 4096) are reported before any launch.
+ * Device-side cu_seqlens are not validated (that would need a
+ * synchronisation): they must start at 0, be non-decreasing and end at
+ * <= total_tokens; kernels clamp every row index to [0, total_tokens) so a
+ * bad cu_seqlens cannot write outside X.
  * KDA_ERR_HIP reports a failed launch (hipGetLastError after the launch).
  * Zero tokens, zero batch or zero requests is a no-op returning KDA_OK.
  *
@@ -142,6 +143,35 @@ kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dt
                                int64_t total_tokens, int32_t H, const int32_t *chunk_indices,
                                int64_t num_chunks, void *workspace, size_t workspace_bytes,
                                kda_algo algo, hipStream_t stream);
+
+/*
+ * The shared chunk solver's other branches (same PR, PR description: the
+ * 64-token kernel is the 64-token branch of a solver shared across chunk
+ * sizes). chunk_size C is 16, 32 or 64; A and X are [B, T, H, C] (dense) or
+ * [total_tokens, H, C] (packed), every chunk-head matrix is C x C, chunks of
+ * C tokens restart at every request's first token, and chunk_indices (if
+ * given) pairs count chunks of C tokens. Everything else (layout of a row,
+ * ignored entries, full-row output, dtypes, ownership, errors) is as above.
+ *   C = 64       identical to kda_tril_inv_dense / kda_tril_inv_packed.
+ *   C = 16, 32   one kernel: the 16-token branch is the diagonal solve alone,
+ *                the 32-token branch two diagonal solves and one merge on the
+ *                matrix cores. Only AUTO and FUSED are accepted (SPLIT and
+ *                FUSED_VALU return KDA_ERR_UNSUPPORTED); no workspace is used
+ *                (pass NULL, 0).
+ * Any other chunk_size returns KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_tril_inv_dense_chunk(const void *A, kda_dtype a_dtype, void *X,
+                                    kda_dtype x_dtype, int64_t B, int64_t T, int32_t H,
+                                    int32_t chunk_size, void *workspace,
+                                    size_t workspace_bytes, kda_algo algo, hipStream_t stream);
+
+kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
+                                     kda_dtype x_dtype, const int32_t *cu_seqlens,
+                                     int64_t num_seqs, int64_t total_tokens, int32_t H,
+                                     int32_t chunk_size, const int32_t *chunk_indices,
+                                     int64_t num_chunks, void *workspace,
+                                     size_t workspace_bytes, kda_algo algo,
+                                     hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);

@@ -5,7 +5,8 @@ imports neither the oracle nor the HIP library, both of which consume what it
 makes.
 
 The intra-chunk matrix follows the delta-rule shape that KDA prefill hands to
-the solver: for tokens i > j of one 64-token chunk and one head,
+the solver: for tokens i > j of one chunk (64 tokens, or 16 or 32 for the
+smaller branches) and one head,
 
     A[i, j] = -beta_i * sum_d k[i, d] * k[j, d] * exp(g[i, d] - g[j, d])
 
@@ -34,9 +35,9 @@ import numpy as np
 CHUNK = 64
 KEY_DIM = 128
 
-# The five workloads, each named by its layout, request lengths, heads and
-# dtypes. Fields: layout, request lengths (or dense B, T), heads, input and
-# output dtypes, data seed.
+# The workloads, each named by its layout, request lengths, heads, dtypes and
+# (when not 64) chunk size. Fields: layout, request lengths (or dense B, T),
+# heads, input and output dtypes, data seed, optional chunk size.
 CONFIGS = {
     "packed_1x64_h64_f32": dict(layout="packed", lengths=[64], H=64, a_dtype="f32",
                                    x_dtype="f32", seed=0),
@@ -48,6 +49,11 @@ CONFIGS = {
                                             a_dtype="f32", x_dtype="bf16", seed=3),
     "packed_1x131072_h64_f32": dict(layout="packed", lengths=[131072], H=64,
                                        a_dtype="f32", x_dtype="f32", seed=4),
+    # the solver's 16- and 32-token branches on the same tokens and heads
+    "packed_16x512_h64_c16_f32": dict(layout="packed", lengths=[512] * 16, H=64,
+                                         a_dtype="f32", x_dtype="f32", seed=5, chunk=16),
+    "packed_16x512_h64_c32_f32": dict(layout="packed", lengths=[512] * 16, H=64,
+                                         a_dtype="f32", x_dtype="f32", seed=6, chunk=32),
 }
 
 
@@ -73,18 +79,18 @@ def cu_seqlens(lengths) -> np.ndarray:
     return cu.astype(np.int32)
 
 
-def _chunk_rows(lengths):
+def _chunk_rows(lengths, chunk: int = CHUNK):
     """(first token, valid rows) of every chunk, in packed order."""
     out = []
     bos = 0
     for n in lengths:
-        for p in range(0, n, CHUNK):
-            out.append((bos + p, min(CHUNK, n - p)))
+        for p in range(0, n, chunk):
+            out.append((bos + p, min(chunk, n - p)))
         bos += n
     return out
 
 
-def _one_chunk(seed: int, idx: int, L: int, H: int, K: int) -> np.ndarray:
+def _one_chunk(seed: int, idx: int, L: int, H: int, K: int, chunk: int) -> np.ndarray:
     rng = np.random.default_rng([seed, idx])
     k = rng.standard_normal((L, H, K))
     z = rng.standard_normal((L, H, K))
@@ -97,26 +103,26 @@ def _one_chunk(seed: int, idx: int, L: int, H: int, K: int) -> np.ndarray:
     S = np.matmul(kq, kk)                            # [H, L, L]
     a = -beta.T[:, :, None] * S                      # [H, L, L]
     a = np.tril(a, -1).transpose(1, 0, 2)            # [L, H, L]
-    out = np.zeros((L, H, CHUNK), np.float32)
+    out = np.zeros((L, H, chunk), np.float32)
     out[:, :, :L] = a
     return out
 
 
 def delta_rule_A(lengths, H: int, seed: int, K: int = KEY_DIM, upper: str = "zero",
-                 threads: int | None = None) -> np.ndarray:
-    """Packed float32 A [T, H, 64] for requests of the given lengths.
+                 threads: int | None = None, chunk: int = CHUNK) -> np.ndarray:
+    """Packed float32 A [T, H, chunk] for requests of the given lengths.
 
     ``upper`` fills the entries on and above the diagonal (and the columns past
     a partial chunk's length), which the solver must ignore: "zero", "nan", or
     "garbage" (large finite values, +-inf and NaN mixed)."""
-    chunks = _chunk_rows(lengths)
+    chunks = _chunk_rows(lengths, chunk)
     T = int(sum(lengths))
-    A = np.zeros((T, H, CHUNK), np.float32)
+    A = np.zeros((T, H, chunk), np.float32)
     nthr = threads or min(16, os.cpu_count() or 1)
 
     def work(i):
         s, L = chunks[i]
-        A[s:s + L] = _one_chunk(seed, i, L, H, K)
+        A[s:s + L] = _one_chunk(seed, i, L, H, K, chunk)
 
     if len(chunks) > 1 and nthr > 1:
         with ThreadPoolExecutor(nthr) as ex:
@@ -131,7 +137,7 @@ def delta_rule_A(lengths, H: int, seed: int, K: int = KEY_DIM, upper: str = "zer
 
 def _fill_upper(A, chunks, mode, seed):
     rng = np.random.default_rng([seed, 0x5EED])
-    col = np.arange(CHUNK)
+    col = np.arange(A.shape[-1])
     for s, L in chunks:
         rows = np.arange(L)
         mask = col[None, :] >= rows[:, None]                  # on/above diagonal
@@ -167,11 +173,13 @@ def to_f16_bits(a: np.ndarray) -> np.ndarray:
 def make(name_or_cfg, upper: str = "zero") -> dict:
     """Materialise one workload. Returns a dict with the input ``A`` (float32,
     or uint16 bit patterns when a_dtype is bf16 or f16) in its layout
-    ([T, H, 64] packed or [B, T, H, 64] dense), ``cu_seqlens`` (packed only),
-    the request lengths and the config fields."""
+    ([T, H, C] packed or [B, T, H, C] dense, C = the config's "chunk", default
+    64), ``cu_seqlens`` (packed only), the request lengths and the config
+    fields."""
     cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    C = cfg.setdefault("chunk", CHUNK)
     lengths = config_lengths(cfg)
-    A = delta_rule_A(lengths, cfg["H"], cfg["seed"], upper=upper)
+    A = delta_rule_A(lengths, cfg["H"], cfg["seed"], upper=upper, chunk=C)
     if cfg["a_dtype"] == "bf16":
         A = to_bf16_bits(A)
     elif cfg["a_dtype"] == "f16":
@@ -179,9 +187,9 @@ def make(name_or_cfg, upper: str = "zero") -> dict:
     out = dict(cfg)
     out["lengths"] = lengths
     out["T_total"] = int(sum(lengths))
-    out["num_chunks"] = len(_chunk_rows(lengths))
+    out["num_chunks"] = len(_chunk_rows(lengths, C))
     if cfg["layout"] == "dense":
-        out["A"] = A.reshape(cfg["B"], cfg["T"], cfg["H"], CHUNK)
+        out["A"] = A.reshape(cfg["B"], cfg["T"], cfg["H"], C)
     else:
         out["A"] = A
         out["cu_seqlens"] = cu_seqlens(lengths)

@@ -63,7 +63,7 @@ def excess(got, ref, x_dtype):
 
 def residual_chunks(A64, X64, chunks):
     """max |(I + A_L) X_L - I| over the given (start, len, head) matrices;
-    A64, X64 packed [T, H, 64] float64."""
+    A64, X64 packed [T, H, C] float64."""
     worst = 0.0
     for s, L, h in chunks:
         M = np.tril(A64[s:s + L, h, :L], -1)
@@ -73,12 +73,21 @@ def residual_chunks(A64, X64, chunks):
     return worst
 
 
-def all_chunk_heads(lengths, H):
+def all_chunk_heads(lengths, H, C=64):
     out = []
     bos = 0
     for n in lengths:
-        for p in range(0, n, 64):
+        for p in range(0, n, C):
             for h in range(H):
-                out.append((bos + p, min(64, n - p), h))
+                out.append((bos + p, min(C, n - p), h))
         bos += n
     return out
+
+
+def host_chunk_map(lengths, C=64):
+    """(request, chunk-within-request) pairs in packed order, int32 [n, 2]."""
+    pairs = []
+    for s, n in enumerate(lengths):
+        for c in range((n + C - 1) // C):
+            pairs.append((s, c))
+    return np.asarray(pairs, np.int32).reshape(-1, 2)

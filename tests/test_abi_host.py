@@ -145,3 +145,54 @@ def test_empty_problems_are_noops(kt):
     assert _packed(kt, T=0, A=None, X=None, cu=None) == kt.KDA_OK
     assert _dense(kt, B=0) == kt.KDA_OK
     assert _dense(kt, T=0, A=None, X=None) == kt.KDA_OK
+
+
+# ---- the 16- and 32-token entry points ---------------------------------------
+
+def _packed_c(kt, C, A=0x10000, ad=0, X=0x90000000, xd=0, cu=0x2000, nseq=1, T=64, H=2,
+              cmap=None, nch=0, ws=None, wsb=0, algo=1):
+    return kt._lib.kda_tril_inv_packed_chunk(P(A), ad, P(X), xd, P(cu), nseq, T, H, C, P(cmap),
+                                             nch, P(ws), wsb, algo, None)
+
+
+def _dense_c(kt, C, A=0x10000, ad=0, X=0x90000000, xd=0, B=1, T=64, H=2, ws=None, wsb=0,
+             algo=1):
+    return kt._lib.kda_tril_inv_dense_chunk(P(A), ad, P(X), xd, B, T, H, C, P(ws), wsb, algo,
+                                            None)
+
+
+def test_chunk_size_validation(kt):
+    E, U = kt.KDA_ERR_INVALID_ARG, kt.KDA_ERR_UNSUPPORTED
+    for C in (0, -16, 8, 48, 128):
+        assert _packed_c(kt, C) == E
+        assert _dense_c(kt, C) == E
+    for C in (16, 32):
+        # one kernel per small chunk size: no split, no VALU merge
+        assert _packed_c(kt, C, algo=kt.KDA_ALGO_SPLIT) == U
+        assert _packed_c(kt, C, algo=kt.KDA_ALGO_FUSED_VALU) == U
+        assert _dense_c(kt, C, algo=kt.KDA_ALGO_SPLIT) == U
+        assert _packed_c(kt, C, algo=9) == E
+        assert _packed_c(kt, C, ad=3) == E
+        assert _packed_c(kt, C, A=None) == E
+        assert _packed_c(kt, C, cu=None) == E
+        assert _packed_c(kt, C, cmap=0x3000, nch=0) == E
+        assert _packed_c(kt, C, T=2**31) == U
+        # empty problems return before touching the device
+        assert _packed_c(kt, C, T=0, A=None, X=None, cu=None) == kt.KDA_OK
+        assert _dense_c(kt, C, B=0) == kt.KDA_OK
+    # the overlap check uses the row length C: X starting inside the 64 x 2 x C
+    # floats of A overlaps, for every C
+    for C in (16, 32, 64):
+        assert _packed_c(kt, C, X=0x10000 + 64 * 2 * C * 4 - 16) == E
+    # C = 64 is the 64-token entry point: forced split without workspace
+    assert _packed_c(kt, 64, algo=kt.KDA_ALGO_SPLIT) == kt.KDA_ERR_WORKSPACE
+
+
+def test_head_limit(kt):
+    U = kt.KDA_ERR_UNSUPPORTED
+    assert _packed(kt, H=4097) == U
+    assert _dense(kt, H=4097) == U
+    assert _packed_c(kt, 16, H=4097) == U
+    with pytest.raises(kt.KdaError) as e:
+        kt.kda_tril_inv_workspace_size(64, 1, 0, 4097, "auto")
+    assert e.value.status == U

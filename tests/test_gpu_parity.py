@@ -336,14 +336,6 @@ def test_deterministic(kt, algo):
         assert torch.equal(kt.tril_inv(A, cu, algo=algo), X0)
 
 
-def _host_chunk_map(lengths):
-    m = []
-    for s, n in enumerate(lengths):
-        for c in range((n + 63) // 64):
-            m.append((s, c))
-    return np.array(m, np.int32).reshape(-1, 2)
-
-
 @pytest.mark.parametrize("algo", ["fused", "split"])
 def test_chunk_map_matches_device_scan(kt, algo):
     rng = np.random.default_rng(71)
@@ -352,7 +344,7 @@ def test_chunk_map_matches_device_scan(kt, algo):
     A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=71)).to(DEV)
     cu_np = synth.cu_seqlens(lengths)
     cu = torch.from_numpy(cu_np).to(DEV)
-    cmap = torch.from_numpy(_host_chunk_map(lengths)).to(DEV)
+    cmap = torch.from_numpy(gh.host_chunk_map(lengths)).to(DEV)
     X0 = kt.tril_inv(A, cu, algo=algo)
     X1 = kt.tril_inv(A, cu, algo=algo, chunk_indices=cmap)
     assert torch.equal(X0, X1)
@@ -430,7 +422,7 @@ def test_graph_capture_replay(kt, algo):
     T = sum(lengths)
     inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (101, 102, 103)]
     cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
-    cmap = torch.from_numpy(_host_chunk_map(lengths)).to(DEV)
+    cmap = torch.from_numpy(gh.host_chunk_map(lengths)).to(DEV)
     A = torch.from_numpy(inputs[0]).to(DEV)
     X = torch.empty_like(A)
     nbytes, _ = kt.kda_tril_inv_workspace_size(T, len(lengths), cmap.shape[0], H, algo)

@@ -6,8 +6,10 @@ the current stream. There is no CPU fallback: if the library is missing or
 fails to load, importing this package raises.
 
 The functions named like the C entry points take torch tensors and forward
-their data pointers; ``tril_inv`` is the convenience form that allocates X
-(and the split workspace when needed) with torch.
+their data pointers (the chunk size C is the last dimension of A: 64 goes to
+the 64-token entry points, 16 and 32 to the chunk-size ones); ``tril_inv`` is
+the convenience form that allocates X (and the split workspace when needed)
+with torch.
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m tril_solve_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python tril_solve_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -45,9 +47,17 @@ _lib.kda_tril_inv_packed.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i6
                                      _i64, _p, _sz, ctypes.c_int, _p]
 _lib.kda_tril_auto_plan.restype = ctypes.c_int
 _lib.kda_tril_auto_plan.argtypes = [_i64, _i64, _i32, _sz]
+_lib.kda_tril_inv_dense_chunk.restype = ctypes.c_int
+_lib.kda_tril_inv_dense_chunk.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i32,
+                                          _i32, _p, _sz, ctypes.c_int, _p]
+_lib.kda_tril_inv_packed_chunk.restype = ctypes.c_int
+_lib.kda_tril_inv_packed_chunk.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64,
+                                           _i32, _i32, _p, _i64, _p, _sz, ctypes.c_int, _p]
 
 EXPORTED = ("kda_tril_inv_workspace_size", "kda_tril_inv_dense", "kda_tril_inv_packed",
-            "kda_status_string", "kda_tril_auto_plan")
+            "kda_status_string", "kda_tril_auto_plan", "kda_tril_inv_dense_chunk",
+            "kda_tril_inv_packed_chunk")
+CHUNK_SIZES = (16, 32, 64)
 
 
 class KdaError(RuntimeError):
@@ -110,88 +120,118 @@ def _ws_bytes(ws):
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def kda_tril_inv_dense(A, X, workspace=None, algo="auto", stream=None) -> None:
-    """A [B, T, H, 64] -> X [B, T, H, 64] (both cuda, contiguous)."""
+def _dense_args(A, X, workspace, algo, stream):
     assert A.is_contiguous() and X.is_contiguous() and A.dim() == 4 and A.shape == X.shape
     B, T, H, C = A.shape
-    assert C == 64
-    _check(_lib.kda_tril_inv_dense(_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H,
-                                   _ptr(workspace), _ws_bytes(workspace), _algo(algo),
-                                   _stream_ptr(stream)))
+    assert C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)"
+    return (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H, C, _ptr(workspace),
+            _ws_bytes(workspace), _algo(algo), _stream_ptr(stream))
 
 
-def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, algo="auto",
-                        stream=None) -> None:
-    """A [T, H, 64] -> X [T, H, 64] for requests given by int32 cu_seqlens."""
+def _packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream):
     import torch
     assert A.is_contiguous() and X.is_contiguous() and A.dim() == 3 and A.shape == X.shape
     assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
     T, H, C = A.shape
-    assert C == 64
+    assert C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)"
     nch = 0
     if chunk_indices is not None:
         assert chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous()
         nch = chunk_indices.numel() // 2
-    _check(_lib.kda_tril_inv_packed(_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X),
-                                    _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, H,
-                                    _ptr(chunk_indices), nch, _ptr(workspace),
-                                    _ws_bytes(workspace), _algo(algo), _stream_ptr(stream)))
+    return (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), _ptr(cu_seqlens),
+            cu_seqlens.numel() - 1, T, H, C, _ptr(chunk_indices), nch, _ptr(workspace),
+            _ws_bytes(workspace), _algo(algo), _stream_ptr(stream))
 
 
-def prepare_packed(A, X, cu_seqlens, workspace=None, algo="auto", stream=None):
+def _dense_fn(args):
+    """The C entry point for marshalled dense arguments, and its argument
+    tuple: the 64-token entry point for C = 64, the chunk-size one else."""
+    if args[7] == 64:
+        return _lib.kda_tril_inv_dense, args[:7] + args[8:]
+    return _lib.kda_tril_inv_dense_chunk, args
+
+
+def _packed_fn(args):
+    if args[8] == 64:
+        return _lib.kda_tril_inv_packed, args[:8] + args[9:]
+    return _lib.kda_tril_inv_packed_chunk, args
+
+
+def kda_tril_inv_dense(A, X, workspace=None, algo="auto", stream=None) -> None:
+    """A [B, T, H, C] -> X [B, T, H, C] (both cuda, contiguous), C = 16, 32
+    or 64 (kda_tril_inv_dense for 64, kda_tril_inv_dense_chunk else)."""
+    fn, args = _dense_fn(_dense_args(A, X, workspace, algo, stream))
+    _check(fn(*args))
+
+
+def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, algo="auto",
+                        stream=None) -> None:
+    """A [T, H, C] -> X [T, H, C] for requests given by int32 cu_seqlens,
+    C = 16, 32 or 64."""
+    fn, args = _packed_fn(_packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream))
+    _check(fn(*args))
+
+
+def kda_tril_inv_dense_chunk(A, X, chunk_size, workspace=None, algo="auto", stream=None) -> None:
+    """kda_tril_inv_dense_chunk itself (any C, including 64)."""
+    args = _dense_args(A, X, workspace, algo, stream)
+    assert args[7] == chunk_size
+    _check(_lib.kda_tril_inv_dense_chunk(*args))
+
+
+def kda_tril_inv_packed_chunk(A, X, cu_seqlens, chunk_size, chunk_indices=None, workspace=None,
+                              algo="auto", stream=None) -> None:
+    """kda_tril_inv_packed_chunk itself (any C, including 64)."""
+    args = _packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream)
+    assert args[8] == chunk_size
+    _check(_lib.kda_tril_inv_packed_chunk(*args))
+
+
+def _prepared(fn, args):
+    def call():
+        st = fn(*args)
+        if st != KDA_OK:
+            raise KdaError(st)
+    return call
+
+
+def prepare_packed(A, X, cu_seqlens, workspace=None, algo="auto", stream=None,
+                   chunk_indices=None):
     """Marshal the arguments of one packed call once and return a function
     that issues exactly that call (for launch loops that should not pay the
     per-call Python checks). The tensors must stay alive while it is used."""
-    import torch
-    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 3 and A.shape == X.shape
-    assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
-    T, H, _ = A.shape
-    args = (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), _ptr(cu_seqlens),
-            cu_seqlens.numel() - 1, T, H, None, 0, _ptr(workspace), _ws_bytes(workspace),
-            _algo(algo), _stream_ptr(stream))
-    fn = _lib.kda_tril_inv_packed
-
-    def call():
-        st = fn(*args)
-        if st != KDA_OK:
-            raise KdaError(st)
-    return call
+    return _prepared(*_packed_fn(_packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo,
+                                              stream)))
 
 
 def prepare_dense(A, X, workspace=None, algo="auto", stream=None):
-    """Dense counterpart of prepare_packed: A, X [B, T, H, 64]."""
-    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 4 and A.shape == X.shape
-    B, T, H, _ = A.shape
-    args = (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H, _ptr(workspace),
-            _ws_bytes(workspace), _algo(algo), _stream_ptr(stream))
-    fn = _lib.kda_tril_inv_dense
-
-    def call():
-        st = fn(*args)
-        if st != KDA_OK:
-            raise KdaError(st)
-    return call
+    """Dense counterpart of prepare_packed: A, X [B, T, H, C]."""
+    return _prepared(*_dense_fn(_dense_args(A, X, workspace, algo, stream)))
 
 
 def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None, out=None,
              stream=None):
-    """X = (I + A)^-1 per 64-token chunk and head.
+    """X = (I + A)^-1 per chunk of C = A.shape[-1] tokens (16, 32 or 64) and
+    head.
 
-    A: cuda tensor, [T, H, 64] packed (with int32 ``cu_seqlens``) or
-    [B, T, H, 64] dense, float32 or bfloat16. Returns X of ``out_dtype``
-    (default float32), same shape. The split workspace, when the plan needs
-    one, is allocated here with torch.
+    A: cuda tensor, [T, H, C] packed (with int32 ``cu_seqlens``) or
+    [B, T, H, C] dense, float32, bfloat16 or float16. Returns X of
+    ``out_dtype`` (default float32), same shape. The split workspace, when the
+    plan needs one, is allocated here with torch.
     """
     import torch
     out_dtype = out_dtype or torch.float32
     X = out if out is not None else torch.empty(A.shape, dtype=out_dtype, device=A.device)
-    if cu_seqlens is None:
-        B, T, H, _ = A.shape
-        nbytes, _chosen = kda_tril_inv_workspace_size(B * T, B, B * ((T + 63) // 64), H, algo)
-    else:
-        T, H, _ = A.shape
-        nch = 0 if chunk_indices is None else chunk_indices.numel() // 2
-        nbytes, _chosen = kda_tril_inv_workspace_size(T, cu_seqlens.numel() - 1, nch, H, algo)
+    C = A.shape[-1]
+    nbytes = 0
+    if C == 64:
+        if cu_seqlens is None:
+            B, T, H, _ = A.shape
+            nbytes, _chosen = kda_tril_inv_workspace_size(B * T, B, B * ((T + 63) // 64), H, algo)
+        else:
+            T, H, _ = A.shape
+            nch = 0 if chunk_indices is None else chunk_indices.numel() // 2
+            nbytes, _chosen = kda_tril_inv_workspace_size(T, cu_seqlens.numel() - 1, nch, H, algo)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device=A.device) if nbytes else None
     if cu_seqlens is None:
         kda_tril_inv_dense(A, X, workspace=ws, algo=algo, stream=stream)

@@ -1,6 +1,7 @@
 """Build libkda_tril.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m tril_solve_amd.build
+Usage: python tril_solve_amd/build.py   (run as a script: importing the
+package would load the library before it is built)
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ LIB = os.path.join(HERE, "libkda_tril.so")
 PROBE_LIB = os.path.join(HERE, "libkda_bench_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "plan.cpp", "launch_common.cpp", "tril_fused.hip", "tril_split.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "launch_common.cpp", "tril_fused.hip", "tril_split.hip",
+           "tril_small.hip"]
 PROBE_SOURCES = ["bench_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -17,13 +17,17 @@ namespace {
 
 // Token counts are int32 inside the kernels; keep room for +64 arithmetic.
 constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 64;
+// Heads: keeps every byte offset inside one chunk's rows (64 rows of H x 64
+// elements) below 2^31, which the kernels' 32-bit buffer offsets rely on.
+constexpr int32_t kMaxHeads = 4096;
 
 bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16 || d == KDA_F16; }
 bool valid_algo(kda_algo a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_FUSED_VALU; }
+bool valid_chunk(int32_t c) { return c == 16 || c == 32 || c == 64; }
 size_t dtype_bytes(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
 
-// One wavefront of 64 lanes per chunk slot and head; the launch must stay
-// below 2^32 threads.
+// At most one wavefront of 64 lanes per chunk slot and head; the launch must
+// stay below 2^32 threads.
 bool grid_fits(int64_t slots, int32_t H) {
     return slots <= kMaxTokens && slots * (int64_t)H * 64 < (int64_t)UINT32_MAX;
 }
@@ -53,29 +57,100 @@ kda_status run(const Problem &p, kda_algo algo, int a_dt, int x_dt, hipStream_t 
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-// Checks shared by both layouts; rows = tokens covered by A and X.
+// Checks shared by both layouts; rows = tokens covered by A and X, C = chunk
+// size (row length of A and X).
 kda_status check_common(const void *A, kda_dtype a_dtype, const void *X, kda_dtype x_dtype,
-                        int64_t rows, int32_t H, kda_algo algo) {
-    if (!valid_dtype(a_dtype) || !valid_dtype(x_dtype) || !valid_algo(algo))
+                        int64_t rows, int32_t H, int32_t C, kda_algo algo) {
+    if (!valid_dtype(a_dtype) || !valid_dtype(x_dtype) || !valid_algo(algo) || !valid_chunk(C))
         return KDA_ERR_INVALID_ARG;
     if (H <= 0) return KDA_ERR_INVALID_ARG;
-    if (rows > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    if (rows > kMaxTokens || H > kMaxHeads) return KDA_ERR_UNSUPPORTED;
+    // the 16- and 32-token branches have a single kernel (no split, no
+    // second merge engine)
+    if (C != 64 && algo != KDA_ALGO_AUTO && algo != KDA_ALGO_FUSED) return KDA_ERR_UNSUPPORTED;
     if (rows == 0) return KDA_OK;
     if (A == nullptr || X == nullptr) return KDA_ERR_INVALID_ARG;
     if (!aligned16(A) || !aligned16(X)) return KDA_ERR_INVALID_ARG;
-    const size_t elems = (size_t)rows * (size_t)H * 64;
+    const size_t elems = (size_t)rows * (size_t)H * (size_t)C;
     if (overlap(A, elems * dtype_bytes(a_dtype), X, elems * dtype_bytes(x_dtype)))
         return KDA_ERR_INVALID_ARG;
     return KDA_OK;
 }
 
-kda_status plan_call(int64_t rows, int64_t slots, int32_t H, kda_algo algo, void *workspace,
-                     size_t workspace_bytes, kda_algo *chosen) {
+kda_status plan_call(int64_t rows, int64_t slots, int32_t H, int32_t C, kda_algo algo,
+                     void *workspace, size_t workspace_bytes, kda_algo *chosen) {
+    if (C != 64) {  // one kernel per small chunk size, no workspace
+        *chosen = KDA_ALGO_FUSED;
+        return KDA_OK;
+    }
     const size_t offered = workspace ? workspace_bytes : 0;
     kda_status st = resolve_plan(rows, slots, H, algo, offered, chosen);
     if (st != KDA_OK) return st;
     if (*chosen == KDA_ALGO_SPLIT && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     return KDA_OK;
+}
+
+kda_status dense_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype, int64_t B,
+                      int64_t T, int32_t H, int32_t C, void *workspace, size_t workspace_bytes,
+                      kda_algo algo, hipStream_t stream) {
+    if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+    if (B > 0 && T > kMaxTokens / B) return KDA_ERR_UNSUPPORTED;
+    const int64_t rows = B * T;
+    kda_status st = check_common(A, a_dtype, X, x_dtype, rows, H, C, algo);
+    if (st != KDA_OK || rows == 0) return st;
+    const int64_t slots = B * ((T + C - 1) / C);
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    kda_algo chosen = KDA_ALGO_FUSED;
+    st = plan_call(rows, slots, H, C, algo, workspace, workspace_bytes, &chosen);
+    if (st != KDA_OK) return st;
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    p.A = A;
+    p.X = X;
+    p.ws = static_cast<float *>(workspace);
+    p.num_seqs = (int32_t)B;
+    p.seq_len = (int32_t)T;
+    p.total_tokens = (int32_t)rows;
+    p.heads = H;
+    p.slots = (int32_t)slots;
+    if (C != 64)
+        return launch_small(p, C, (int)a_dtype, (int)x_dtype, stream) == hipSuccess ? KDA_OK
+                                                                                   : KDA_ERR_HIP;
+    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
+}
+
+kda_status packed_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
+                       const int32_t *cu_seqlens, int64_t num_seqs, int64_t total_tokens,
+                       int32_t H, int32_t C, const int32_t *chunk_indices, int64_t num_chunks,
+                       void *workspace, size_t workspace_bytes, kda_algo algo,
+                       hipStream_t stream) {
+    if (num_seqs < 0 || total_tokens < 0 || num_chunks < 0) return KDA_ERR_INVALID_ARG;
+    if ((chunk_indices == nullptr) != (num_chunks == 0)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs > kMaxTokens || num_chunks > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    kda_status st = check_common(A, a_dtype, X, x_dtype, total_tokens, H, C, algo);
+    if (st != KDA_OK) return st;
+    if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+    if (cu_seqlens == nullptr) return KDA_ERR_INVALID_ARG;
+    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks, C);
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    kda_algo chosen = KDA_ALGO_FUSED;
+    st = plan_call(total_tokens, slots, H, C, algo, workspace, workspace_bytes, &chosen);
+    if (st != KDA_OK) return st;
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    p.A = A;
+    p.X = X;
+    p.cu = cu_seqlens;
+    p.cmap = chunk_indices;
+    p.ws = static_cast<float *>(workspace);
+    p.num_seqs = (int32_t)num_seqs;
+    p.total_tokens = (int32_t)total_tokens;
+    p.heads = H;
+    p.slots = (int32_t)slots;
+    if (C != 64)
+        return launch_small(p, C, (int)a_dtype, (int)x_dtype, stream) == hipSuccess ? KDA_OK
+                                                                                   : KDA_ERR_HIP;
+    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
 }
 
 }  // namespace
@@ -114,8 +189,8 @@ kda_status kda_tril_inv_workspace_size(int64_t total_tokens, int64_t num_seqs,
     if (bytes == nullptr || !valid_algo(algo)) return KDA_ERR_INVALID_ARG;
     if (total_tokens < 0 || num_seqs < 0 || num_chunks < 0 || num_heads <= 0)
         return KDA_ERR_INVALID_ARG;
-    if (total_tokens > kMaxTokens) return KDA_ERR_UNSUPPORTED;
-    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks);
+    if (total_tokens > kMaxTokens || num_heads > kMaxHeads) return KDA_ERR_UNSUPPORTED;
+    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks, 64);
     kda_algo c = KDA_ALGO_FUSED;
     kda_status st = resolve_plan(total_tokens, slots, num_heads, algo, SIZE_MAX, &c);
     if (st != KDA_OK) return st;
@@ -127,27 +202,8 @@ kda_status kda_tril_inv_workspace_size(int64_t total_tokens, int64_t num_seqs,
 kda_status kda_tril_inv_dense(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
                               int64_t B, int64_t T, int32_t H, void *workspace,
                               size_t workspace_bytes, kda_algo algo, hipStream_t stream) {
-    if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
-    if (B > 0 && T > kMaxTokens / B) return KDA_ERR_UNSUPPORTED;
-    const int64_t rows = B * T;
-    kda_status st = check_common(A, a_dtype, X, x_dtype, rows, H, algo);
-    if (st != KDA_OK || rows == 0) return st;
-    const int64_t slots = B * ((T + 63) / 64);
-    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
-    kda_algo chosen = KDA_ALGO_FUSED;
-    st = plan_call(rows, slots, H, algo, workspace, workspace_bytes, &chosen);
-    if (st != KDA_OK) return st;
-    Problem p;
-    memset(&p, 0, sizeof(p));
-    p.A = A;
-    p.X = X;
-    p.ws = static_cast<float *>(workspace);
-    p.num_seqs = (int32_t)B;
-    p.seq_len = (int32_t)T;
-    p.total_tokens = (int32_t)rows;
-    p.heads = H;
-    p.slots = (int32_t)slots;
-    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
+    return dense_call(A, a_dtype, X, x_dtype, B, T, H, 64, workspace, workspace_bytes, algo,
+                      stream);
 }
 
 kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,
@@ -155,30 +211,28 @@ kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dt
                                int64_t total_tokens, int32_t H, const int32_t *chunk_indices,
                                int64_t num_chunks, void *workspace, size_t workspace_bytes,
                                kda_algo algo, hipStream_t stream) {
-    if (num_seqs < 0 || total_tokens < 0 || num_chunks < 0) return KDA_ERR_INVALID_ARG;
-    if ((chunk_indices == nullptr) != (num_chunks == 0)) return KDA_ERR_INVALID_ARG;
-    if (num_seqs > kMaxTokens || num_chunks > kMaxTokens) return KDA_ERR_UNSUPPORTED;
-    kda_status st = check_common(A, a_dtype, X, x_dtype, total_tokens, H, algo);
-    if (st != KDA_OK) return st;
-    if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
-    if (cu_seqlens == nullptr) return KDA_ERR_INVALID_ARG;
-    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks);
-    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
-    kda_algo chosen = KDA_ALGO_FUSED;
-    st = plan_call(total_tokens, slots, H, algo, workspace, workspace_bytes, &chosen);
-    if (st != KDA_OK) return st;
-    Problem p;
-    memset(&p, 0, sizeof(p));
-    p.A = A;
-    p.X = X;
-    p.cu = cu_seqlens;
-    p.cmap = chunk_indices;
-    p.ws = static_cast<float *>(workspace);
-    p.num_seqs = (int32_t)num_seqs;
-    p.total_tokens = (int32_t)total_tokens;
-    p.heads = H;
-    p.slots = (int32_t)slots;
-    return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
+    return packed_call(A, a_dtype, X, x_dtype, cu_seqlens, num_seqs, total_tokens, H, 64,
+                       chunk_indices, num_chunks, workspace, workspace_bytes, algo, stream);
+}
+
+kda_status kda_tril_inv_dense_chunk(const void *A, kda_dtype a_dtype, void *X,
+                                    kda_dtype x_dtype, int64_t B, int64_t T, int32_t H,
+                                    int32_t chunk_size, void *workspace,
+                                    size_t workspace_bytes, kda_algo algo, hipStream_t stream) {
+    return dense_call(A, a_dtype, X, x_dtype, B, T, H, chunk_size, workspace, workspace_bytes,
+                      algo, stream);
+}
+
+kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
+                                     kda_dtype x_dtype, const int32_t *cu_seqlens,
+                                     int64_t num_seqs, int64_t total_tokens, int32_t H,
+                                     int32_t chunk_size, const int32_t *chunk_indices,
+                                     int64_t num_chunks, void *workspace,
+                                     size_t workspace_bytes, kda_algo algo,
+                                     hipStream_t stream) {
+    return packed_call(A, a_dtype, X, x_dtype, cu_seqlens, num_seqs, total_tokens, H,
+                       chunk_size, chunk_indices, num_chunks, workspace, workspace_bytes, algo,
+                       stream);
 }
 
 }  // extern "C"

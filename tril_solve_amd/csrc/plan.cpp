@@ -30,9 +30,9 @@ int64_t split_min_tokens() {
     return kDefaultSplitMinTokens;
 }
 
-int64_t chunk_slots(int64_t total_tokens, int64_t num_seqs, int64_t num_chunks) {
+int64_t chunk_slots(int64_t total_tokens, int64_t num_seqs, int64_t num_chunks, int chunk) {
     if (num_chunks > 0) return num_chunks;
-    return total_tokens / 64 + num_seqs;
+    return total_tokens / chunk + num_seqs;
 }
 
 int64_t split_workspace_bytes(int64_t slots, int32_t heads) {

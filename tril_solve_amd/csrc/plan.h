@@ -18,9 +18,10 @@ constexpr int64_t kF32RowBytes = 64 * 4;
 // Measured on MI355X; overridable with KDA_TRIL_SPLIT_MIN_TOKENS.
 int64_t split_min_tokens();
 
-// Chunk slots the kernels cover: the exact count when known, else the bound
-// floor(T / 64) + num_seqs (each request adds at most one partial chunk).
-int64_t chunk_slots(int64_t total_tokens, int64_t num_seqs, int64_t num_chunks);
+// Chunk slots the kernels cover for chunks of `chunk` tokens: the exact count
+// when known, else the bound floor(T / chunk) + num_seqs (each request adds at
+// most one partial chunk).
+int64_t chunk_slots(int64_t total_tokens, int64_t num_seqs, int64_t num_chunks, int chunk);
 
 // Workspace bytes of the split path for this many chunk slots.
 int64_t split_workspace_bytes(int64_t slots, int32_t heads);

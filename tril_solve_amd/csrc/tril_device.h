@@ -85,23 +85,25 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access, gfx9-family layout
 
-// Rows 0..len-1 (len >= 1) of one chunk-head, row r at base + r * rstride
-// elements. Descriptors are made per group of rows at the point of use (a
-// few scalar instructions) so the row part of every address lives in SGPRs
-// and a single per-lane offset VGPR serves all loads or stores of a tile.
+// Rows 0..len-1 (len >= 1) of one chunk-head (or of a few adjacent heads of
+// one chunk), row r at base + r * rstride elements, `width` elements used per
+// row. Descriptors are made per group of rows at the point of use (a few
+// scalar instructions) so the row part of every address lives in SGPRs and a
+// single per-lane offset VGPR serves all loads or stores of a tile.
 template <class E>
 struct TileView {
     const typename E::T *base;
     int rstride;  // elements between consecutive rows
     int len;      // valid rows
+    int width;    // elements of a row that belong to the view (<= rstride)
 
-    // Descriptor whose byte 0 is row r0; its range ends after row len-1, so
-    // rows at or past len (relative offsets from row r0 onward) are out of
-    // range: loads return 0, stores are dropped.
+    // Descriptor whose byte 0 is row r0; its range ends after the `width`
+    // elements of row len-1, so rows at or past len (relative offsets from
+    // row r0 onward) are out of range: loads return 0, stores are dropped.
     __device__ __forceinline__ Rsrc rows_from(int r0) const {
         const int valid = len - r0;  // rows from r0 on that exist
         const uint32_t n =
-            valid > 0 ? (uint32_t)((valid - 1) * rstride + kChunk) * E::kBytes : 0u;
+            valid > 0 ? (uint32_t)((valid - 1) * rstride + width) * E::kBytes : 0u;
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<typename E::T *>(base + (long)r0 * rstride), 0, n, kRsrcWord3);
     }
@@ -169,11 +171,51 @@ __device__ __forceinline__ void store4<F16>(Rsrc r, uint32_t off, f4 v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, h), r, off, 0, kNontemporal);
 }
 
+// Single elements, for the kernels that give every lane one column of a
+// matrix (each load or store instruction then covers whole adjacent rows).
+template <class E>
+__device__ __forceinline__ float load1(Rsrc r, uint32_t off);
+template <>
+__device__ __forceinline__ float load1<F32>(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float load1<BF16>(Rsrc r, uint32_t off) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float load1<F16>(Rsrc r, uint32_t off) {
+    return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+template <class E>
+__device__ __forceinline__ void store1(Rsrc r, uint32_t off, float v);
+template <>
+__device__ __forceinline__ void store1<F32>(Rsrc r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0,
+                                          kNontemporal);
+}
+template <>
+__device__ __forceinline__ void store1<BF16>(Rsrc r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, 0,
+                                          kNontemporal);
+}
+template <>
+__device__ __forceinline__ void store1<F16>(Rsrc r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), r, off, 0,
+                                          kNontemporal);
+}
+
+// Byte offset that is out of range of every descriptor above (their ranges
+// stay below 2 GiB): OR-ed into the offsets of lanes that must not touch
+// memory, so their loads return 0 and their stores are dropped.
+constexpr uint32_t kOffMasked = 0x80000000u;
+
 // ------------------------------------------------------------ chunk resolution
 
 struct Chunk {
     int32_t start;  // first token (row) of the chunk
-    int32_t len;    // valid rows, 1..64 (0: nothing to do)
+    int32_t len;    // valid rows, 1..C (0: nothing to do)
 };
 
 // wave-wide inclusive prefix sum of an int
@@ -186,18 +228,20 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Resolve chunk slot k (wave-uniform) to rows of A/X. Returns len 0 when the
-// slot is past the last chunk. Dense: chunk c of batch b starts at b*T + 64c.
-// Packed: slots enumerate chunks in packed order; with a chunk map the slot
-// indexes it, else the wave scans cu_seqlens 64 requests at a time.
+// Resolve chunk slot k (wave-uniform) to rows of A/X for chunks of C tokens.
+// Returns len 0 when the slot is past the last chunk. Dense: chunk c of batch
+// b starts at b*T + C*c. Packed: slots enumerate chunks in packed order; with
+// a chunk map the slot indexes it, else the wave scans cu_seqlens 64 requests
+// at a time.
+template <int C>
 __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane) {
     Chunk ch{0, 0};
     if (p.cu == nullptr) {
-        const int per = (p.seq_len + kChunk - 1) / kChunk;
+        const int per = (p.seq_len + C - 1) / C;
         const int b = k / per, c = k - b * per;
         if (b < p.num_seqs) {
-            ch.start = b * p.seq_len + c * kChunk;
-            ch.len = min(kChunk, p.seq_len - c * kChunk);
+            ch.start = b * p.seq_len + c * C;
+            ch.len = min(C, p.seq_len - c * C);
         }
         return ch;
     }
@@ -205,7 +249,7 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
     if (p.cmap != nullptr) {
         const int s = p.cmap[2 * k], c = p.cmap[2 * k + 1];
         if (s < 0 || s >= p.num_seqs || c < 0) return ch;
-        bos = p.cu[s] + c * kChunk;
+        bos = p.cu[s] + c * C;
         eos = p.cu[s + 1];
     } else {
         int base = 0;
@@ -216,7 +260,7 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
             if (s < p.num_seqs) {
                 b0 = p.cu[s];
                 e0 = p.cu[s + 1];
-                cnt = e0 > b0 ? (e0 - b0 + kChunk - 1) / kChunk : 0;
+                cnt = e0 > b0 ? (e0 - b0 + C - 1) / C : 0;
             }
             const int incl = wave_incl_scan(cnt, lane);
             const int total = __shfl(incl, kWave - 1, kWave);
@@ -225,7 +269,7 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
                 const unsigned long long m = __ballot(hit);
                 const int src = __builtin_ctzll(m);
                 const int first = base + __shfl(incl - cnt, src, kWave);
-                bos = __shfl(b0, src, kWave) + (k - first) * kChunk;
+                bos = __shfl(b0, src, kWave) + (k - first) * C;
                 eos = __shfl(e0, src, kWave);
                 found = true;
                 break;
@@ -239,7 +283,7 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
     if (bos < 0 || bos >= p.total_tokens || eos <= bos) return ch;
     eos = min(eos, p.total_tokens);
     ch.start = bos;
-    ch.len = min(kChunk, eos - bos);
+    ch.len = min(C, eos - bos);
     return ch;
 }
 

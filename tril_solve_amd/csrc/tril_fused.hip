@@ -31,11 +31,11 @@ __device__ __forceinline__ Item fetch(const Problem &p, long w, Tile &t, int lan
     Item it;
     const int slot = (int)(w / p.heads);
     it.h = (int)(w - (long)slot * p.heads);
-    it.ch = uniform(resolve_chunk(p, slot, lane));
+    it.ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
     if (it.ch.len > 0) {
         const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
                                  ((long)it.ch.start * p.heads + it.h) * kChunk,
-                             p.heads * kChunk, it.ch.len};
+                             p.heads * kChunk, it.ch.len, kChunk};
         load_tile<EI>(t, A, opaque_lane(lane));
     }
     return it;
@@ -48,7 +48,7 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
     lane = opaque_lane(lane);
     const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
                              ((long)it.ch.start * p.heads + it.h) * kChunk,
-                         p.heads * kChunk, it.ch.len};
+                         p.heads * kChunk, it.ch.len, kChunk};
     diag_inverses(xs, t.arow, lane);
     merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
 }

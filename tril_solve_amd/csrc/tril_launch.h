@@ -33,6 +33,8 @@ long resident_blocks(const void *fn, int threads);
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
+// Chunks of 16 or 32 tokens (A and X rows of `chunk` elements).
+hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream);
 
 // Calls f.template operator()<EI, EO>() for the element types of the codes.
 template <class EF32, class EBF16, class EF16, class F>

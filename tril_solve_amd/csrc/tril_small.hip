@@ -1,0 +1,229 @@
+// The shared chunk solver's 16- and 32-token branches for gfx950.
+//
+// LightLLM PR #1703 ("perf(kda): parallelize diagonal solves in Prefill", PR
+// description) describes the 64-token kernel as one branch of a solver that
+// also serves smaller chunks. With chunks of C tokens every chunk-head matrix
+// is C x C, A and X are [T, H, C] (packed) or [B, T, H, C] (dense), and:
+//
+//   * C = 16: the matrix is a single diagonal block, so the solve is the
+//     diagonal step alone. A wavefront takes four heads of one chunk and
+//     gives every lane one column (lane = 16 * head + column): a row of the
+//     four heads is 64 adjacent elements, so each load or store instruction
+//     covers one whole such row, and the columns never leave their lanes.
+//   * C = 32: two diagonal 16 x 16 inverses and one merge level,
+//     X_10 = -X_11 (A_10 X_00), on the matrix cores. A wavefront takes two
+//     heads of one chunk: its four 16-lane rows run the four diagonal
+//     substitutions of both heads at once, then both merges follow, and the
+//     rows are written through LDS staging as whole 2-head rows.
+//
+// Both kernels walk their work items (chunk, group of heads) with a grid
+// stride like the 64-token kernel, and compute in FP32 with the same
+// operation order as the 64-token kernel's corresponding blocks, so a 16- or
+// 32-token chunk gives bit for bit the leading block of the 64-token result
+// on the same (zero-padded) rows.
+#include <utility>
+
+#include "tril_device.h"
+#include "tril_launch.h"
+
+namespace kda {
+
+// --------------------------------------------------------------- 16 tokens
+
+constexpr int kHeads16 = 4;  // heads per wavefront (4 x 16 columns = 64 lanes)
+
+// -sum_{j<I} A[I][j] x[j] (j increasing) for the lane's column: A[I][j] is
+// element I of column j, held by lane j of this 16-lane row.
+template <int I, int... J>
+__device__ __forceinline__ float col_dot(const float (&a)[16], const float (&x)[16],
+                                         std::integer_sequence<int, J...>) {
+    float acc = 0.0f;
+    ((acc = __builtin_fmaf(row_bcast<J>(a[I]), x[J], acc)), ...);
+    return acc;
+}
+
+// Forward substitution for column c of (I + A)^-1 (rows in increasing order;
+// only rows below the diagonal are computed, so A's own diagonal and upper
+// part are never read).
+template <int... I>
+__device__ __forceinline__ void col_subst(const float (&a)[16], float (&x)[16], int c,
+                                          std::integer_sequence<int, I...>) {
+    ((x[I] = (I > c) ? -col_dot<I>(a, x, std::make_integer_sequence<int, I>{}) : x[I]), ...);
+}
+
+template <class EI, class EO>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_c16(Problem p) {
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane0 = threadIdx.x & (kWave - 1);
+    const int groups = (p.heads + kHeads16 - 1) / kHeads16;
+    const long total = (long)p.slots * groups;
+    const long G = (long)gridDim.x * kFusedWaves;
+    for (long w = (long)blockIdx.x * kFusedWaves + wid; w < total; w += G) {
+        const int slot = (int)(w / groups);
+        const int hg = (int)(w - (long)slot * groups);
+        const Chunk ch = uniform(resolve_chunk<16>(p, slot, lane0));
+        if (ch.len <= 0) continue;
+        const int lane = opaque_lane(lane0);
+        const int c = lane & 15;
+        const int h0 = kHeads16 * hg;
+        const int hv = min(kHeads16, p.heads - h0);  // heads of this group that exist
+        const int rstride = p.heads * 16;
+        const long base = ((long)ch.start * p.heads + h0) * 16;
+        const TileView<EI> A{static_cast<const typename EI::T *>(p.A) + base, rstride, ch.len,
+                             16 * hv};
+        const TileView<EO> X{static_cast<typename EO::T *>(p.X) + base, rstride, ch.len,
+                             16 * hv};
+        const uint32_t mask = (lane >> 4) < hv ? 0u : kOffMasked;
+
+        // a[i] = A[i][c] of this lane's head; rows past the chunk read as 0
+        float a[16];
+        const Rsrc ra = A.rows_from(0);
+        const uint32_t offa = (uint32_t)lane * EI::kBytes | mask;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            a[i] = load1<EI>(ra, offa + (uint32_t)(i * rstride * EI::kBytes));
+
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.0f : 0.0f;
+        col_subst(a, x, c, std::make_integer_sequence<int, 16>{});
+
+        // row i of the four heads is one 64-element store; rows past the
+        // chunk are dropped by the descriptor
+        const Rsrc rx = X.rows_from(0);
+        const uint32_t offx = (uint32_t)lane * EO::kBytes | mask;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            store1<EO>(rx, offx + (uint32_t)(i * rstride * EO::kBytes), x[i]);
+    }
+}
+
+// --------------------------------------------------------------- 32 tokens
+
+constexpr int kHeads32 = 2;  // heads per wavefront (2 heads x 2 diagonal blocks)
+constexpr int kStage32 = 2 * 32 + 4;  // LDS row stride of the 2-head staging
+static_assert(16 * kStage32 <= kLdsPerWave, "the staging of a block row must fit");
+
+// Rows 16I..16I+15 of both heads through LDS: xo[m][J] is block (I, J) of
+// head m in OPND_O layout (J <= I); columns past the diagonal block are 0.
+// Each store instruction then covers four whole 2-head rows.
+template <class E, int I>
+__device__ __forceinline__ void store_pair_rows(const TileView<E> &X, const f4 (&xo)[2][2],
+                                                float *stage, uint32_t mask_hi, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    wave_sync();  // earlier reads of this LDS region have completed
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int J = 0; J <= I; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) stage[(4 * g + r) * kStage32 + 32 * m + 16 * J + n] = xo[m][J][r];
+    wave_sync();
+    const int r4 = lane >> 4, c4 = (lane & 15) * 4;
+    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t off = (uint32_t)(r4 * X.rstride + c4) * E::kBytes | (c4 >= 32 ? mask_hi : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + r4;
+        f4 v = z;
+        if ((c4 & 31) < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * kStage32 + c4]);
+        store4<E>(X.rows_from(16 * I + 4 * i), off, v);
+    }
+    wave_sync();
+}
+
+template <class EI, class EO>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
+    __shared__ float lds_all[kFusedWaves * kLdsPerWave];
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane0 = threadIdx.x & (kWave - 1);
+    float *xs = lds_all + wid * kLdsPerWave;
+    const int groups = (p.heads + kHeads32 - 1) / kHeads32;
+    const long total = (long)p.slots * groups;
+    const long G = (long)gridDim.x * kFusedWaves;
+    for (long w = (long)blockIdx.x * kFusedWaves + wid; w < total; w += G) {
+        const int slot = (int)(w / groups);
+        const int hg = (int)(w - (long)slot * groups);
+        const Chunk ch = uniform(resolve_chunk<32>(p, slot, lane0));
+        if (ch.len <= 0) continue;
+        const int lane = opaque_lane(lane0);
+        const int h0 = kHeads32 * hg;
+        const int hv = min(kHeads32, p.heads - h0);
+        const int rstride = p.heads * 32;
+        const long base = ((long)ch.start * p.heads + h0) * 32;
+        const TileView<EI> A{static_cast<const typename EI::T *>(p.A) + base, rstride, ch.len,
+                             32 * hv};
+        const TileView<EO> X{static_cast<typename EO::T *>(p.X) + base, rstride, ch.len,
+                             32 * hv};
+        const uint32_t mask_hi = hv > 1 ? 0u : kOffMasked;  // second head missing
+
+        // Diagonal rows: lane (b, i), b = 2m + d, holds row 16d + i, columns
+        // 16d..16d+15 of head m (block d of head m goes to LDS block b).
+        float arow[16];
+        {
+            const int b = lane >> 4, i = lane & 15, m = b >> 1, d = b & 1;
+            const uint32_t off =
+                (uint32_t)((16 * d + i) * rstride + 32 * m + 16 * d) * EI::kBytes |
+                (m > 0 ? mask_hi : 0u);
+            const Rsrc r = A.rows_from(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4 v = load4<EI>(r, off + 4 * q * EI::kBytes);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * q + e] = v[e];
+            }
+        }
+        // A_10 of both heads in OPND_A layout (row 16 + m', columns 4g..4g+3)
+        f4 a10[2];
+        {
+            const int g = lane >> 4, mr = lane & 15;
+            const Rsrc r = A.rows_from(16);
+            const uint32_t off = (uint32_t)(mr * rstride + 4 * g) * EI::kBytes;
+            a10[0] = load4<EI>(r, off);
+            a10[1] = load4<EI>(r, (off + 32 * EI::kBytes) | mask_hi);
+        }
+
+        diag_inverses(xs, arow, lane);
+        // Everything the merge needs from the diagonal copies is read into
+        // registers before the first staging, which reuses the same LDS.
+        const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
+        const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f4 x00[2], row1[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) x00[m] = xs_opnd_o<kXsBlock, kXsCol>(xs, 2 * m, lane);
+        const bool two_rows = ch.len > 16;
+        if (two_rows) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                row1[m][1] = xs_opnd_o<kXsBlock, kXsCol>(xs, 2 * m + 1, lane);
+                row1[m][0] = eng.negx(2 * m + 1, eng.mm(a10[m], x00[m], z));
+            }
+        }
+        const f4 row0[2][2] = {{x00[0], z}, {x00[1], z}};
+        store_pair_rows<EO, 0>(X, row0, xs, mask_hi, lane);
+        if (two_rows) store_pair_rows<EO, 1>(X, row1, xs, mask_hi, lane);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class K>
+static hipError_t launch_groups(K kernel, const Problem &p, int heads_per_wave,
+                                hipStream_t stream) {
+    const long groups = (p.heads + heads_per_wave - 1) / heads_per_wave;
+    const long need = ((long)p.slots * groups + kFusedWaves - 1) / kFusedWaves;
+    const long cap = resident_blocks(reinterpret_cast<const void *>(kernel), kFusedThreads);
+    const long blocks = cap > 0 && cap < need ? cap : need;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream) {
+    return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
+        if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, kHeads16, stream);
+        if (chunk == 32) return launch_groups(tril_inv_c32<EI, EO>, p, kHeads32, stream);
+        return hipErrorInvalidValue;
+    });
+}
+
+}  // namespace kda

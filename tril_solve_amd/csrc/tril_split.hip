@@ -27,14 +27,14 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_diag(Problem p) 
     const int slot = (int)(w / p.heads);
     const int h = (int)(w - (long)slot * p.heads);
     if (slot >= p.slots) return;
-    const Chunk ch = uniform(resolve_chunk(p, slot, lane));
+    const Chunk ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
     if (ch.len <= 0) return;
 
     const int rstride = p.heads * kChunk;
     const long base = ((long)ch.start * p.heads + h) * kChunk;
     const typename EI::T *A = static_cast<const typename EI::T *>(p.A) + base;
     float arow[16];
-    load_diag_rows<EI>(arow, TileView<EI>{A, rstride, ch.len}, lane);
+    load_diag_rows<EI>(arow, TileView<EI>{A, rstride, ch.len, kChunk}, lane);
     diag_inverses(lds, arow, lane);
 
     // lane (b, c) copies column c of tile b: 64 contiguous bytes per lane,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p)
     const int slot = (int)(w / p.heads);
     const int h = (int)(w - (long)slot * p.heads);
     if (slot >= p.slots) return;
-    const Chunk ch = uniform(resolve_chunk(p, slot, lane));
+    const Chunk ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
     if (ch.len <= 0) return;
 
     const int rstride = p.heads * kChunk;
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge(Problem p)
     const float *tiles = p.ws + ((long)slot * p.heads + h) * 4 * kWsTile;
 
     f4 blk[4][4];
-    load_offdiag_blocks<EI>(blk, TileView<EI>{A, rstride, ch.len}, lane);
+    load_offdiag_blocks<EI>(blk, TileView<EI>{A, rstride, ch.len, kChunk}, lane);
     const MfmaEngine<kWsTile, kWsCol> eng{tiles, lane};
     merge_and_store<EO, kWsTile, kWsCol>(eng, blk, tiles, stage,
-                                         TileView<EO>{X, rstride, ch.len}, lane);
+                                         TileView<EO>{X, rstride, ch.len, kChunk}, lane);
 }
 
 template <class EI, class EO>
