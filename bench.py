@@ -36,8 +36,17 @@ WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_16x512
              "packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"]
 MAIN_WORKLOAD = "packed_16x512_h64_f32"
 METRIC = "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_packed16x512.json")
-KERNEL_SOURCES = ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
+# Kernel timed per chunk size, and the sources its code comes from (a
+# counter summary taken on other sources is not used).
+KERNELS = {64: "tril_inv_fused_mfma", 32: "tril_inv_c32", 16: "tril_inv_c16"}
+KERNEL_SOURCES = {64: ["tril_device.h", "tril_fused.hip", "tril_launch.h"],
+                  32: ["tril_device.h", "tril_small.hip", "tril_launch.h"],
+                  16: ["tril_device.h", "tril_small.hip", "tril_launch.h"]}
+COPY_KERNEL = "kda_probe_copy_kernel"
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def log(*a):
@@ -52,9 +61,9 @@ def load_copy_probe():
     return lib
 
 
-def kernel_hash() -> str:
+def kernel_hash(C: int = 64) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[C]:
         with open(os.path.join(ROOT, "tril_solve_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -65,17 +74,63 @@ def algorithmic_bytes(lengths, H, a_bytes, x_bytes, C=64) -> int:
     return int(sum(lengths)) * H * C * (a_bytes + x_bytes)
 
 
-def load_traffic(bytes_alg):
+def load_traffic(workload: str, C: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash(C):
         return None
     return int(t["hbm_bytes_per_launch"])
+
+
+def _counter_mean(csv_path: str, kernel: str, counter: str) -> tuple[float, int]:
+    """Mean value of `counter` (KiB per dispatch) over the dispatches of the
+    kernel whose name contains `kernel`, from a rocprofv3 counter CSV."""
+    import csv
+    vals = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{csv_path}: no {counter} rows for {kernel}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(workload: str, C: int, a_bytes_total: int, csvs, out_path: str) -> dict:
+    """Counter summary of the solver kernel: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch) each scaled by what the same counter reads for the copy
+    probe moving a known byte count (A's size each way)."""
+    fetch_csv, write_csv, copy_fetch_csv, copy_write_csv = csvs
+    k = KERNELS[C]
+    fetch, nf = _counter_mean(fetch_csv, k + "<", "FETCH_SIZE")
+    write, nw = _counter_mean(write_csv, k + "<", "WRITE_SIZE")
+    cfetch, _ = _counter_mean(copy_fetch_csv, COPY_KERNEL, "FETCH_SIZE")
+    cwrite, _ = _counter_mean(copy_write_csv, COPY_KERNEL, "WRITE_SIZE")
+    known = a_bytes_total / 1024.0
+    fs, ws = known / cfetch, known / cwrite
+    rd, wr = int(fetch * fs * 1024), int(write * ws * 1024)
+    t = {"kernel": k, "workload": workload, "kernel_hash": kernel_hash(C),
+         "dispatches": {"fetch": nf, "write": nw},
+         "fetch_size_kib_raw": round(fetch, 1), "write_size_kib_raw": round(write, 1),
+         "copy_fetch_size_kib_raw": round(cfetch, 1), "copy_write_size_kib_raw": round(cwrite, 1),
+         "copy_known_kib_each_way": round(known, 1),
+         "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+         "hbm_bytes_per_launch": rd + wr,
+         "commands": [
+             f"rocprofv3 --pmc {c} -f csv -d <out> -o run -- python3 bench.py --workload "
+             f"{workload} {extra}"
+             for extra in ("--steps 10 --warmup 2 --no-cpu-baseline",
+                           "--probe copy --steps 3 --warmup 1")
+             for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    with open(out_path, "w") as f:
+        json.dump(t, f, indent=1)
+    return t
 
 
 def cpu_baseline(d, budget_s=12.0):
@@ -92,7 +147,19 @@ def cpu_baseline(d, budget_s=12.0):
     return {"value": mats / el, "unit": "inverses/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"whole workload ({d['num_chunks'] * d['H']} matrices) solved {n}x "
-                      f"by the fp64 oracle in {el:.1f} s"}
+                      f"by the fp64 oracle in {el:.1f} s",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def describe(d) -> str:
@@ -120,7 +187,23 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run only a plain copy of A's byte count (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
+                    help="write the HBM-traffic summary of --workload from rocprofv3 counter "
+                         "CSVs (no GPU use)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        import synth
+        cfg = synth.CONFIGS[args.workload]
+        C = cfg.get("chunk", 64)
+        lengths = synth.config_lengths(cfg)
+        a_bytes = 2 if cfg["a_dtype"] in ("bf16", "f16") else 4
+        total = int(sum(lengths)) * cfg["H"] * C * a_bytes
+        t = record_traffic(args.workload, C, total, args.record_traffic[:4],
+                           args.record_traffic[4])
+        log(json.dumps(t))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py: this solver is measured on one GPU only; a multi-GPU run would shard "
@@ -146,7 +229,7 @@ def main() -> int:
     T = d0["T_total"]
     mats = d0["num_chunks"] * H
     bytes_alg = algorithmic_bytes(d0["lengths"], H, a_bytes, x_bytes, C)
-    nsets = args.sets or max(1, min(4, -(-(1 << 30) // bytes_alg)))
+    nsets = args.sets or max(1, min(16, -(-(1 << 30) // bytes_alg)))
     x_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["x_dtype"], torch.float32)
 
     def to_dev(d):
@@ -180,20 +263,26 @@ def main() -> int:
     probe = load_copy_probe()
 
     # The copy probe has destinations of its own, each exactly the byte size of
-    # its source (X may be narrower than A, e.g. bf16 X from fp32 A).
-    copy_dst = {}
+    # its source (X may be narrower than A, e.g. bf16 X from fp32 A). Its
+    # arguments are marshalled once per buffer set, like the solver calls.
+    copy_calls = {}
 
     def copy(A, _X=None):
-        nbytes = A.numel() * A.element_size()
-        D = copy_dst.get(A.data_ptr())
-        if D is None:
-            D = copy_dst[A.data_ptr()] = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
-        if nbytes % 16 or D.numel() * 4 != nbytes:
-            raise RuntimeError("copy probe: source and destination sizes differ")
-        st = probe.kda_probe_copy_f32(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()),
-                                      nbytes // 4, ctypes.c_void_p(stream.cuda_stream))
-        if st != 0:
-            raise RuntimeError(f"copy probe failed ({st})")
+        fn = copy_calls.get(A.data_ptr())
+        if fn is None:
+            nbytes = A.numel() * A.element_size()
+            D = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+            if nbytes % 16 or D.numel() * 4 != nbytes:
+                raise RuntimeError("copy probe: source and destination sizes differ")
+            cargs = (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()), nbytes // 4,
+                     ctypes.c_void_p(stream.cuda_stream))
+            f = probe.kda_probe_copy_f32
+
+            def fn(D=D):
+                if f(*cargs) != 0:
+                    raise RuntimeError("copy probe failed")
+            copy_calls[A.data_ptr()] = fn
+        fn()
 
     if args.probe == "copy":
         for _ in range(args.warmup + args.steps):
@@ -227,6 +316,20 @@ def main() -> int:
     el = time.perf_counter() - t0
     k_avg = e0.elapsed_time(e1) * 1e-3 / args.steps  # seconds per launch
 
+    # per-launch distribution (diagnostic, after the timed region): each of
+    # up to 50 launches bracketed by its own pair of events on the stream
+    reps = min(50, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        calls[i % len(calls)]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # microseconds
+    dist = {"median": per[len(per) // 2], "min": per[0], "p90": per[int(0.9 * (len(per) - 1))],
+            "launches": reps}
+
     # measured copy roofline: a plain streaming copy of A's byte count, read
     # and written, same buffer rotation, events over the region
     if a_bytes == 4:
@@ -247,8 +350,8 @@ def main() -> int:
 
     value = mats * args.steps / el
     achieved = bytes_alg / k_avg / 1e9
-    traffic = load_traffic(bytes_alg) if args.workload == MAIN_WORKLOAD and args.algo in (
-        "auto", "fused") and chosen == "fused" else None
+    traffic = load_traffic(args.workload, C) if args.algo in ("auto", "fused") and \
+        chosen == "fused" else None
     h200 = H200_INV_PER_S.get(args.workload)
     out = {
         "metric": METRIC if C == 64 else f"{C}x{C} tril inverses/sec + achieved HBM GB/s "
@@ -271,6 +374,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernel_us_avg": k_avg * 1e6,
+        "kernel_us_per_launch": dist,
         "algorithmic_bytes_per_launch": bytes_alg,
         "copy_roofline_gbs": copy_gbs,
     }
