@@ -10,6 +10,10 @@ parallelize diagonal solves in Prefill", PR description) computes: for every
 matrix, by fp64 column forward substitution (``tril_oracle.c``). Inputs in
 float32, bfloat16 or binary16 are upcast to float64 exactly before the solve.
 
+For the fused path that first builds A from keys, cumulative log-decays and
+write strengths, ``kkt_*`` evaluate A from its definition in float64 and
+``kkt_tril_inv_*`` invert that A without rounding it.
+
 Pins (each in ``tests/test_oracle_pins.py``): exact rational Neumann series,
 the single-subdiagonal closed form, LAPACK inversion, the residual of
 (I + A) X = I, the leading-principal-block property for partial chunks,
@@ -36,7 +40,7 @@ def build(force: bool = True) -> str:
         tmp = _LIB + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-             "-o", tmp, _SRC])
+             "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -60,6 +64,10 @@ def _load():
         lib.oracle_tril_inv_packed_c.argtypes = [p, p, p, i64, i64, i32, ci, ci]
         lib.oracle_tril_inv_dense_c.restype = i64
         lib.oracle_tril_inv_dense_c.argtypes = [p, p, i64, i64, i32, ci, ci]
+        lib.oracle_kkt_packed.restype = i64
+        lib.oracle_kkt_packed.argtypes = [p, p, p, p, p, i64, i64, i32, ci, ci]
+        lib.oracle_kkt_dense.restype = i64
+        lib.oracle_kkt_dense.argtypes = [p, p, p, p, i64, i64, i32, ci, ci]
         lib.oracle_rne_bf16.restype = None
         lib.oracle_rne_bf16.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -148,6 +156,53 @@ def tril_inv_dense(A: np.ndarray, dtype: str = "f32", nthreads: int = 0) -> np.n
     if r < 0:
         raise ValueError("malformed dense problem")
     return X
+
+
+def kkt_packed(k: np.ndarray, g: np.ndarray, beta: np.ndarray, cu_seqlens,
+               k_dtype: str = "f32", nthreads: int = 0) -> np.ndarray:
+    """The delta-rule matrix A [T, H, 64] (float64) of every 64-token chunk
+    and head, from keys k [T, H, K] (``k_dtype``; beta has the same dtype),
+    float32 cumulative log-decays g [T, H, K] and write strengths beta [T, H].
+    Rows outside every chunk hold NaN."""
+    k64 = to_f64(k, k_dtype)
+    b64 = to_f64(beta, k_dtype)
+    g64 = to_f64(g, "f32")
+    T, H, K = k64.shape
+    assert g64.shape == (T, H, K) and b64.shape == (T, H)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    A = np.full((T, H, CHUNK), np.nan, np.float64)
+    r = _load().oracle_kkt_packed(_ptr(k64), _ptr(g64), _ptr(b64), _ptr(A), _ptr(cu),
+                                  cu.shape[0] - 1, T, H, K, nthreads)
+    if r < 0:
+        raise ValueError("malformed packed problem")
+    return A
+
+
+def kkt_dense(k: np.ndarray, g: np.ndarray, beta: np.ndarray, k_dtype: str = "f32",
+              nthreads: int = 0) -> np.ndarray:
+    """Dense counterpart of kkt_packed: k, g [B, T, H, K], beta [B, T, H]."""
+    k64 = to_f64(k, k_dtype)
+    b64 = to_f64(beta, k_dtype)
+    g64 = to_f64(g, "f32")
+    B, T, H, K = k64.shape
+    A = np.full((B, T, H, CHUNK), np.nan, np.float64)
+    r = _load().oracle_kkt_dense(_ptr(k64), _ptr(g64), _ptr(b64), _ptr(A), B, T, H, K, nthreads)
+    if r < 0:
+        raise ValueError("malformed dense problem")
+    return A
+
+
+def kkt_tril_inv_packed(k, g, beta, cu_seqlens, k_dtype: str = "f32",
+                        nthreads: int = 0) -> np.ndarray:
+    """Oracle of the fused path: A from its definition, kept in float64, then
+    X = (I + A)^-1 per chunk-head. Returns X [T, H, 64] (NaN outside chunks)."""
+    A = kkt_packed(k, g, beta, cu_seqlens, k_dtype, nthreads)
+    return tril_inv_packed(A, cu_seqlens, "f64", nthreads)
+
+
+def kkt_tril_inv_dense(k, g, beta, k_dtype: str = "f32", nthreads: int = 0) -> np.ndarray:
+    A = kkt_dense(k, g, beta, k_dtype, nthreads)
+    return tril_inv_dense(A, "f64", nthreads)
 
 
 def rne_bf16(x: np.ndarray) -> np.ndarray:

@@ -30,7 +30,13 @@
  * Layouts: packed A and X are [T, H, C] row-major (token, head, column) for
  * chunks of C tokens; dense ones are [B, T, H, C]. Element (token t, head h,
  * column j) is the entry (t - chunk_start, j) of that chunk-head's matrix.
+ *
+ * For the fused path that builds A from keys, decays and write strengths
+ * before inverting it, oracle_kkt_* evaluate that A from its definition (see
+ * there); the oracle of the fused path is that A, kept in double precision,
+ * followed by the inverse above.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -198,3 +204,84 @@ void oracle_rne_bf16(const uint32_t *f32bits, uint16_t *out, int64_t n) {
 }
 
 int oracle_num_threads(void) { return oracle_threads(0); }
+
+/*
+ * The matrix A itself, for the fused "build A, then invert" path. KDA prefill
+ * hands the solver its delta-rule intra-chunk matrix (same PR, PR
+ * description: KDA Prefill uses the shared solver's 64-token branch); for
+ * tokens i > j of one chunk and one head it is
+ *
+ *     A[i][j] = -beta_i * sum_d k[i][d] * k[j][d] * exp(g[i][d] - g[j][d]),
+ *
+ * with k the key rows (K channels), g the cumulative log-decay of each
+ * channel and beta_i the token's write strength; A[i][j] = 0 for j >= i.
+ * Evaluated from this definition in double precision: one exp per
+ * difference, the sum over d in increasing d.
+ *
+ * One chunk of L rows: k, g are row-major with rs_kg elements between
+ * consecutive tokens (H * K in [T, H, K]), beta has rs_b between tokens (H);
+ * A gets L full rows of 64 entries, rs_a apart.
+ */
+static void oracle_kkt_chunk(const double *k, const double *g, const double *beta,
+                             int64_t rs_kg, int64_t rs_b, int L, int K, double *A,
+                             int64_t rs_a) {
+    for (int i = 0; i < L; ++i) {
+        for (int j = 0; j < ORACLE_CHUNK; ++j) A[(int64_t)i * rs_a + j] = 0.0;
+        for (int j = 0; j < i; ++j) {
+            double s = 0.0;
+            for (int d = 0; d < K; ++d)
+                s += k[(int64_t)i * rs_kg + d] * k[(int64_t)j * rs_kg + d] *
+                     exp(g[(int64_t)i * rs_kg + d] - g[(int64_t)j * rs_kg + d]);
+            A[(int64_t)i * rs_a + j] = -beta[(int64_t)i * rs_b] * s;
+        }
+    }
+}
+
+/*
+ * Packed layout, 64-token chunks: k, g [T, H, K], beta [T, H], A out
+ * [T, H, 64] (doubles). Rows of every chunk are written in full; rows outside
+ * all chunks are untouched. Returns the number of chunk-head matrices, or -1
+ * on a malformed problem.
+ */
+int64_t oracle_kkt_packed(const double *k, const double *g, const double *beta, double *A,
+                          const int32_t *cu, int64_t nseq, int64_t T, int32_t H, int K,
+                          int nthreads) {
+    if (H <= 0 || nseq < 0 || K < 1) return -1;
+    int64_t nt = oracle_chunks_packed_c(cu, nseq, ORACLE_CHUNK, NULL, NULL, NULL, 0);
+    if (nt < 0 || (nseq > 0 && cu[nseq] > T)) return -1;
+    int64_t *start = (int64_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int64_t));
+    int32_t *len = (int32_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(int32_t));
+    if (!start || !len) { free(start); free(len); return -1; }
+    oracle_chunks_packed_c(cu, nseq, ORACLE_CHUNK, NULL, start, len, nt);
+    const int64_t work = nt * (int64_t)H;
+#pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
+    for (int64_t w = 0; w < work; ++w) {
+        int64_t c = w / H, h = w % H;
+        int64_t t0 = start[c];
+        oracle_kkt_chunk(k + (t0 * H + h) * K, g + (t0 * H + h) * K, beta + t0 * H + h,
+                         (int64_t)H * K, H, len[c], K, A + (t0 * H + h) * ORACLE_CHUNK,
+                         (int64_t)H * ORACLE_CHUNK);
+    }
+    free(start);
+    free(len);
+    return work;
+}
+
+/* Dense layout: k, g [B, T, H, K], beta [B, T, H], A [B, T, H, 64]; every
+ * batch element is one request of T tokens. */
+int64_t oracle_kkt_dense(const double *k, const double *g, const double *beta, double *A,
+                         int64_t B, int64_t T, int32_t H, int K, int nthreads) {
+    if (H <= 0 || B < 0 || T < 0 || K < 1) return -1;
+    const int64_t per_b = (T + ORACLE_CHUNK - 1) / ORACLE_CHUNK;
+    const int64_t work = B * per_b * (int64_t)H;
+#pragma omp parallel for schedule(static) num_threads(oracle_threads(nthreads))
+    for (int64_t w = 0; w < work; ++w) {
+        int64_t h = w % H, c = (w / H) % per_b, b = w / H / per_b;
+        int64_t t0 = b * T + c * ORACLE_CHUNK;
+        int L = (int)(T - c * ORACLE_CHUNK < ORACLE_CHUNK ? T - c * ORACLE_CHUNK : ORACLE_CHUNK);
+        oracle_kkt_chunk(k + (t0 * H + h) * K, g + (t0 * H + h) * K, beta + t0 * H + h,
+                         (int64_t)H * K, H, L, K, A + (t0 * H + h) * ORACLE_CHUNK,
+                         (int64_t)H * ORACLE_CHUNK);
+    }
+    return work;
+}

@@ -90,7 +90,9 @@ def _chunk_rows(lengths, chunk: int = CHUNK):
     return out
 
 
-def _one_chunk(seed: int, idx: int, L: int, H: int, K: int, chunk: int) -> np.ndarray:
+def _chunk_draws(seed: int, idx: int, L: int, H: int, K: int):
+    """Keys k [L, H, K] (unit rows), write strengths beta [L, H] and
+    within-chunk cumulative log-decays g [L, H, K] of chunk number idx."""
     rng = np.random.default_rng([seed, idx])
     k = rng.standard_normal((L, H, K))
     z = rng.standard_normal((L, H, K))
@@ -98,6 +100,11 @@ def _one_chunk(seed: int, idx: int, L: int, H: int, K: int, chunk: int) -> np.nd
     k /= np.linalg.norm(k, axis=-1, keepdims=True)
     beta = 1.0 / (1.0 + np.exp(-b))
     g = np.cumsum(-np.logaddexp(0.0, -(z + 3.0)), axis=0)  # logsigmoid(z + 3)
+    return k, g, beta
+
+
+def _one_chunk(seed: int, idx: int, L: int, H: int, K: int, chunk: int) -> np.ndarray:
+    k, g, beta = _chunk_draws(seed, idx, L, H, K)
     kq = (k * np.exp(g)).transpose(1, 0, 2)          # [H, L, K]
     kk = (k * np.exp(-g)).transpose(1, 2, 0)         # [H, K, L]
     S = np.matmul(kq, kk)                            # [H, L, L]
@@ -133,6 +140,33 @@ def delta_rule_A(lengths, H: int, seed: int, K: int = KEY_DIM, upper: str = "zer
     if upper != "zero":
         _fill_upper(A, chunks, upper, seed)
     return A
+
+
+def delta_rule_inputs(lengths, H: int, seed: int, K: int = KEY_DIM,
+                      threads: int | None = None):
+    """Packed float32 keys k [T, H, K], cumulative log-decays g [T, H, K]
+    (restarting at every 64-token chunk) and write strengths beta [T, H]:
+    the same draws from which delta_rule_A builds A, rounded to float32 once.
+    The matrix itself is not formed here."""
+    chunks = _chunk_rows(lengths, CHUNK)
+    T = int(sum(lengths))
+    k = np.zeros((T, H, K), np.float32)
+    g = np.zeros((T, H, K), np.float32)
+    beta = np.zeros((T, H), np.float32)
+    nthr = threads or min(16, os.cpu_count() or 1)
+
+    def work(i):
+        s, L = chunks[i]
+        kc, gc, bc = _chunk_draws(seed, i, L, H, K)
+        k[s:s + L], g[s:s + L], beta[s:s + L] = kc, gc, bc
+
+    if len(chunks) > 1 and nthr > 1:
+        with ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(work, range(len(chunks))))
+    else:
+        for i in range(len(chunks)):
+            work(i)
+    return k, g, beta
 
 
 def _fill_upper(A, chunks, mode, seed):

@@ -231,3 +231,90 @@ def read_chunk_maps_sized():
                 cases.append((size, cu, chunks))
     return cases
 
+
+
+# ---- the delta-rule matrix A built from keys, decays and write strengths ----
+#
+# Each check takes ``kkt(k, g, beta, cu) -> A``: float64 inputs k, g [T, H, K],
+# beta [T, H], int32 cu_seqlens; A [T, H, 64] for 64-token chunks that
+# restart at every request's first token. The decays g are float32 values
+# (the solver takes them in float32), so the checks draw them as such.
+
+def kkt_brute_force(k, g, beta, cu):
+    """A from its definition with Python floats and math.exp, chunk by chunk:
+    A[i][j] = -beta_i sum_d k[i][d] k[j][d] exp(g[i][d] - g[j][d]), j < i."""
+    import math
+    T, H, K = k.shape
+    A = np.full((T, H, 64), np.nan)
+    for s in range(len(cu) - 1):
+        for c0 in range(int(cu[s]), int(cu[s + 1]), 64):
+            L = min(64, int(cu[s + 1]) - c0)
+            for h in range(H):
+                for i in range(L):
+                    row = [0.0] * 64
+                    for j in range(i):
+                        acc = 0.0
+                        for d in range(K):
+                            acc += (float(k[c0 + i, h, d]) * float(k[c0 + j, h, d]) *
+                                    math.exp(float(g[c0 + i, h, d]) - float(g[c0 + j, h, d])))
+                        row[j] = -float(beta[c0 + i, h]) * acc
+                    A[c0 + i, h, :] = row
+    return A
+
+
+def check_kkt_scalar_key(kkt, seed=0):
+    """K = 1 and g = 0: A[i][j] = -beta_i k_i k_j below the diagonal, 0 on
+    and above it (exactly: exp(0) = 1)."""
+    rng = np.random.default_rng(seed)
+    lengths = [64, 20]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H = int(cu[-1]), 2
+    k = rng.standard_normal((T, H, 1))
+    g = np.zeros((T, H, 1))
+    beta = rng.random((T, H))
+    A = kkt(k, g, beta, cu)
+    for c0, L in ((0, 64), (64, 20)):
+        for h in range(H):
+            kv = k[c0:c0 + L, h, 0]
+            want = np.tril(-beta[c0:c0 + L, h, None] * (kv[:, None] * kv[None, :]), -1)
+            if not np.array_equal(A[c0:c0 + L, h, :L], want) or np.any(A[c0:c0 + L, h, L:] != 0):
+                return False
+    return True
+
+
+def check_kkt_uniform_decay(kkt, seed=1):
+    """A decay shared by all channels of a token, g[i][d] = gamma_i: then
+    A = -diag(beta) (E * K K^T) below the diagonal with E[i][j] =
+    exp(gamma_i - gamma_j) (a Gram matrix of the keys, evaluated by numpy)."""
+    rng = np.random.default_rng(seed)
+    T, H, K = 64, 1, 16
+    k = rng.standard_normal((T, H, K))
+    gamma = np.cumsum(-rng.random(T) * 0.2).astype(np.float32).astype(np.float64)
+    g = np.repeat(gamma[:, None, None], K, axis=2)
+    beta = rng.random((T, H))
+    A = kkt(k, g, beta, np.array([0, T], np.int32))
+    G = k[:, 0, :] @ k[:, 0, :].T
+    E = np.exp(gamma[:, None] - gamma[None, :])
+    want = np.tril(-beta[:, 0, None] * E * G, -1)
+    return bool(np.abs(A[:, 0, :] - want).max() <= 1e-12 * max(1.0, np.abs(want).max()))
+
+
+def check_kkt_brute_force(kkt, seed=2):
+    """Ragged requests (one longer than a chunk) against the brute force."""
+    rng = np.random.default_rng(seed)
+    lengths = [5, 70, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, K = int(cu[-1]), 2, 3
+    k = rng.standard_normal((T, H, K))
+    g = np.cumsum(-rng.random((T, H, K)) * 0.3, axis=0).astype(np.float32).astype(np.float64)
+    beta = rng.random((T, H))
+    A = kkt(k, g, beta, cu)
+    want = kkt_brute_force(k, g, beta, cu)
+    return bool(np.abs(A - want).max() <= 1e-13)
+
+
+def kkt_all(kkt):
+    """Names of the A-construction checks that fail (empty when all pass)."""
+    checks = {"scalar_key": check_kkt_scalar_key, "uniform_decay": check_kkt_uniform_decay,
+              "brute_force": check_kkt_brute_force}
+    return [n for n, f in checks.items() if not f(kkt)]

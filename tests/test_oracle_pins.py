@@ -171,6 +171,13 @@ _MUTANTS = {
     "ties_away": ("(rest == 0x8000u && (kept & 1u))", "(rest == 0x8000u)"),
     "dense_row0": ("int64_t row0 = b * T + c * C;",
                    "int64_t row0 = (b * per_b + c) * C;"),
+    # the delta-rule matrix A built from keys, decays and write strengths
+    "kkt_exp_sign": ("exp(g[(int64_t)i * rs_kg + d] - g[(int64_t)j * rs_kg + d])",
+                     "exp(g[(int64_t)j * rs_kg + d] - g[(int64_t)i * rs_kg + d])"),
+    "kkt_beta_of_column": ("-beta[(int64_t)i * rs_b] * s", "-beta[(int64_t)j * rs_b] * s"),
+    "kkt_keeps_diagonal": ("for (int j = 0; j < i; ++j) {\n            double s = 0.0;",
+                           "for (int j = 0; j <= i; ++j) {\n            double s = 0.0;"),
+    "kkt_drops_last_channel": ("for (int d = 0; d < K; ++d)", "for (int d = 0; d < K - 1; ++d)"),
 }
 
 
@@ -184,16 +191,22 @@ def _build_mutant(tmp_path, name):
     c = tmp_path / f"{name}.c"
     c.write_text(src)
     so = tmp_path / f"lib{name}.so"
+    return _load_lib(c, so)
+
+
+def _load_lib(c, so):
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o",
-                           str(so), str(c)])
+                           str(so), str(c), "-lm"])
     lib = ctypes.CDLL(str(so))
-    p, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
+    p, i64, i32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.oracle_inv_unit_lower.argtypes = [p, i64, ci, p, i64]
     lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
     lib.oracle_chunks_packed.restype = i64
     lib.oracle_rne_bf16.argtypes = [p, p, i64]
-    lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int]
+    lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, i32, ci]
     lib.oracle_tril_inv_dense.restype = i64
+    lib.oracle_kkt_packed.argtypes = [p, p, p, p, p, i64, i64, i32, ci, ci]
+    lib.oracle_kkt_packed.restype = i64
     return lib
 
 
@@ -244,7 +257,16 @@ def _pins_fail(lib):
                 got = X[b, c0:c0 + L, h, :L]
                 if not np.all(np.isfinite(got)) or np.abs(got - ref).max() > 1e-12:
                     return True
-    return False
+
+    def kkt(k, g, beta, cu):
+        k, g, beta = (np.ascontiguousarray(a, np.float64) for a in (k, g, beta))
+        T, H, K = k.shape
+        A = np.full((T, H, 64), np.nan)
+        lib.oracle_kkt_packed(_ptr(k), _ptr(g), _ptr(beta), _ptr(A), _ptr(cu), len(cu) - 1, T,
+                              H, K, 1)
+        return A
+
+    return bool(pins.kkt_all(kkt))
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -257,18 +279,7 @@ def test_unpatched_oracle_passes_the_same_gate(tmp_path):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "tril_oracle.c")).read()
     c = tmp_path / "plain.c"
     c.write_text(src)
-    so = tmp_path / "libplain.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o",
-                           str(so), str(c)])
-    lib = ctypes.CDLL(str(so))
-    p, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.oracle_inv_unit_lower.argtypes = [p, i64, ctypes.c_int, p, i64]
-    lib.oracle_chunks_packed.argtypes = [p, i64, p, p, p, i64]
-    lib.oracle_chunks_packed.restype = i64
-    lib.oracle_rne_bf16.argtypes = [p, p, i64]
-    lib.oracle_tril_inv_dense.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int]
-    lib.oracle_tril_inv_dense.restype = i64
-    assert not _pins_fail(lib)
+    assert not _pins_fail(_load_lib(c, tmp_path / "libplain.so"))
 
 
 # ---- the 16- and 32-token branches -------------------------------------------
@@ -313,3 +324,47 @@ def test_small_chunk_is_leading_block_of_64():
     for C in (16, 32):
         X = oracle.inv_unit_lower(M[:C, :C], width=C)
         assert np.array_equal(X, full[:C, :C])
+
+
+# ---- the delta-rule matrix A (fused "build A, then invert" path) --------------
+
+def _oracle_kkt(k, g, beta, cu):
+    return oracle.kkt_packed(k, g, beta, cu, "f64")
+
+
+def test_kkt_scalar_key_closed_form():
+    assert pins.check_kkt_scalar_key(_oracle_kkt)
+
+
+def test_kkt_uniform_decay_gram():
+    assert pins.check_kkt_uniform_decay(_oracle_kkt)
+
+
+def test_kkt_brute_force():
+    assert pins.check_kkt_brute_force(_oracle_kkt)
+
+
+def test_kkt_dense_equals_packed_and_inverse_composes():
+    """Dense driver equals the packed one on the same rows; the fused oracle
+    is the inverse (LAPACK) of that float64 A, never rounded in between."""
+    rng = np.random.default_rng(7)
+    B, T, H, K = 2, 70, 2, 8
+    k = rng.standard_normal((B, T, H, K))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)  # unit keys
+    g = np.cumsum(-rng.random((B, T, H, K)) * 0.1, axis=1).astype(np.float32)
+    beta = rng.random((B, T, H)).astype(np.float32)
+    Ad = oracle.kkt_dense(k, g, beta)
+    cu = np.array([0, T, 2 * T], np.int32)
+    Ap = oracle.kkt_packed(k.reshape(B * T, H, K), g.reshape(B * T, H, K), beta.reshape(B * T, H),
+                           cu)
+    assert np.array_equal(Ad.reshape(B * T, H, 64), Ap)
+    X = oracle.kkt_tril_inv_packed(k.reshape(B * T, H, K), g.reshape(B * T, H, K),
+                                   beta.reshape(B * T, H), cu)
+    Xd = oracle.kkt_tril_inv_dense(k, g, beta)
+    assert np.array_equal(Xd.reshape(B * T, H, 64), X)
+    for t0, L in ((0, 64), (64, 6), (70, 64), (134, 6)):
+        for h in range(H):
+            M = np.tril(Ap[t0:t0 + L, h, :L], -1)
+            ref = np.linalg.inv(np.eye(L) + M)
+            assert np.abs(X[t0:t0 + L, h, :L] - ref).max() < 1e-12 * max(1.0, np.abs(ref).max())
+
