@@ -11,6 +11,11 @@ the steps rotate over several independently generated buffer sets (more
 bytes than the 256 MB Infinity Cache) so that no step reads its input from
 the cache.
 
+Other workloads (--workload) are diagnostics: the other batch shapes, the
+16- and 32-token branches, and the path that builds A from keys, decays and
+write strengths inside the solver (timed beside the unfused pair: A stored,
+then solved).
+
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -27,22 +32,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak, AMD published
 # The pages' H200 solver times after the change they describe (context: a
 # different GPU, dtypes not stated), as inverses per second:
 #   8192 tokens x 64 heads (8192 matrices): 0.476 ms;  64 tokens x 64 heads: 0.0254 ms.
 H200_INV_PER_S = {"packed_16x512_h64_f32": 8192 / 0.476e-3, "packed_1x64_h64_f32": 64 / 0.0254e-3}
-WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_16x512_h64_f32",
-             "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32",
-             "packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"]
+SOLVE_WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_16x512_h64_f32",
+                   "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32",
+                   "packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"]
+KKT_WORKLOADS = ["packed_16x512_h64_k128_kkt_bf16_f32", "packed_16x512_h64_k128_kkt_f32_f32"]
+WORKLOADS = SOLVE_WORKLOADS + KKT_WORKLOADS
 MAIN_WORKLOAD = "packed_16x512_h64_f32"
 METRIC = "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads"
-# Kernel timed per chunk size, and the sources its code comes from (a
-# counter summary taken on other sources is not used).
-KERNELS = {64: "tril_inv_fused_mfma", 32: "tril_inv_c32", 16: "tril_inv_c16"}
-KERNEL_SOURCES = {64: ["tril_device.h", "tril_fused.hip", "tril_launch.h"],
-                  32: ["tril_device.h", "tril_small.hip", "tril_launch.h"],
-                  16: ["tril_device.h", "tril_small.hip", "tril_launch.h"]}
 COPY_KERNEL = "kda_probe_copy_kernel"
+
+
+def dtype_bytes(name: str) -> int:
+    return 2 if name in ("bf16", "f16") else 4
+
+
+def kernel_of(workload: str):
+    """(kernel name, sources its code comes from) of the kernel a workload
+    times; a counter summary taken on other sources is not used."""
+    if workload in KKT_WORKLOADS:
+        return "tril_kkt", ["tril_device.h", "tril_kkt.hip", "tril_launch.h"]
+    import synth
+    C = synth.CONFIGS[workload].get("chunk", 64)
+    if C == 64:
+        return "tril_inv_fused_mfma", ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
+    return f"tril_inv_c{C}", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
+
+
+def copy_bytes_of(workload: str) -> int:
+    """Bytes the copy probe moves each way for a workload: A's size, or the
+    decays' size for the path that builds A from keys."""
+    import synth
+    if workload in KKT_WORKLOADS:
+        cfg = synth.KKT_CONFIGS[workload]
+        return int(sum(synth.config_lengths(cfg))) * cfg["H"] * cfg["K"] * 4
+    cfg = synth.CONFIGS[workload]
+    return (int(sum(synth.config_lengths(cfg))) * cfg["H"] * cfg.get("chunk", 64) *
+            dtype_bytes(cfg["a_dtype"]))
 
 
 def traffic_file(workload: str) -> str:
@@ -61,9 +91,9 @@ def load_copy_probe():
     return lib
 
 
-def kernel_hash(C: int = 64) -> str:
+def kernel_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[C]:
+    for f in kernel_of(workload)[1]:
         with open(os.path.join(ROOT, "tril_solve_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -74,7 +104,13 @@ def algorithmic_bytes(lengths, H, a_bytes, x_bytes, C=64) -> int:
     return int(sum(lengths)) * H * C * (a_bytes + x_bytes)
 
 
-def load_traffic(workload: str, C: int):
+def kkt_algorithmic_bytes(lengths, H, K, k_bytes, x_bytes) -> int:
+    """Keys, decays (FP32) and write strengths read, full 64-wide rows of X
+    written: rows x H x (K (k + 4) + k + 64 x)."""
+    return int(sum(lengths)) * H * (K * (k_bytes + 4) + k_bytes + 64 * x_bytes)
+
+
+def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on other kernel sources."""
     try:
@@ -82,7 +118,7 @@ def load_traffic(workload: str, C: int):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash(C):
+    if t.get("kernel_hash") != kernel_hash(workload):
         return None
     return int(t["hbm_bytes_per_launch"])
 
@@ -101,20 +137,20 @@ def _counter_mean(csv_path: str, kernel: str, counter: str) -> tuple[float, int]
     return sum(vals) / len(vals), len(vals)
 
 
-def record_traffic(workload: str, C: int, a_bytes_total: int, csvs, out_path: str) -> dict:
-    """Counter summary of the solver kernel: FETCH_SIZE and WRITE_SIZE (KiB
+def record_traffic(workload: str, csvs, out_path: str) -> dict:
+    """Counter summary of a workload's kernel: FETCH_SIZE and WRITE_SIZE (KiB
     per dispatch) each scaled by what the same counter reads for the copy
-    probe moving a known byte count (A's size each way)."""
+    probe moving a known byte count each way."""
     fetch_csv, write_csv, copy_fetch_csv, copy_write_csv = csvs
-    k = KERNELS[C]
+    k = kernel_of(workload)[0]
     fetch, nf = _counter_mean(fetch_csv, k + "<", "FETCH_SIZE")
     write, nw = _counter_mean(write_csv, k + "<", "WRITE_SIZE")
     cfetch, _ = _counter_mean(copy_fetch_csv, COPY_KERNEL, "FETCH_SIZE")
     cwrite, _ = _counter_mean(copy_write_csv, COPY_KERNEL, "WRITE_SIZE")
-    known = a_bytes_total / 1024.0
+    known = copy_bytes_of(workload) / 1024.0
     fs, ws = known / cfetch, known / cwrite
     rd, wr = int(fetch * fs * 1024), int(write * ws * 1024)
-    t = {"kernel": k, "workload": workload, "kernel_hash": kernel_hash(C),
+    t = {"kernel": k, "workload": workload, "kernel_hash": kernel_hash(workload),
          "dispatches": {"fetch": nf, "write": nw},
          "fetch_size_kib_raw": round(fetch, 1), "write_size_kib_raw": round(write, 1),
          "copy_fetch_size_kib_raw": round(cfetch, 1), "copy_write_size_kib_raw": round(cwrite, 1),
@@ -169,62 +205,141 @@ def describe(d) -> str:
         shape = f"packed {len(d['lengths'])} x {d['lengths'][0]} tokens"
     else:
         shape = f"packed {len(d['lengths'])} ragged requests, {d['T_total']} tokens"
+    if "K" in d:
+        return (f"{shape}, {d['H']} heads, A built from {d['k_dtype']} keys (K={d['K']}), "
+                f"fp32 decays and {d['k_dtype']} write strengths -> {d['x_dtype']} X "
+                f"({d['num_chunks'] * d['H']} chunk-head 64x64 matrices)")
     C = d.get("chunk", 64)
     return (f"{shape}, {d['H']} heads, {d['a_dtype']} A -> {d['x_dtype']} X "
             f"({d['num_chunks'] * d['H']} chunk-head {C}x{C} matrices)")
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "split", "fused_valu"])
-    ap.add_argument("--workload", default=MAIN_WORKLOAD, choices=WORKLOADS,
-                    help="the default is the metric's workload; the others are diagnostics")
-    ap.add_argument("--sets", type=int, default=0,
-                    help="rotating input/output buffer sets (default: enough for >= 1 GB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", choices=["copy"], default=None,
-                    help="run only a plain copy of A's byte count (counter calibration)")
-    ap.add_argument("--record-traffic", nargs=5, default=None,
-                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
-                    help="write the HBM-traffic summary of --workload from rocprofv3 counter "
-                         "CSVs (no GPU use)")
-    args = ap.parse_args()
+class Timer:
+    """Launch timing on one stream: K back-to-back calls bracketed by HIP
+    events on that stream and by device synchronisation, plus a per-launch
+    distribution from individually bracketed calls (after the timed region)."""
 
-    if args.record_traffic:
-        import synth
-        cfg = synth.CONFIGS[args.workload]
-        C = cfg.get("chunk", 64)
-        lengths = synth.config_lengths(cfg)
-        a_bytes = 2 if cfg["a_dtype"] in ("bf16", "f16") else 4
-        total = int(sum(lengths)) * cfg["H"] * C * a_bytes
-        t = record_traffic(args.workload, C, total, args.record_traffic[:4],
-                           args.record_traffic[4])
-        log(json.dumps(t))
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, calls, steps, warmup):
+        torch, stream = self.torch, self.stream
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            calls[i % len(calls)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        avg = e0.elapsed_time(e1) * 1e-3 / steps  # seconds per call
+        reps = min(50, steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            calls[i % len(calls)]()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # microseconds
+        dist = {"median": per[len(per) // 2], "min": per[0],
+                "p90": per[int(0.9 * (len(per) - 1))], "launches": reps}
+        return el, avg, dist
+
+
+class CopyProbe:
+    """A plain streaming copy (read N, write N bytes) of a tensor's bytes into
+    a destination of its own, marshalled once per source."""
+
+    def __init__(self, torch, stream, dev):
+        self.torch, self.stream, self.dev = torch, stream, dev
+        self.lib = load_copy_probe()
+        self.calls = {}
+
+    def __call__(self, A):
+        fn = self.calls.get(A.data_ptr())
+        if fn is None:
+            nbytes = A.numel() * A.element_size()
+            D = self.torch.empty(nbytes // 4, dtype=self.torch.float32, device=self.dev)
+            if nbytes % 16 or D.numel() * 4 != nbytes:
+                raise RuntimeError("copy probe: source and destination sizes differ")
+            cargs = (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()), nbytes // 4,
+                     ctypes.c_void_p(self.stream.cuda_stream))
+            f = self.lib.kda_probe_copy_f32
+
+            def fn(D=D):
+                if f(*cargs) != 0:
+                    raise RuntimeError("copy probe failed")
+            self.calls[A.data_ptr()] = fn
+        fn()
+
+    def rate_gbs(self, tensors, ncopy=40):
+        """Read + write bytes per second of the copy over the rotation."""
+        torch = self.torch
+        for i in range(4):
+            self(tensors[i % len(tensors)])
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(self.stream)
+        for i in range(ncopy):
+            self(tensors[i % len(tensors)])
+        c1.record(self.stream)
+        torch.cuda.synchronize()
+        copy_s = c0.elapsed_time(c1) * 1e-3 / ncopy
+        t = tensors[0]
+        return 2 * t.numel() * t.element_size() / copy_s / 1e9
+
+    def only(self, tensors, args):
+        """--probe copy: copies only (counter calibration runs)."""
+        for _ in range(args.warmup + args.steps):
+            for t in tensors:
+                self(t)
+        self.torch.cuda.synchronize()
+        log(f"copy probe: {args.warmup + args.steps} x {len(tensors)} copies of "
+            f"{tensors[0].numel() * tensors[0].element_size()} bytes read + written")
         return 0
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        log("bench.py: this solver is measured on one GPU only; a multi-GPU run would shard "
-            "chunk-heads with no communication and is not part of this build.")
-        return 2
 
-    import numpy as np  # noqa: F401
-    import torch
+def base_line(args, el, k_avg, dist, mats, bytes_alg, nsets, metric, vs_baseline, config):
+    achieved = bytes_alg / k_avg / 1e9
+    return {
+        "metric": metric,
+        "value": mats * args.steps / el,
+        "unit": "inverses/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": el / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs_baseline,
+        "dtype": "f32",
+        "data": f"synthetic (seeded delta-rule generator, {nsets} rotating buffer sets)",
+        "config": config,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernel_us_avg": k_avg * 1e6,
+        "kernel_us_per_launch": dist,
+        "algorithmic_bytes_per_launch": bytes_alg,
+    }
 
+
+def run_solve(args, torch, np, dev, stream):
     import synth
     import tril_solve_amd as kt
 
-    dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.workload]
     d0 = synth.make(cfg)
     C = d0["chunk"]
     if C != 64 and args.algo not in ("auto", "fused"):
         log(f"bench.py: the {C}-token branch has a single kernel (algo auto or fused)")
         return 2
-    a_bytes = 2 if cfg["a_dtype"] in ("bf16", "f16") else 4
-    x_bytes = 2 if cfg["x_dtype"] in ("bf16", "f16") else 4
+    a_bytes, x_bytes = dtype_bytes(cfg["a_dtype"]), dtype_bytes(cfg["x_dtype"])
     H = cfg["H"]
     T = d0["T_total"]
     mats = d0["num_chunks"] * H
@@ -259,125 +374,32 @@ def main() -> int:
     ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=dev) if nbytes else None
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    probe = load_copy_probe()
-
-    # The copy probe has destinations of its own, each exactly the byte size of
-    # its source (X may be narrower than A, e.g. bf16 X from fp32 A). Its
-    # arguments are marshalled once per buffer set, like the solver calls.
-    copy_calls = {}
-
-    def copy(A, _X=None):
-        fn = copy_calls.get(A.data_ptr())
-        if fn is None:
-            nbytes = A.numel() * A.element_size()
-            D = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
-            if nbytes % 16 or D.numel() * 4 != nbytes:
-                raise RuntimeError("copy probe: source and destination sizes differ")
-            cargs = (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()), nbytes // 4,
-                     ctypes.c_void_p(stream.cuda_stream))
-            f = probe.kda_probe_copy_f32
-
-            def fn(D=D):
-                if f(*cargs) != 0:
-                    raise RuntimeError("copy probe failed")
-            copy_calls[A.data_ptr()] = fn
-        fn()
-
+    copy = CopyProbe(torch, stream, dev)
     if args.probe == "copy":
-        for _ in range(args.warmup + args.steps):
-            for A, X in sets:
-                copy(A, X)
-        torch.cuda.synchronize()
-        log(f"copy probe: {args.warmup + args.steps} x {len(sets)} copies of "
-            f"{A.numel() * A.element_size()} bytes read + written")
-        return 0
+        return copy.only([A for A, _ in sets], args)
 
     if dense:
         calls = [kt.prepare_dense(A, X, workspace=ws, algo=args.algo) for A, X in sets]
     else:
         calls = [kt.prepare_packed(A, X, cu, workspace=ws, algo=args.algo) for A, X in sets]
-
-    for i in range(args.warmup):
-        calls[i % len(calls)]()
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back solver calls on the current stream,
-    # bracketed by HIP events on that stream and by device synchronisation.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % len(calls)]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    k_avg = e0.elapsed_time(e1) * 1e-3 / args.steps  # seconds per launch
-
-    # per-launch distribution (diagnostic, after the timed region): each of
-    # up to 50 launches bracketed by its own pair of events on the stream
-    reps = min(50, args.steps)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        calls[i % len(calls)]()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # microseconds
-    dist = {"median": per[len(per) // 2], "min": per[0], "p90": per[int(0.9 * (len(per) - 1))],
-            "launches": reps}
+    el, k_avg, dist = Timer(torch, stream).run(calls, args.steps, args.warmup)
 
     # measured copy roofline: a plain streaming copy of A's byte count, read
     # and written, same buffer rotation, events over the region
-    if a_bytes == 4:
-        for i in range(4):
-            copy(*sets[i % len(sets)])
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        ncopy = 40
-        c0.record(stream)
-        for i in range(ncopy):
-            copy(*sets[i % len(sets)])
-        c1.record(stream)
-        torch.cuda.synchronize()
-        copy_s = c0.elapsed_time(c1) * 1e-3 / ncopy
-        copy_gbs = 2 * sets[0][0].numel() * 4 / copy_s / 1e9
-    else:
-        copy_gbs = None
+    copy_gbs = copy.rate_gbs([A for A, _ in sets]) if a_bytes == 4 else None
 
-    value = mats * args.steps / el
-    achieved = bytes_alg / k_avg / 1e9
-    traffic = load_traffic(args.workload, C) if args.algo in ("auto", "fused") and \
-        chosen == "fused" else None
     h200 = H200_INV_PER_S.get(args.workload)
-    out = {
-        "metric": METRIC if C == 64 else f"{C}x{C} tril inverses/sec + achieved HBM GB/s "
-                                         f"(% peak)",
-        "value": value,
-        "unit": "inverses/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": el / args.steps * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": (value / h200) if h200 else None,
-        "dtype": "f32",
-        "data": f"synthetic (seeded delta-rule generator, {len(sets)} rotating buffer sets)",
-        "config": {"workload": describe(d0), "tokens": T, "heads": H,
-                   "requests": len(d0["lengths"]), "matrices": mats,
-                   "a_dtype": cfg["a_dtype"], "x_dtype": cfg["x_dtype"],
-                   "algo": args.algo, "plan": chosen},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "kernel_us_avg": k_avg * 1e6,
-        "kernel_us_per_launch": dist,
-        "algorithmic_bytes_per_launch": bytes_alg,
-        "copy_roofline_gbs": copy_gbs,
-    }
+    metric = METRIC if C == 64 else f"{C}x{C} tril inverses/sec + achieved HBM GB/s (% peak)"
+    value = mats * args.steps / el
+    out = base_line(args, el, k_avg, dist, mats, bytes_alg, len(sets), metric,
+                    (value / h200) if h200 else None,
+                    {"workload": describe(d0), "tokens": T, "heads": H,
+                     "requests": len(d0["lengths"]), "matrices": mats,
+                     "a_dtype": cfg["a_dtype"], "x_dtype": cfg["x_dtype"],
+                     "algo": args.algo, "plan": chosen})
+    if args.algo in ("auto", "fused") and chosen == "fused":
+        out["roofline"]["traffic"] = load_traffic(args.workload)
+    out["copy_roofline_gbs"] = copy_gbs
     if not args.no_cpu_baseline and args.workload == MAIN_WORKLOAD:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(d0)
@@ -385,6 +407,118 @@ def main() -> int:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
     return 0
+
+
+def run_kkt(args, torch, np, dev, stream):
+    """The path that builds A from keys k, decays g and write strengths beta
+    inside the solver; also times the unfused pair (A stored in FP32 by the
+    matrix-only kernel, then the 64-token solver) on the same inputs."""
+    import synth
+    import tril_solve_amd as kt
+
+    cfg = synth.KKT_CONFIGS[args.workload]
+    d0 = synth.make_kkt(cfg)
+    kb, xb = dtype_bytes(cfg["k_dtype"]), dtype_bytes(cfg["x_dtype"])
+    H, K, T = cfg["H"], cfg["K"], d0["T_total"]
+    mats = d0["num_chunks"] * H
+    bytes_alg = kkt_algorithmic_bytes(d0["lengths"], H, K, kb, xb)
+    nsets = args.sets or max(1, min(16, -(-(1 << 30) // bytes_alg)))
+    x_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["x_dtype"], torch.float32)
+    k_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["k_dtype"], torch.float32)
+
+    def to_dev(a):
+        if k_dt != torch.float32:
+            return torch.from_numpy(a.view(np.int16)).view(k_dt).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    sets = []
+    for i in range(nsets):
+        d = d0
+        if i:
+            c = dict(cfg)
+            c["seed"] = cfg["seed"] + 100 * i
+            d = synth.make_kkt(c)
+        kd, gd, bd = to_dev(d["k"]), torch.from_numpy(d["g"]).to(dev), to_dev(d["beta"])
+        sets.append((kd, gd, bd, torch.empty((T, H, 64), dtype=x_dt, device=dev)))
+    cu = torch.from_numpy(d0["cu_seqlens"]).to(dev)
+    torch.cuda.synchronize()
+
+    copy = CopyProbe(torch, stream, dev)
+    if args.probe == "copy":
+        return copy.only([s[1] for s in sets], args)
+
+    calls = [kt.prepare_kkt(k, g, b, X, cu, solve=True) for k, g, b, X in sets]
+    timer = Timer(torch, stream)
+    el, k_avg, dist = timer.run(calls, args.steps, args.warmup)
+
+    # the unfused pair on the same inputs: FP32 A written, then read back
+    A32 = torch.empty((T, H, 64), dtype=torch.float32, device=dev)
+    pairs = []
+    for k, g, b, X in sets:
+        build = kt.prepare_kkt(k, g, b, A32, cu, solve=False)
+        solve = kt.prepare_packed(A32, X, cu, algo="fused")
+        pairs.append(lambda build=build, solve=solve: (build(), solve()))
+    _, pair_avg, _ = timer.run(pairs, max(10, args.steps // 4), min(args.warmup, 5))
+
+    copy_gbs = copy.rate_gbs([s[1] for s in sets])
+    flops = 10 * 2 * 16 * 16 * K * mats  # the ten 16 x 16 blocks of A, K-long products
+    out = base_line(args, el, k_avg, dist, mats, bytes_alg, len(sets),
+                    f"delta-rule 64x64 chunk inverses/sec with A built in-kernel from keys "
+                    f"(K={K}) + achieved HBM GB/s (% peak)", None,
+                    {"workload": describe(d0), "tokens": T, "heads": H, "key_dim": K,
+                     "requests": len(d0["lengths"]), "matrices": mats,
+                     "k_dtype": cfg["k_dtype"], "x_dtype": cfg["x_dtype"], "plan": "fused"})
+    out["roofline"]["traffic"] = load_traffic(args.workload)
+    out["mfma_fp32"] = {"tflops": flops / k_avg / 1e12, "peak": MFMA_F32_PEAK_TFLOPS,
+                        "frac": flops / k_avg / 1e12 / MFMA_F32_PEAK_TFLOPS}
+    out["unfused_pair_us_avg"] = pair_avg * 1e6
+    out["unfused_over_fused"] = pair_avg / k_avg
+    out["copy_roofline_gbs"] = copy_gbs
+    out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "split", "fused_valu"])
+    ap.add_argument("--workload", default=MAIN_WORKLOAD, choices=WORKLOADS,
+                    help="the default is the metric's workload; the others are diagnostics")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating input/output buffer sets (default: enough for >= 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", choices=["copy"], default=None,
+                    help="run only a plain copy of the input's byte count (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
+                    help="write the HBM-traffic summary of --workload from rocprofv3 counter "
+                         "CSVs (no GPU use)")
+    args = ap.parse_args()
+
+    if args.record_traffic:
+        t = record_traffic(args.workload, args.record_traffic[:4], args.record_traffic[4])
+        log(json.dumps(t))
+        return 0
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py: this solver is measured on one GPU only; a multi-GPU run would shard "
+            "chunk-heads with no communication and is not part of this build.")
+        return 2
+
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    if args.workload in KKT_WORKLOADS:
+        if args.algo not in ("auto", "fused"):
+            log("bench.py: the build-A path has a single kernel (algo auto or fused)")
+            return 2
+        return run_kkt(args, torch, np, dev, stream)
+    return run_solve(args, torch, np, dev, stream)
 
 
 if __name__ == "__main__":

@@ -173,6 +173,57 @@ kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
                                      size_t workspace_bytes, kda_algo algo,
                                      hipStream_t stream);
 
+/*
+ * The matrix built inside the solver. KDA prefill hands the 64-token branch
+ * (same PR, PR description) its delta-rule intra-chunk matrix; for tokens
+ * i > j of one 64-token chunk and one head
+ *
+ *     A[i][j] = -beta_i * sum_d k[i][d] * k[j][d] * exp(g[i][d] - g[j][d]),
+ *
+ * and A[i][j] = 0 for j >= i. These calls take the keys, decays and write
+ * strengths instead of A:
+ *   k      [rows, H, K] of k_dtype: key rows, K channels; K a multiple of 16,
+ *          16 <= K <= 256 (other K: KDA_ERR_UNSUPPORTED).
+ *   g      [rows, H, K] FP32: cumulative log-decay of each channel (only
+ *          differences within a chunk enter; the kernels evaluate
+ *          exp(g_i - g_r) exp(g_r - g_j) with r the first row of i's 16-row
+ *          block, so g should not increase along a chunk by more than ~80
+ *          within 16 tokens, as cumulative sums of log-gates <= 0 never do).
+ *   beta   [rows, H] of k_dtype: write strengths.
+ * rows = total_tokens (packed, with cu_seqlens and optional chunk_indices as
+ * for kda_tril_inv_packed) or B * T (dense, [B, T, H, ...]). k, g and the
+ * output must be 16-byte aligned, beta aligned to its element size, and the
+ * output must not overlap the inputs. All arithmetic is FP32 (k and beta
+ * widened exactly); A is never rounded before the inverse.
+ *
+ *   kda_kkt_tril_inv_*  X = (I + A)^-1, [rows, H, 64] of x_dtype, written as
+ *                       kda_tril_inv_* writes it. A never goes to memory.
+ *   kda_kkt_*           A itself, [rows, H, 64] of a_dtype: every valid row
+ *                       in full, exact zeros on and above the diagonal and in
+ *                       columns >= L (the input of kda_tril_inv_*).
+ * No workspace; the fused/split plans do not apply.
+ */
+kda_status kda_kkt_tril_inv_packed(const void *k, const float *g, const void *beta,
+                                   kda_dtype k_dtype, void *X, kda_dtype x_dtype,
+                                   const int32_t *cu_seqlens, int64_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t K,
+                                   const int32_t *chunk_indices, int64_t num_chunks,
+                                   hipStream_t stream);
+
+kda_status kda_kkt_tril_inv_dense(const void *k, const float *g, const void *beta,
+                                  kda_dtype k_dtype, void *X, kda_dtype x_dtype, int64_t B,
+                                  int64_t T, int32_t H, int32_t K, hipStream_t stream);
+
+kda_status kda_kkt_packed(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                          void *A, kda_dtype a_dtype, const int32_t *cu_seqlens,
+                          int64_t num_seqs, int64_t total_tokens, int32_t H, int32_t K,
+                          const int32_t *chunk_indices, int64_t num_chunks,
+                          hipStream_t stream);
+
+kda_status kda_kkt_dense(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                         void *A, kda_dtype a_dtype, int64_t B, int64_t T, int32_t H, int32_t K,
+                         hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);
 

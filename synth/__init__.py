@@ -56,6 +56,15 @@ CONFIGS = {
                                          a_dtype="f32", x_dtype="f32", seed=6, chunk=32),
 }
 
+# Workloads of the path that builds A from keys k, decays g and write
+# strengths beta: k and beta in k_dtype, g in float32, X in x_dtype.
+KKT_CONFIGS = {
+    "packed_16x512_h64_k128_kkt_bf16_f32": dict(layout="packed", lengths=[512] * 16, H=64, K=128,
+                                                 k_dtype="bf16", x_dtype="f32", seed=7),
+    "packed_16x512_h64_k128_kkt_f32_f32": dict(layout="packed", lengths=[512] * 16, H=64, K=128,
+                                                k_dtype="f32", x_dtype="f32", seed=8),
+}
+
 
 def ragged_lengths(n: int = 48, lo: int = 1, hi: int = 1500, seed: int = 0) -> list[int]:
     """Request lengths uniform in [lo, hi] (seed 0 gives T = 33,139 tokens in
@@ -228,3 +237,29 @@ def make(name_or_cfg, upper: str = "zero") -> dict:
         out["A"] = A
         out["cu_seqlens"] = cu_seqlens(lengths)
     return out
+
+
+def make_kkt(name_or_cfg) -> dict:
+    """Materialise one workload of the build-A-from-keys path: ``k`` [T, H, K]
+    and ``beta`` [T, H] (float32, or uint16 bit patterns for bf16 / f16),
+    ``g`` [T, H, K] float32, in the packed or dense ([B, T, ...]) layout, plus
+    ``cu_seqlens`` (packed), the lengths and the config fields."""
+    cfg = dict(KKT_CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    lengths = config_lengths(cfg)
+    k, g, beta = delta_rule_inputs(lengths, cfg["H"], cfg["seed"], K=cfg["K"])
+    if cfg["k_dtype"] == "bf16":
+        k, beta = to_bf16_bits(k), to_bf16_bits(beta)
+    elif cfg["k_dtype"] == "f16":
+        k, beta = to_f16_bits(k), to_f16_bits(beta)
+    out = dict(cfg)
+    out["lengths"] = lengths
+    out["T_total"] = int(sum(lengths))
+    out["num_chunks"] = len(_chunk_rows(lengths, CHUNK))
+    if cfg["layout"] == "dense":
+        B, T, H, K = cfg["B"], cfg["T"], cfg["H"], cfg["K"]
+        k, g, beta = k.reshape(B, T, H, K), g.reshape(B, T, H, K), beta.reshape(B, T, H)
+    else:
+        out["cu_seqlens"] = cu_seqlens(lengths)
+    out["k"], out["g"], out["beta"] = k, g, beta
+    return out
+

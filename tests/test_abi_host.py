@@ -196,3 +196,48 @@ def test_head_limit(kt):
     with pytest.raises(kt.KdaError) as e:
         kt.kda_tril_inv_workspace_size(64, 1, 0, 4097, "auto")
     assert e.value.status == U
+
+
+# ---- A built from keys, decays and write strengths ---------------------------
+
+def _kkt_p(kt, k=0x10000, g=0x20000, beta=0x30000, kd=0, X=0x90000000, xd=0, cu=0x2000, nseq=1,
+           T=64, H=2, K=128, cmap=None, nch=0, solve=True):
+    fn = kt._lib.kda_kkt_tril_inv_packed if solve else kt._lib.kda_kkt_packed
+    return fn(P(k), P(g), P(beta), kd, P(X), xd, P(cu), nseq, T, H, K, P(cmap), nch, None)
+
+
+def _kkt_d(kt, k=0x10000, g=0x20000, beta=0x30000, kd=0, X=0x90000000, xd=0, B=1, T=64, H=2,
+           K=128, solve=True):
+    fn = kt._lib.kda_kkt_tril_inv_dense if solve else kt._lib.kda_kkt_dense
+    return fn(P(k), P(g), P(beta), kd, P(X), xd, B, T, H, K, None)
+
+
+def test_kkt_argument_validation(kt):
+    E, U = kt.KDA_ERR_INVALID_ARG, kt.KDA_ERR_UNSUPPORTED
+    for solve in (True, False):
+        for K in (8, 24, 100, 272, 512):       # not a multiple of 16, or too wide
+            assert _kkt_p(kt, K=K, solve=solve) == U
+        assert _kkt_p(kt, K=0, solve=solve) == E
+        assert _kkt_p(kt, kd=3, solve=solve) == E
+        assert _kkt_p(kt, xd=7, solve=solve) == E
+        assert _kkt_p(kt, H=0, solve=solve) == E
+        assert _kkt_p(kt, H=4097, solve=solve) == U
+        assert _kkt_p(kt, k=None, solve=solve) == E
+        assert _kkt_p(kt, g=None, solve=solve) == E
+        assert _kkt_p(kt, beta=None, solve=solve) == E
+        assert _kkt_p(kt, cu=None, solve=solve) == E
+        assert _kkt_p(kt, k=0x10008, solve=solve) == E      # misaligned keys
+        assert _kkt_p(kt, g=0x20004, solve=solve) == E      # misaligned decays
+        assert _kkt_p(kt, beta=0x30002, solve=solve) == E   # fp32 beta not 4-byte aligned
+        # X starting inside the 64 x 2 x 128 fp32 keys overlaps them
+        assert _kkt_p(kt, X=0x10000 + 64 * 2 * 128 * 4 - 16, solve=solve) == E
+        assert _kkt_p(kt, X=0x30000 + 64 * 2 * 4 - 16, solve=solve) == E  # overlaps beta
+        assert _kkt_p(kt, cmap=0x3000, nch=0, solve=solve) == E
+        assert _kkt_p(kt, T=-1, solve=solve) == E
+        assert _kkt_p(kt, T=2**31, solve=solve) == U
+        assert _kkt_d(kt, B=-1, solve=solve) == E
+        assert _kkt_d(kt, K=40, solve=solve) == U
+        # empty problems return before touching the device
+        assert _kkt_p(kt, T=0, k=None, g=None, beta=None, X=None, cu=None, solve=solve) == kt.KDA_OK
+        assert _kkt_d(kt, B=0, solve=solve) == kt.KDA_OK
+        assert _kkt_d(kt, T=0, k=None, g=None, beta=None, X=None, solve=solve) == kt.KDA_OK

@@ -1,0 +1,196 @@
+"""GPU parity of the path that builds the delta-rule matrix A from keys,
+decays and write strengths (kda_kkt_tril_inv_*, kda_kkt_*) against the fp64
+oracle, which evaluates A from its definition and inverts it without
+rounding.
+
+Bar: X as for the solver (fp32 |X - X_ref| <= 2e-5 (1 + |X_ref|), bf16 / f16
+with their relative terms, residual of the fp32 X against the oracle's
+float64 A <= 1e-4); A from kda_kkt_* to the same elementwise bounds. Exact
+zeros and the fused-equals-unfused identity are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_helpers as gh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+# full chunks, partial last chunks, a one-token request, a request of 3 chunks
+LENGTHS = [64, 37, 1, 150, 16, 70]
+
+
+@pytest.fixture(scope="module")
+def kt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tril_solve_amd
+    return tril_solve_amd
+
+
+def _inputs(lengths, H, K, k_dtype, seed):
+    k, g, beta = synth.delta_rule_inputs(lengths, H, seed, K=K)
+    if k_dtype == "bf16":
+        k, beta = synth.to_bf16_bits(k), synth.to_bf16_bits(beta)
+    elif k_dtype == "f16":
+        k, beta = synth.to_f16_bits(k), synth.to_f16_bits(beta)
+    return k, g, beta
+
+
+def _dev(k, g, beta, k_dtype):
+    return (gh.to_torch_input(k, k_dtype, DEV), torch.from_numpy(g).to(DEV),
+            gh.to_torch_input(beta, k_dtype, DEV))
+
+
+def _solve(kt, kd, gd, bd, cu, x_dtype="f32", solve=True, out=None, chunk_indices=None):
+    shape = kd.shape[:-1] + (64,)
+    X = out if out is not None else torch.empty(shape, dtype=gh.out_torch_dtype(x_dtype),
+                                                device=DEV)
+    cud = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).to(DEV)
+    if solve:
+        kt.kda_kkt_tril_inv(kd, gd, bd, X, cud, chunk_indices=chunk_indices)
+    else:
+        kt.kda_kkt(kd, gd, bd, X, cud, chunk_indices=chunk_indices)
+    torch.cuda.synchronize()
+    return X
+
+
+@pytest.mark.parametrize("K", [16, 64, 128])
+@pytest.mark.parametrize("H", [1, 3, 8])
+def test_fused_parity(kt, H, K):
+    print(f"\n[kkt] fused H={H} K={K}", flush=True)
+    k, g, beta = _inputs(LENGTHS, H, K, "f32", seed=50 + H + K)
+    cu = synth.cu_seqlens(LENGTHS)
+    got = gh.to_numpy_f64(_solve(kt, *_dev(k, g, beta, "f32"), cu))
+    A64 = oracle.kkt_packed(k, g, beta, cu)
+    ref = oracle.tril_inv_packed(A64, cu, "f64")
+    e = gh.excess(got, ref, "f32")
+    assert e <= 0, f"exceeds tolerance by {e:.3g}"
+    assert gh.residual_chunks(A64, got, gh.all_chunk_heads(LENGTHS, H)) <= gh.RESIDUAL_TOL
+
+
+@pytest.mark.parametrize("K", [16, 128])
+@pytest.mark.parametrize("H", [2, 5])
+def test_matrix_alone_parity_and_exact_zeros(kt, H, K):
+    k, g, beta = _inputs(LENGTHS, H, K, "f32", seed=60 + H + K)
+    cu = synth.cu_seqlens(LENGTHS)
+    A = _solve(kt, *_dev(k, g, beta, "f32"), cu, solve=False)
+    got = gh.to_numpy_f64(A)
+    ref = oracle.kkt_packed(k, g, beta, cu)
+    e = gh.excess(got, ref, "f32")
+    assert e <= 0, f"exceeds tolerance by {e:.3g}"
+    for s, L, h in gh.all_chunk_heads(LENGTHS, H):
+        blk = got[s:s + L, h]
+        assert np.all(np.triu(blk[:, :L]) == 0) and np.all(blk[:, L:] == 0)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("k_dtype", ["f32", "bf16", "f16"])
+def test_dtype_matrix(kt, k_dtype, x_dtype):
+    print(f"\n[kkt] dtypes {k_dtype}->{x_dtype}", flush=True)
+    H, K = 4, 128
+    k, g, beta = _inputs(LENGTHS, H, K, k_dtype, seed=70)
+    cu = synth.cu_seqlens(LENGTHS)
+    dv = _dev(k, g, beta, k_dtype)
+    got = gh.to_numpy_f64(_solve(kt, *dv, cu, x_dtype))
+    ref = oracle.kkt_tril_inv_packed(k, g, beta, cu, k_dtype)
+    e = gh.excess(got, ref, x_dtype)
+    assert e <= 0, f"X exceeds tolerance by {e:.3g}"
+    gotA = gh.to_numpy_f64(_solve(kt, *dv, cu, x_dtype, solve=False))
+    refA = oracle.kkt_packed(k, g, beta, cu, k_dtype)
+    e = gh.excess(gotA, refA, x_dtype)
+    assert e <= 0, f"A exceeds tolerance by {e:.3g}"
+
+
+@pytest.mark.parametrize("k_dtype", ["f32", "bf16"])
+def test_fused_equals_unfused_bitwise(kt, k_dtype):
+    """X from the fused call equals, bit for bit, the 64-token solver applied
+    to the FP32 A that kda_kkt_* stores: both solve the same FP32 values with
+    the same code, the fused one without the round trip through memory."""
+    H, K = 6, 128
+    k, g, beta = _inputs(LENGTHS, H, K, k_dtype, seed=71)
+    cu = synth.cu_seqlens(LENGTHS)
+    dv = _dev(k, g, beta, k_dtype)
+    Xf = _solve(kt, *dv, cu)
+    A = _solve(kt, *dv, cu, solve=False)
+    Xu = kt.tril_inv(A, torch.from_numpy(cu).to(DEV), algo="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(Xf, Xu)
+
+
+def test_dense_equals_packed_and_chunk_map(kt):
+    B, T, H, K = 3, 100, 4, 64
+    k, g, beta = _inputs([T] * B, H, K, "f32", seed=72)
+    cu = synth.cu_seqlens([T] * B)
+    dv = _dev(k, g, beta, "f32")
+    Xp = _solve(kt, *dv, cu)
+    kd, gd, bd = dv
+    Xd = _solve(kt, kd.view(B, T, H, K), gd.view(B, T, H, K), bd.view(B, T, H), None)
+    assert torch.equal(Xd.view(B * T, H, 64), Xp)
+    Ad = _solve(kt, kd.view(B, T, H, K), gd.view(B, T, H, K), bd.view(B, T, H), None, solve=False)
+    Ap = _solve(kt, *dv, cu, solve=False)
+    assert torch.equal(Ad.view(B * T, H, 64), Ap)
+    cmap = torch.from_numpy(gh.host_chunk_map([T] * B)).to(DEV)
+    Xm = _solve(kt, *dv, cu, chunk_indices=cmap)
+    assert torch.equal(Xm, Xp)
+
+
+@pytest.mark.parametrize("solve", [True, False])
+def test_rows_outside_chunks_untouched(kt, solve):
+    H, K = 3, 32
+    k, g, beta = _inputs(LENGTHS, H, K, "f32", seed=73)
+    n = k.shape[0]
+    extra = 9
+    kp = np.concatenate([k, np.full((extra, H, K), np.nan, np.float32)])
+    gp = np.concatenate([g, np.full((extra, H, K), np.nan, np.float32)])
+    bp = np.concatenate([beta, np.full((extra, H), np.nan, np.float32)])
+    canary = -777.0
+    out = torch.full((n + extra, H, 64), canary, device=DEV)
+    X = _solve(kt, *_dev(kp, gp, bp, "f32"), synth.cu_seqlens(LENGTHS), solve=solve, out=out)
+    assert bool((X[n:] == canary).all())
+    assert not bool((X[:n] == canary).any())
+    assert bool(torch.isfinite(X[:n]).all())
+
+
+def test_zero_keys_give_identity(kt):
+    """k = 0 (any decays, beta): A = 0 exactly, so X = I exactly."""
+    H, K = 2, 16
+    T = sum(LENGTHS)
+    rng = np.random.default_rng(3)
+    k = np.zeros((T, H, K), np.float32)
+    g = np.cumsum(-rng.random((T, H, K)), axis=0).astype(np.float32)
+    beta = rng.random((T, H)).astype(np.float32)
+    cu = synth.cu_seqlens(LENGTHS)
+    X = gh.to_numpy_f64(_solve(kt, *_dev(k, g, beta, "f32"), cu))
+    for s, L, h in gh.all_chunk_heads(LENGTHS, H):
+        want = np.zeros((L, 64))
+        want[:, :L] = np.eye(L)
+        assert np.array_equal(X[s:s + L, h], want)
+
+
+def test_full_workload_sampled(kt):
+    """16 requests x 512 tokens, 64 heads, K = 128, bf16 keys: 16 sampled
+    chunks (all 64 heads each) against the oracle, every row's unit diagonal
+    and zero upper triangle checked on the device."""
+    name = "packed_16x512_h64_k128_kkt_bf16_f32"
+    print(f"\n[kkt] workload {name}", flush=True)
+    d = synth.make_kkt(name)
+    dv = _dev(d["k"], d["g"], d["beta"], d["k_dtype"])
+    X = _solve(kt, *dv, d["cu_seqlens"])
+    T, H = d["T_total"], d["H"]
+    t = X.view(T // 64, 64, H, 64).permute(0, 2, 1, 3)
+    assert bool((torch.diagonal(t, dim1=2, dim2=3) == 1).all())
+    upper = torch.triu(torch.ones(64, 64, device=DEV, dtype=torch.bool), 1)
+    assert bool((t[:, :, upper] == 0).all())
+    got = gh.to_numpy_f64(X)
+    rng = np.random.default_rng(4)
+    for c in rng.choice(T // 64, 16, replace=False):
+        s = 64 * int(c)
+        sl = slice(s, s + 64)
+        ref = oracle.kkt_tril_inv_packed(d["k"][sl], d["g"][sl], d["beta"][sl], [0, 64],
+                                         d["k_dtype"])
+        e = gh.excess(got[sl], ref, "f32")
+        assert e <= 0, f"chunk {c}: exceeds tolerance by {e:.3g}"

@@ -54,9 +54,19 @@ _lib.kda_tril_inv_packed_chunk.restype = ctypes.c_int
 _lib.kda_tril_inv_packed_chunk.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64,
                                            _i32, _i32, _p, _i64, _p, _sz, ctypes.c_int, _p]
 
+for _n in ("kda_kkt_tril_inv_packed", "kda_kkt_packed"):
+    getattr(_lib, _n).restype = ctypes.c_int
+    getattr(_lib, _n).argtypes = [_p, _p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64, _i32,
+                                  _i32, _p, _i64, _p]
+for _n in ("kda_kkt_tril_inv_dense", "kda_kkt_dense"):
+    getattr(_lib, _n).restype = ctypes.c_int
+    getattr(_lib, _n).argtypes = [_p, _p, _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i32,
+                                  _i32, _p]
+
 EXPORTED = ("kda_tril_inv_workspace_size", "kda_tril_inv_dense", "kda_tril_inv_packed",
             "kda_status_string", "kda_tril_auto_plan", "kda_tril_inv_dense_chunk",
-            "kda_tril_inv_packed_chunk")
+            "kda_tril_inv_packed_chunk", "kda_kkt_tril_inv_packed", "kda_kkt_tril_inv_dense",
+            "kda_kkt_packed", "kda_kkt_dense")
 CHUNK_SIZES = (16, 32, 64)
 
 
@@ -239,3 +249,63 @@ def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None
         kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=chunk_indices, workspace=ws,
                             algo=algo, stream=stream)
     return X
+
+
+# ---- A built from keys, decays and write strengths ------------------------
+
+def _kkt_args(k, g, beta, out, cu_seqlens, chunk_indices, stream):
+    import torch
+    assert k.is_contiguous() and g.is_contiguous() and beta.is_contiguous() and out.is_contiguous()
+    assert g.dtype == torch.float32 and beta.dtype == k.dtype
+    lead = k.shape[:-1]
+    K = k.shape[-1]
+    assert g.shape == k.shape and beta.shape == lead and out.shape == lead + (64,)
+    H = k.shape[-2]
+    if cu_seqlens is None:
+        assert k.dim() == 4
+        B, T = k.shape[0], k.shape[1]
+        return (_ptr(k), _ptr(g), _ptr(beta), _dtype_code(k), _ptr(out), _dtype_code(out), B, T, H,
+                K, _stream_ptr(stream))
+    assert k.dim() == 3 and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    nch = 0
+    if chunk_indices is not None:
+        assert chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous()
+        nch = chunk_indices.numel() // 2
+    return (_ptr(k), _ptr(g), _ptr(beta), _dtype_code(k), _ptr(out), _dtype_code(out),
+            _ptr(cu_seqlens), cu_seqlens.numel() - 1, k.shape[0], H, K, _ptr(chunk_indices), nch,
+            _stream_ptr(stream))
+
+
+def kda_kkt_tril_inv(k, g, beta, X, cu_seqlens=None, chunk_indices=None, stream=None) -> None:
+    """X = (I + A)^-1 with A built from keys k [.., H, K], FP32 decays g
+    [.., H, K] and write strengths beta [.., H] (k's dtype); packed with
+    ``cu_seqlens`` ([T, H, *]) or dense ([B, T, H, *]). X [.., H, 64]."""
+    args = _kkt_args(k, g, beta, X, cu_seqlens, chunk_indices, stream)
+    fn = _lib.kda_kkt_tril_inv_dense if cu_seqlens is None else _lib.kda_kkt_tril_inv_packed
+    _check(fn(*args))
+
+
+def kda_kkt(k, g, beta, A, cu_seqlens=None, chunk_indices=None, stream=None) -> None:
+    """The delta-rule matrix A [.., H, 64] itself (same inputs as kda_kkt_tril_inv)."""
+    args = _kkt_args(k, g, beta, A, cu_seqlens, chunk_indices, stream)
+    fn = _lib.kda_kkt_dense if cu_seqlens is None else _lib.kda_kkt_packed
+    _check(fn(*args))
+
+
+def prepare_kkt(k, g, beta, out, cu_seqlens=None, solve=True, stream=None):
+    """Marshalled form of one kda_kkt_tril_inv (solve) or kda_kkt call."""
+    args = _kkt_args(k, g, beta, out, cu_seqlens, None, stream)
+    if cu_seqlens is None:
+        fn = _lib.kda_kkt_tril_inv_dense if solve else _lib.kda_kkt_dense
+    else:
+        fn = _lib.kda_kkt_tril_inv_packed if solve else _lib.kda_kkt_packed
+    return _prepared(fn, args)
+
+
+def kkt_tril_inv(k, g, beta, cu_seqlens=None, out_dtype=None, chunk_indices=None, stream=None):
+    """Convenience form of kda_kkt_tril_inv: allocates X with torch."""
+    import torch
+    X = torch.empty(k.shape[:-1] + (64,), dtype=out_dtype or torch.float32, device=k.device)
+    kda_kkt_tril_inv(k, g, beta, X, cu_seqlens, chunk_indices, stream)
+    return X
+

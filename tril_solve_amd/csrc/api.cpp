@@ -20,6 +20,9 @@ constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 64;
 // Heads: keeps every byte offset inside one chunk's rows (64 rows of H x 64
 // elements) below 2^31, which the kernels' 32-bit buffer offsets rely on.
 constexpr int32_t kMaxHeads = 4096;
+// Key channels of the "build A from keys" path (64 rows x H x K elements of
+// one chunk also stay below 2^31 bytes).
+constexpr int32_t kMaxKeyDim = 256;
 
 bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16 || d == KDA_F16; }
 bool valid_algo(kda_algo a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_FUSED_VALU; }
@@ -153,6 +156,80 @@ kda_status packed_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dt
     return run(p, chosen, (int)a_dtype, (int)x_dtype, stream);
 }
 
+// The "build A from keys" path: k [rows, H, K] and beta [rows, H] of k_dtype,
+// g [rows, H, K] FP32, out [rows, H, 64] of x_dtype.
+kda_status check_kkt(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                     const void *out, kda_dtype x_dtype, int64_t rows, int32_t H, int32_t K) {
+    if (!valid_dtype(k_dtype) || !valid_dtype(x_dtype) || H <= 0 || K <= 0)
+        return KDA_ERR_INVALID_ARG;
+    if (rows > kMaxTokens || H > kMaxHeads) return KDA_ERR_UNSUPPORTED;
+    if (K % 16 != 0 || K > kMaxKeyDim) return KDA_ERR_UNSUPPORTED;
+    if (rows == 0) return KDA_OK;
+    if (!k || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    const size_t eb = dtype_bytes(k_dtype);
+    if (!aligned16(k) || !aligned16(g) || !aligned16(out) || ((uintptr_t)beta % eb) != 0)
+        return KDA_ERR_INVALID_ARG;
+    const size_t nk = (size_t)rows * (size_t)H * (size_t)K;
+    const size_t no = (size_t)rows * (size_t)H * 64 * dtype_bytes(x_dtype);
+    if (overlap(out, no, k, nk * eb) || overlap(out, no, g, nk * 4) ||
+        overlap(out, no, beta, (size_t)rows * (size_t)H * eb))
+        return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+kda_status kkt_call(const void *k, const float *g, const void *beta, kda_dtype k_dtype, void *out,
+                    kda_dtype x_dtype, const int32_t *cu_seqlens, int64_t num_seqs,
+                    int64_t rows, int64_t dense_T, int32_t H, int32_t K,
+                    const int32_t *chunk_indices, int64_t num_chunks, bool solve,
+                    hipStream_t stream) {
+    kda_status st = check_kkt(k, g, beta, k_dtype, out, x_dtype, rows, H, K);
+    if (st != KDA_OK || rows == 0 || num_seqs == 0) return st;
+    int64_t slots;
+    if (dense_T >= 0) {
+        slots = num_seqs * ((dense_T + 63) / 64);
+    } else {
+        if (cu_seqlens == nullptr) return KDA_ERR_INVALID_ARG;
+        slots = chunk_slots(rows, num_seqs, num_chunks, 64);
+    }
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    KktProblem q;
+    memset(&q, 0, sizeof(q));
+    q.p.X = out;
+    q.p.cu = dense_T >= 0 ? nullptr : cu_seqlens;
+    q.p.cmap = dense_T >= 0 ? nullptr : chunk_indices;
+    q.p.num_seqs = (int32_t)num_seqs;
+    q.p.seq_len = dense_T >= 0 ? (int32_t)dense_T : 0;
+    q.p.total_tokens = (int32_t)rows;
+    q.p.heads = H;
+    q.p.slots = (int32_t)slots;
+    q.k = k;
+    q.g = g;
+    q.beta = beta;
+    q.K = K;
+    return launch_kkt(q, solve, (int)k_dtype, (int)x_dtype, stream) == hipSuccess ? KDA_OK
+                                                                                 : KDA_ERR_HIP;
+}
+
+kda_status kkt_packed(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                      void *out, kda_dtype x_dtype, const int32_t *cu_seqlens, int64_t num_seqs,
+                      int64_t total_tokens, int32_t H, int32_t K, const int32_t *chunk_indices,
+                      int64_t num_chunks, bool solve, hipStream_t stream) {
+    if (num_seqs < 0 || total_tokens < 0 || num_chunks < 0) return KDA_ERR_INVALID_ARG;
+    if ((chunk_indices == nullptr) != (num_chunks == 0)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs > kMaxTokens || num_chunks > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    return kkt_call(k, g, beta, k_dtype, out, x_dtype, cu_seqlens, num_seqs, total_tokens, -1, H,
+                    K, chunk_indices, num_chunks, solve, stream);
+}
+
+kda_status kkt_dense(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                     void *out, kda_dtype x_dtype, int64_t B, int64_t T, int32_t H, int32_t K,
+                     bool solve, hipStream_t stream) {
+    if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+    if (B > 0 && T > kMaxTokens / B) return KDA_ERR_UNSUPPORTED;
+    return kkt_call(k, g, beta, k_dtype, out, x_dtype, nullptr, B, B * T, T, H, K, nullptr, 0,
+                    solve, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +310,37 @@ kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
     return packed_call(A, a_dtype, X, x_dtype, cu_seqlens, num_seqs, total_tokens, H,
                        chunk_size, chunk_indices, num_chunks, workspace, workspace_bytes, algo,
                        stream);
+}
+
+kda_status kda_kkt_tril_inv_packed(const void *k, const float *g, const void *beta,
+                                   kda_dtype k_dtype, void *X, kda_dtype x_dtype,
+                                   const int32_t *cu_seqlens, int64_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t K,
+                                   const int32_t *chunk_indices, int64_t num_chunks,
+                                   hipStream_t stream) {
+    return kkt_packed(k, g, beta, k_dtype, X, x_dtype, cu_seqlens, num_seqs, total_tokens, H, K,
+                      chunk_indices, num_chunks, true, stream);
+}
+
+kda_status kda_kkt_tril_inv_dense(const void *k, const float *g, const void *beta,
+                                  kda_dtype k_dtype, void *X, kda_dtype x_dtype, int64_t B,
+                                  int64_t T, int32_t H, int32_t K, hipStream_t stream) {
+    return kkt_dense(k, g, beta, k_dtype, X, x_dtype, B, T, H, K, true, stream);
+}
+
+kda_status kda_kkt_packed(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                          void *A, kda_dtype a_dtype, const int32_t *cu_seqlens,
+                          int64_t num_seqs, int64_t total_tokens, int32_t H, int32_t K,
+                          const int32_t *chunk_indices, int64_t num_chunks,
+                          hipStream_t stream) {
+    return kkt_packed(k, g, beta, k_dtype, A, a_dtype, cu_seqlens, num_seqs, total_tokens, H, K,
+                      chunk_indices, num_chunks, false, stream);
+}
+
+kda_status kda_kkt_dense(const void *k, const float *g, const void *beta, kda_dtype k_dtype,
+                         void *A, kda_dtype a_dtype, int64_t B, int64_t T, int32_t H, int32_t K,
+                         hipStream_t stream) {
+    return kkt_dense(k, g, beta, k_dtype, A, a_dtype, B, T, H, K, false, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,17 @@ struct Problem {
     int32_t slots;         // chunk slots in the grid (>= number of chunks)
 };
 
+// The fused "build A, then invert" path: A is formed from keys, cumulative
+// log-decays and write strengths instead of being read (p.A unused; p.X is X,
+// or A itself when only the matrix is wanted).
+struct KktProblem {
+    Problem p;
+    const void *k;     // [rows, H, K], element type k_dt
+    const float *g;    // [rows, H, K], FP32
+    const void *beta;  // [rows, H], element type k_dt
+    int32_t K;         // channels, a multiple of 16
+};
+
 constexpr int kFusedWaves = 4;  // independent wavefronts per workgroup
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
@@ -35,6 +46,8 @@ hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream
 hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 // Chunks of 16 or 32 tokens (A and X rows of `chunk` elements).
 hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream);
+// A from keys, decays and write strengths; inverted (solve) or stored.
+hipError_t launch_kkt(const KktProblem &q, bool solve, int k_dt, int x_dt, hipStream_t stream);
 
 // Calls f.template operator()<EI, EO>() for the element types of the codes.
 template <class EF32, class EBF16, class EF16, class F>
