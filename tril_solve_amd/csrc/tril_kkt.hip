@@ -14,17 +14,22 @@
 //
 // One wavefront per chunk-head, grid-stride walk as in the 64-token solver.
 // A is formed as ten 16 x 16 blocks A_IJ (J <= I, blocks of 16 rows), each a
-// K-long contraction on the FP32 matrix cores, K in slices of 16 channels:
+// K-long contraction on the FP32 matrix cores, K in slices of 16 channels.
+// With r_I = 16 I the first row of block I, exp(g_i - g_j) factors as
 //
-//   A_IJ = -diag(beta_I) Q_I Kx_J^T,  Q_I[i][d] = k[i][d] e^{g[i][d] - g[r][d]},
-//                                     Kx_J[j][d] = k[j][d] e^{g[r][d] - g[j][d]},
+//   exp(g_i - g_rI) * exp(g_rI - g_rJ) * exp(g_rJ - g_j)   (i in block I, j in J)
 //
-// with the reference row r = 16 I, the first row of block row I. The
-// factors exp(g_i - g_r) and exp(g_r - g_j) multiply to exp(g_i - g_j); for
-// blocks below the diagonal (j < r <= i) both are at most 1 when the decay
-// does not grow along the chunk, and on the diagonal block the second spans at
-// most 15 tokens of decay, so neither factor overflows for any realistic
-// gate. Each product is computed transposed, D = Kx_J Q_I^T: the MFMA
+// so A_IJ = -diag(beta_I) Q_I (P_J * c_IJ)^T with Q_I = k_I e^{g_I - g_rI},
+// P_J = k_J e^{g_rJ - g_J} and c_IJ = e^{g_rI - g_rJ} per channel (c_II = 1).
+// When the decay does not grow along the chunk, Q and c are at most 1 and P
+// spans at most 15 tokens of decay, so no factor overflows for any realistic
+// gate; exponentials per lane and 16-channel slice drop from 56 (one per
+// block pair and row) to 36: 16 for Q, 16 for P and 4 for the six c_IJ, which
+// depend on the channel only and are spread over the lanes of a 16-lane row
+// and shared by DPP broadcasts. Decays are scaled by log2(e) once so every
+// exponential is a bare v_exp_f32.
+//
+// Each product is computed transposed, D = (P_J c_IJ) Q_I^T: the MFMA
 // accumulator then holds row i of A_IJ, columns 4g..4g+3, in lane (g, i),
 // which is the layout the merge consumes (OPND_A) with no data movement.
 // The diagonal blocks go through LDS once to become the row-per-lane layout
@@ -42,12 +47,68 @@ struct KktViews {
     TileView<EK> beta;
 };
 
-// a * exp(x), with x already the decay difference (a = 0 rows stay 0 by
-// select, so an overflowing factor on a row past the chunk cannot make NaN).
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Four elements as loaded (no conversion), so that a load issued a slice
+// ahead is not waited for at once by its widening; widen4 converts at use.
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+template <class E>
+struct Raw4 {
+    typedef u2 T;  // four 16-bit elements
+    static __device__ __forceinline__ T load(Rsrc r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+};
+template <>
+struct Raw4<F32> {
+    typedef u4 T;
+    static __device__ __forceinline__ T load(Rsrc r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+};
+template <class E>
+__device__ __forceinline__ f4 widen4(typename Raw4<E>::T v);
+template <>
+__device__ __forceinline__ f4 widen4<F32>(u4 v) {
+    return __builtin_bit_cast(f4, v);
+}
+template <>
+__device__ __forceinline__ f4 widen4<BF16>(u2 v) {
+    f4 o;
+    o[0] = bf16_to_f32(v[0] & 0xFFFFu);
+    o[1] = bf16_to_f32(v[0] >> 16);
+    o[2] = bf16_to_f32(v[1] & 0xFFFFu);
+    o[3] = bf16_to_f32(v[1] >> 16);
+    return o;
+}
+template <>
+__device__ __forceinline__ f4 widen4<F16>(u2 v) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 h = __builtin_bit_cast(h4, v);
+    f4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)h[e];  // exact widening
+    return o;
+}
+
+// a * 2^x (x a decay difference already scaled by log2 e); rows past the
+// chunk are 0 by select, so an overflowing factor there cannot make NaN.
 __device__ __forceinline__ f4 scaled(f4 a, f4 x, bool keep) {
     f4 r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r[s] = keep ? a[s] * __expf(x[s]) : 0.0f;
+    for (int s = 0; s < 4; ++s) r[s] = keep ? a[s] * __builtin_amdgcn_exp2f(x[s]) : 0.0f;
+    return r;
+}
+
+// Block pairs I > J get numbers p = 0..5 in the order (1,0), (2,0), (2,1),
+// (3,0), (3,1), (3,2); lane p of every 16-lane row evaluates c for pair p
+// (its four channels), and pair_factor<p> hands it to the whole row.
+template <int P>
+__device__ __forceinline__ f4 pair_factor(const f4 &cv) {
+    f4 r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = row_bcast<P>(cv[s]);
     return r;
 }
 
@@ -83,27 +144,75 @@ __device__ __forceinline__ void build_blocks(const KktViews<EK> &v, int K, int l
     const uint32_t offg = (uint32_t)(n * v.g.rstride + 4 * g4) * F32::kBytes;
     const uint32_t blk_k = (uint32_t)(16 * v.k.rstride) * EK::kBytes;
     const uint32_t blk_g = (uint32_t)(16 * v.g.rstride) * F32::kBytes;
+    // the pair whose c_IJ this lane evaluates (lanes 6..15 of a row repeat
+    // pair 0; nobody reads them)
+    const int pn = n < 6 ? n : 0;
+    const int pI = pn == 0 ? 1 : pn < 3 ? 2 : 3;
+    const int pJ = pn == 0 || pn == 1 || pn == 3 ? 0 : pn == 2 || pn == 4 ? 1 : 2;
+    // software pipeline: the next slice's eight loads are in flight while
+    // this slice is computed
+    typename Raw4<EK>::T kn[4];
+    u4 gn[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        gn[b] = Raw4<F32>::load(rg, offg + b * blk_g);
+        kn[b] = Raw4<EK>::load(rk, offk + b * blk_k);
+    }
 #pragma unroll 1
     for (int d0 = 0; d0 < K; d0 += 16) {
-        f4 kb[4], gb[4];
+        typename Raw4<EK>::T kr[4];
+        u4 gr4[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            kb[b] = load4<EK>(rk, offk + b * blk_k + d0 * EK::kBytes);
-            gb[b] = load4<F32>(rg, offg + b * blk_g + d0 * F32::kBytes);
+            kr[b] = kn[b];
+            gr4[b] = gn[b];
         }
+        if (d0 + 16 < K) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if (16 * I >= len) break;  // uniform: block row I lies past the chunk
-            f4 gref;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) gref[s] = row_bcast<0>(gb[I][s]);
-            const f4 Q = scaled(kb[I], gb[I] - gref, valid[I]);
-#pragma unroll
-            for (int J = 0; J <= I; ++J) {
-                const f4 Kx = scaled(kb[J], gref - gb[J], valid[J]);
-                acc[I][J] = mma_kq(Kx, Q, acc[I][J]);
+            for (int b = 0; b < 4; ++b) {
+                gn[b] = Raw4<F32>::load(rg, offg + b * blk_g + (d0 + 16) * F32::kBytes);
+                kn[b] = Raw4<EK>::load(rk, offk + b * blk_k + (d0 + 16) * EK::kBytes);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        f4 kb[4], gl[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            kb[b] = widen4<EK>(kr[b]);
+            gl[b] = widen4<F32>(gr4[b]) * kLog2e;
+        }
+        // decays of the reference rows (row 0 of each block) in every lane
+        f4 gr[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gr[b][s] = row_bcast<0>(gl[b][s]);
+        // c for this lane's pair, then every pair's c by broadcast
+        f4 cv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float hi = pI == 1 ? gr[1][s] : pI == 2 ? gr[2][s] : gr[3][s];
+            const float lo = pJ == 0 ? gr[0][s] : pJ == 1 ? gr[1][s] : gr[2][s];
+            cv[s] = __builtin_amdgcn_exp2f(hi - lo);
+        }
+        // per block: P (row factors against the block's own first row) and Q
+        // (against it from the other side); the raw loads die here
+        f4 Pb[4], Qb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            Pb[b] = scaled(kb[b], gr[b] - gl[b], valid[b]);
+            Qb[b] = scaled(kb[b], gl[b] - gr[b], valid[b]);
+        }
+        // all ten products, also for blocks past a partial chunk (their P and
+        // Q are zero): no branches in the loop
+#pragma unroll
+        for (int I = 0; I < 4; ++I) acc[I][I] = mma_kq(Pb[I], Qb[I], acc[I][I]);
+        acc[1][0] = mma_kq(Pb[0] * pair_factor<0>(cv), Qb[1], acc[1][0]);
+        acc[2][0] = mma_kq(Pb[0] * pair_factor<1>(cv), Qb[2], acc[2][0]);
+        acc[2][1] = mma_kq(Pb[1] * pair_factor<2>(cv), Qb[2], acc[2][1]);
+        acc[3][0] = mma_kq(Pb[0] * pair_factor<3>(cv), Qb[3], acc[3][0]);
+        acc[3][1] = mma_kq(Pb[1] * pair_factor<4>(cv), Qb[3], acc[3][1]);
+        acc[3][2] = mma_kq(Pb[2] * pair_factor<5>(cv), Qb[3], acc[3][2]);
     }
     // -beta of this lane's row in each block row; strictly-lower mask on the
     // diagonal blocks (column 4g + s < row n), by select
