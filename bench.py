@@ -52,15 +52,16 @@ def dtype_bytes(name: str) -> int:
 
 
 def kernel_of(workload: str):
-    """(kernel name, sources its code comes from) of the kernel a workload
-    times; a counter summary taken on other sources is not used."""
-    if workload in KKT_WORKLOADS:
-        return "tril_kkt", ["tril_device.h", "tril_kkt.hip", "tril_launch.h"]
+    """(kernel name pattern, sources its code comes from) of the kernel a
+    workload times; a counter summary taken on other sources is not used.
+    The pattern is matched against rocprofv3's demangled kernel names."""
+    if workload in KKT_WORKLOADS:  # the fused kernel, not the matrix-only one
+        return r"tril_kkt<.*, true>", ["tril_device.h", "tril_kkt.hip", "tril_launch.h"]
     import synth
     C = synth.CONFIGS[workload].get("chunk", 64)
     if C == 64:
-        return "tril_inv_fused_mfma", ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
-    return f"tril_inv_c{C}", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
+        return r"tril_inv_fused_mfma<", ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
+    return rf"tril_inv_c{C}<", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
 
 
 def copy_bytes_of(workload: str) -> int:
@@ -125,12 +126,15 @@ def load_traffic(workload: str):
 
 def _counter_mean(csv_path: str, kernel: str, counter: str) -> tuple[float, int]:
     """Mean value of `counter` (KiB per dispatch) over the dispatches of the
-    kernel whose name contains `kernel`, from a rocprofv3 counter CSV."""
+    kernels whose name matches the pattern `kernel`, from a rocprofv3 counter
+    CSV."""
     import csv
+    import re
+    pat = re.compile(kernel)
     vals = []
     with open(csv_path, newline="") as f:
         for row in csv.DictReader(f):
-            if kernel in row["Kernel_Name"] and row["Counter_Name"] == counter:
+            if pat.search(row["Kernel_Name"]) and row["Counter_Name"] == counter:
                 vals.append(float(row["Counter_Value"]))
     if not vals:
         raise SystemExit(f"{csv_path}: no {counter} rows for {kernel}")
@@ -143,8 +147,8 @@ def record_traffic(workload: str, csvs, out_path: str) -> dict:
     probe moving a known byte count each way."""
     fetch_csv, write_csv, copy_fetch_csv, copy_write_csv = csvs
     k = kernel_of(workload)[0]
-    fetch, nf = _counter_mean(fetch_csv, k + "<", "FETCH_SIZE")
-    write, nw = _counter_mean(write_csv, k + "<", "WRITE_SIZE")
+    fetch, nf = _counter_mean(fetch_csv, k, "FETCH_SIZE")
+    write, nw = _counter_mean(write_csv, k, "WRITE_SIZE")
     cfetch, _ = _counter_mean(copy_fetch_csv, COPY_KERNEL, "FETCH_SIZE")
     cwrite, _ = _counter_mean(copy_write_csv, COPY_KERNEL, "WRITE_SIZE")
     known = copy_bytes_of(workload) / 1024.0

@@ -92,12 +92,11 @@ __device__ __forceinline__ f4 widen4<F16>(u2 v) {
     return o;
 }
 
-// a * 2^x (x a decay difference already scaled by log2 e); rows past the
-// chunk are 0 by select, so an overflowing factor there cannot make NaN.
-__device__ __forceinline__ f4 scaled(f4 a, f4 x, bool keep) {
+// a * 2^x (x a decay difference already scaled by log2 e).
+__device__ __forceinline__ f4 scaled(f4 a, f4 x) {
     f4 r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r[s] = keep ? a[s] * __builtin_amdgcn_exp2f(x[s]) : 0.0f;
+    for (int s = 0; s < 4; ++s) r[s] = a[s] * __builtin_amdgcn_exp2f(x[s]);
     return r;
 }
 
@@ -122,6 +121,108 @@ __device__ __forceinline__ f4 mma_kq(f4 Kx, f4 Q, f4 acc) {
     return acc;
 }
 
+// One 32-channel slice of the keys and decays of a chunk-head as loaded:
+// lane (g, n) holds row n of each 16-row block, channels 8g..8g+7 of the
+// slice, so the four lanes of a row cover 128 contiguous bytes of the FP32
+// decays (one whole cache line) and 64 or 128 bytes of the keys. Lines are
+// then used up within one iteration instead of being fetched again from HBM
+// by a later one (rows lie H x K elements apart, so a partly used line
+// rarely survives in L2 until the next slice). It is consumed as two
+// 16-channel sub-slices t = 0, 1 of channels 8g + 4t + s (s = 0..3).
+template <class EK>
+struct Slice {
+    typename Raw4<EK>::T k[4][2];
+    u4 g[4][2];
+};
+
+// Where a lane's loads go: one descriptor per tensor over all rows of the
+// chunk-head (few SGPRs), block b's rows 16 b rows further in the offset.
+template <class EK>
+struct SliceSrc {
+    Rsrc rk, rg;
+    uint32_t offk, blk_k;
+    uint32_t offgb[4];
+    bool upper;  // this lane holds channels 16..31 of a slice (g >= 2)
+
+    // Loads the slice at channel d0. With `half` (K % 32 = 16: only 16
+    // channels are left) the lanes of channels 16..31 read 0 keys and, so
+    // that their factors stay finite, the decays 16 channels lower.
+    __device__ __forceinline__ void load(Slice<EK> &s, int d0, bool half) const {
+        const bool off = half && upper;
+        const uint32_t kmask = off ? kOffMasked : 0u;
+        const uint32_t gback = off ? 16u * F32::kBytes : 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                s.g[b][t] = Raw4<F32>::load(rg, offgb[b] + (d0 + 4 * t) * F32::kBytes - gback);
+                s.k[b][t] =
+                    Raw4<EK>::load(rk, (offk + b * blk_k + (d0 + 4 * t) * EK::kBytes) | kmask);
+            }
+    }
+};
+
+// Adds one 16-channel sub-slice to the ten blocks. Block by block: P_b is
+// kept for the blocks below it, Q_b is used at once, so few factors are live
+// together.
+template <class EK>
+__device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[4],
+                                               const u4 (&graw)[4], int pI, int pJ,
+                                               f4 (&acc)[4][4]) {
+    f4 gl[4], gr[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        gl[b] = widen4<F32>(graw[b]) * kLog2e;
+        // decay of the block's reference row (its row 0) in every lane
+#pragma unroll
+        for (int s = 0; s < 4; ++s) gr[b][s] = row_bcast<0>(gl[b][s]);
+    }
+    // c for this lane's pair; every pair's c reaches the row by broadcast
+    f4 cv;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const float hi = pI == 1 ? gr[1][s] : pI == 2 ? gr[2][s] : gr[3][s];
+        const float lo = pJ == 0 ? gr[0][s] : pJ == 1 ? gr[1][s] : gr[2][s];
+        cv[s] = __builtin_amdgcn_exp2f(hi - lo);
+    }
+    f4 P[4];
+    // all ten products, also for blocks past a partial chunk (their P and Q
+    // are zero): no branches
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const f4 kb = widen4<EK>(kr[b]);
+        P[b] = scaled(kb, gr[b] - gl[b]);
+        const f4 Q = scaled(kb, gl[b] - gr[b]);
+        acc[b][b] = mma_kq(P[b], Q, acc[b][b]);
+        if (b == 1) acc[1][0] = mma_kq(P[0] * pair_factor<0>(cv), Q, acc[1][0]);
+        if (b == 2) {
+            acc[2][0] = mma_kq(P[0] * pair_factor<1>(cv), Q, acc[2][0]);
+            acc[2][1] = mma_kq(P[1] * pair_factor<2>(cv), Q, acc[2][1]);
+        }
+        if (b == 3) {
+            acc[3][0] = mma_kq(P[0] * pair_factor<3>(cv), Q, acc[3][0]);
+            acc[3][1] = mma_kq(P[1] * pair_factor<4>(cv), Q, acc[3][1]);
+            acc[3][2] = mma_kq(P[2] * pair_factor<5>(cv), Q, acc[3][2]);
+        }
+    }
+}
+
+template <class EK>
+__device__ __forceinline__ void accumulate_slice(const Slice<EK> &sl, int pI, int pJ,
+                                                 f4 (&acc)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        typename Raw4<EK>::T kr[4];
+        u4 graw[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            kr[b] = sl.k[b][t];
+            graw[b] = sl.g[b][t];
+        }
+        accumulate_sub<EK>(kr, graw, pI, pJ, acc);
+    }
+}
+
 // The ten blocks A_IJ (J <= I) of one chunk-head in OPND_A layout: row n of
 // block row I in lane (g, n), columns 16J + 4g..+3. Entries on and above the
 // diagonal are exact zeros; rows past the chunk are zero.
@@ -134,85 +235,34 @@ __device__ __forceinline__ void build_blocks(const KktViews<EK> &v, int K, int l
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int J = 0; J < 4; ++J) acc[I][J] = z;
-    bool valid[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) valid[b] = 16 * b + n < len;
-    // one descriptor per tensor over all rows of the chunk-head (few SGPRs);
-    // block b's rows are 16 b rows further in the per-lane offset
-    const Rsrc rk = v.k.rows_from(0), rg = v.g.rows_from(0);
-    const uint32_t offk = (uint32_t)(n * v.k.rstride + 4 * g4) * EK::kBytes;
-    const uint32_t offg = (uint32_t)(n * v.g.rstride + 4 * g4) * F32::kBytes;
-    const uint32_t blk_k = (uint32_t)(16 * v.k.rstride) * EK::kBytes;
+    SliceSrc<EK> src;
+    src.rk = v.k.rows_from(0);
+    src.rg = v.g.rows_from(0);
+    src.offk = (uint32_t)(n * v.k.rstride + 8 * g4) * EK::kBytes;
+    src.blk_k = (uint32_t)(16 * v.k.rstride) * EK::kBytes;
+    src.upper = g4 >= 2;
+    const uint32_t offg = (uint32_t)(n * v.g.rstride + 8 * g4) * F32::kBytes;
     const uint32_t blk_g = (uint32_t)(16 * v.g.rstride) * F32::kBytes;
+    // Rows past a partial chunk read 0 keys (out of the descriptor's range)
+    // and, instead of their own decays, those of their block's first row:
+    // their factors are then 0 * 2^0 = 0 with no select, whatever the
+    // decays' magnitude (a block wholly past the chunk reads 0 for both).
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        src.offgb[b] = (16 * b + n < len ? offg : (uint32_t)(8 * g4) * F32::kBytes) + b * blk_g;
     // the pair whose c_IJ this lane evaluates (lanes 6..15 of a row repeat
     // pair 0; nobody reads them)
     const int pn = n < 6 ? n : 0;
     const int pI = pn == 0 ? 1 : pn < 3 ? 2 : 3;
     const int pJ = pn == 0 || pn == 1 || pn == 3 ? 0 : pn == 2 || pn == 4 ? 1 : 2;
-    // software pipeline: the next slice's eight loads are in flight while
-    // this slice is computed
-    typename Raw4<EK>::T kn[4];
-    u4 gn[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        gn[b] = Raw4<F32>::load(rg, offg + b * blk_g);
-        kn[b] = Raw4<EK>::load(rk, offk + b * blk_k);
-    }
+    // Each iteration issues all loads of a 32-channel slice (whole lines)
+    // before any use; other wavefronts cover their latency.
 #pragma unroll 1
-    for (int d0 = 0; d0 < K; d0 += 16) {
-        typename Raw4<EK>::T kr[4];
-        u4 gr4[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            kr[b] = kn[b];
-            gr4[b] = gn[b];
-        }
-        if (d0 + 16 < K) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                gn[b] = Raw4<F32>::load(rg, offg + b * blk_g + (d0 + 16) * F32::kBytes);
-                kn[b] = Raw4<EK>::load(rk, offk + b * blk_k + (d0 + 16) * EK::kBytes);
-            }
-        }
+    for (int d0 = 0; d0 < K; d0 += 32) {
+        Slice<EK> sl;
+        src.load(sl, d0, d0 + 32 > K);
         __builtin_amdgcn_sched_barrier(0);
-        f4 kb[4], gl[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            kb[b] = widen4<EK>(kr[b]);
-            gl[b] = widen4<F32>(gr4[b]) * kLog2e;
-        }
-        // decays of the reference rows (row 0 of each block) in every lane
-        f4 gr[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) gr[b][s] = row_bcast<0>(gl[b][s]);
-        // c for this lane's pair, then every pair's c by broadcast
-        f4 cv;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float hi = pI == 1 ? gr[1][s] : pI == 2 ? gr[2][s] : gr[3][s];
-            const float lo = pJ == 0 ? gr[0][s] : pJ == 1 ? gr[1][s] : gr[2][s];
-            cv[s] = __builtin_amdgcn_exp2f(hi - lo);
-        }
-        // per block: P (row factors against the block's own first row) and Q
-        // (against it from the other side); the raw loads die here
-        f4 Pb[4], Qb[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            Pb[b] = scaled(kb[b], gr[b] - gl[b], valid[b]);
-            Qb[b] = scaled(kb[b], gl[b] - gr[b], valid[b]);
-        }
-        // all ten products, also for blocks past a partial chunk (their P and
-        // Q are zero): no branches in the loop
-#pragma unroll
-        for (int I = 0; I < 4; ++I) acc[I][I] = mma_kq(Pb[I], Qb[I], acc[I][I]);
-        acc[1][0] = mma_kq(Pb[0] * pair_factor<0>(cv), Qb[1], acc[1][0]);
-        acc[2][0] = mma_kq(Pb[0] * pair_factor<1>(cv), Qb[2], acc[2][0]);
-        acc[2][1] = mma_kq(Pb[1] * pair_factor<2>(cv), Qb[2], acc[2][1]);
-        acc[3][0] = mma_kq(Pb[0] * pair_factor<3>(cv), Qb[3], acc[3][0]);
-        acc[3][1] = mma_kq(Pb[1] * pair_factor<4>(cv), Qb[3], acc[3][1]);
-        acc[3][2] = mma_kq(Pb[2] * pair_factor<5>(cv), Qb[3], acc[3][2]);
+        accumulate_slice<EK>(sl, pI, pJ, acc);
     }
     // -beta of this lane's row in each block row; strictly-lower mask on the
     // diagonal blocks (column 4g + s < row n), by select
