@@ -184,11 +184,13 @@ kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
  * strengths instead of A:
  *   k      [rows, H, K] of k_dtype: key rows, K channels; K a multiple of 16,
  *          16 <= K <= 256 (other K: KDA_ERR_UNSUPPORTED).
- *   g      [rows, H, K] FP32: cumulative log-decay of each channel (only
- *          differences within a chunk enter; the kernels evaluate
- *          exp(g_i - g_r) exp(g_r - g_j) with r the first row of i's 16-row
- *          block, so g should not increase along a chunk by more than ~80
- *          within 16 tokens, as cumulative sums of log-gates <= 0 never do).
+ *   g      [rows, H, K] FP32: cumulative log-decay of each channel. Only
+ *          differences within a chunk enter, evaluated in FP32 as
+ *          exp(g_i - g_ri) exp(g_ri - g_rj) exp(g_rj - g_j) with r_i, r_j the
+ *          first rows of the 16-row blocks of i and j. No factor overflows
+ *          while g does not rise by more than ~88 anywhere in a chunk and does
+ *          not fall by more than ~88 within 16 consecutive tokens (true of
+ *          cumulative sums of log-gates <= 0 that stay above -5.5 per token).
  *   beta   [rows, H] of k_dtype: write strengths.
  * rows = total_tokens (packed, with cu_seqlens and optional chunk_indices as
  * for kda_tril_inv_packed) or B * T (dense, [B, T, H, ...]). k, g and the
