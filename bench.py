@@ -508,8 +508,9 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        log("bench.py: this solver is measured on one GPU only; a multi-GPU run would shard "
-            "chunk-heads with no communication and is not part of this build.")
+        log("bench.py: this solver is measured on one GPU only (--gpus 1). Every chunk-head "
+            "is independent, so a multi-GPU run would shard heads or chunks with no "
+            "communication; that is not implemented.")
         return 2
 
     import numpy as np

@@ -215,7 +215,7 @@ def _ptr(a):
 
 
 def _pins_fail(lib):
-    """True when at least one pin rejects this build."""
+    """True when at least one pin rejects this compiled variant."""
     def inv(M):
         M = np.ascontiguousarray(M, np.float64)
         L = M.shape[0]
