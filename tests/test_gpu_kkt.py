@@ -194,3 +194,33 @@ def test_full_workload_sampled(kt):
                                          d["k_dtype"])
         e = gh.excess(got[sl], ref, "f32")
         assert e <= 0, f"chunk {c}: exceeds tolerance by {e:.3g}"
+
+
+def test_bench_launch_configuration(kt):
+    """Prepared build-A calls over two rotating buffer sets, issued back to
+    back with no synchronisation, as the benchmark times them; each set's X
+    checked on sampled chunks against the oracle."""
+    name = "packed_16x512_h64_k128_kkt_bf16_f32"
+    cfg = dict(synth.KKT_CONFIGS[name])
+    sets = []
+    for i in range(2):
+        c = dict(cfg)
+        c["seed"] = cfg["seed"] + 100 * i
+        d = synth.make_kkt(c)
+        kd, gd, bd = _dev(d["k"], d["g"], d["beta"], d["k_dtype"])
+        X = torch.empty((d["T_total"], d["H"], 64), device=DEV)
+        sets.append((d, kd, gd, bd, X))
+    cu = torch.from_numpy(sets[0][0]["cu_seqlens"]).to(DEV)
+    calls = [kt.prepare_kkt(kd, gd, bd, X, cu) for _, kd, gd, bd, X in sets]
+    for i in range(6):
+        calls[i % 2]()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for d, _, _, _, X in sets:
+        got = gh.to_numpy_f64(X)
+        for c in rng.choice(d["T_total"] // 64, 6, replace=False):
+            sl = slice(64 * int(c), 64 * int(c) + 64)
+            ref = oracle.kkt_tril_inv_packed(d["k"][sl], d["g"][sl], d["beta"][sl], [0, 64],
+                                             d["k_dtype"])
+            e = gh.excess(got[sl], ref, "f32")
+            assert e <= 0, f"seed {d['seed']} chunk {c}: exceeds tolerance by {e:.3g}"

@@ -445,3 +445,29 @@ def test_graph_capture_replay(kt, algo):
         ref = kt.tril_inv(A, cu, algo=algo)
         torch.cuda.synchronize()
         assert torch.equal(X, ref), i
+
+
+@pytest.mark.parametrize("name", ["packed_16x512_h64_f32", "packed_ragged48_h64_f32_bf16"])
+def test_bench_launch_configuration(kt, name):
+    """The launch pattern the benchmark times: calls prepared once per buffer
+    set and issued back to back on one stream over rotating sets, with no
+    synchronisation in between. Every set's X must still match the oracle."""
+    print(f"\n[bench-config] {name}", flush=True)
+    cfg = dict(synth.CONFIGS[name])
+    sets = []
+    for i in range(3):
+        c = dict(cfg)
+        c["seed"] = cfg["seed"] + 100 * i
+        d = synth.make(c)
+        A = gh.to_torch_input(d["A"], d["a_dtype"], DEV)
+        X = torch.empty(A.shape, dtype=gh.out_torch_dtype(d["x_dtype"]), device=DEV)
+        sets.append((d, A, X))
+    cu = torch.from_numpy(sets[0][0]["cu_seqlens"]).to(DEV)
+    calls = [kt.prepare_packed(A, X, cu, algo="auto") for _, A, X in sets]
+    for i in range(9):
+        calls[i % 3]()
+    torch.cuda.synchronize()
+    for d, _, X in sets:
+        ref = oracle.tril_inv_packed(d["A"], d["cu_seqlens"], d["a_dtype"])
+        e = gh.excess(gh.to_numpy_f64(X), ref, d["x_dtype"])
+        assert e <= 0, f"seed {d['seed']}: exceeds tolerance by {e:.3g}"
