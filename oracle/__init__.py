@@ -14,6 +14,9 @@ For the fused path that first builds A from keys, cumulative log-decays and
 write strengths, ``kkt_*`` evaluate A from its definition in float64 and
 ``kkt_tril_inv_*`` invert that A without rounding it.
 
+``kda_decode`` is one step of the fused KDA decode core (causal convolution
+with its state, the KDA recurrent update, gated RMSNorm) from its definition.
+
 Pins (each in ``tests/test_oracle_pins.py``): exact rational Neumann series,
 the single-subdiagonal closed form, LAPACK inversion, the residual of
 (I + A) X = I, the leading-principal-block property for partial chunks,
@@ -68,6 +71,9 @@ def _load():
         lib.oracle_kkt_packed.argtypes = [p, p, p, p, p, i64, i64, i32, ci, ci]
         lib.oracle_kkt_dense.restype = i64
         lib.oracle_kkt_dense.argtypes = [p, p, p, p, i64, i64, i32, ci, ci]
+        lib.oracle_kda_decode.restype = ctypes.c_int
+        lib.oracle_kda_decode.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i32, ci, ci,
+                                          ctypes.c_double, ctypes.c_double]
         lib.oracle_rne_bf16.restype = None
         lib.oracle_rne_bf16.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -203,6 +209,36 @@ def kkt_tril_inv_packed(k, g, beta, cu_seqlens, k_dtype: str = "f32",
 def kkt_tril_inv_dense(k, g, beta, k_dtype: str = "f32", nthreads: int = 0) -> np.ndarray:
     A = kkt_dense(k, g, beta, k_dtype, nthreads)
     return tril_inv_dense(A, "f64", nthreads)
+
+
+def kda_decode(qkv, g, beta, z, wn, cw, slot, S, cs, in_dtype: str = "f32",
+               eps_l2: float = 1e-6, eps_norm: float = 1e-6):
+    """One step of the fused KDA decode core in float64 (see
+    ``oracle_kda_decode`` in tril_oracle.c for the definition and layouts).
+
+    qkv [B, 3, H, d] and z [B, H, d] are in ``in_dtype`` (f32 array, or
+    bfloat16 / binary16 bit patterns); g [B, H, d], beta [B, H], wn [d],
+    cw [3, W, H, d], S [slots, H, d, d] and cs [slots, 3, H, W - 1, d] are
+    float32 (or float64); slot [B] int32 (< 0: padding). Returns
+    (out [B, H, d], S_new, cs_new) as float64 arrays; the inputs are not
+    modified."""
+    qkv64 = to_f64(qkv, in_dtype)
+    z64 = to_f64(z, in_dtype)
+    g64, b64, wn64, cw64 = (np.ascontiguousarray(a, dtype=np.float64) for a in (g, beta, wn, cw))
+    S64 = np.array(S, dtype=np.float64, copy=True, order="C")
+    cs64 = np.array(cs, dtype=np.float64, copy=True, order="C")
+    sl = np.ascontiguousarray(slot, dtype=np.int32)
+    B, three, H, d = qkv64.shape
+    W = cw64.shape[1]
+    assert three == 3 and cw64.shape == (3, W, H, d) and cs64.shape[1:] == (3, H, W - 1, d)
+    assert S64.shape[1:] == (H, d, d) and g64.shape == (B, H, d) and b64.shape == (B, H)
+    out = np.zeros((B, H, d), np.float64)
+    r = _load().oracle_kda_decode(_ptr(qkv64), _ptr(g64), _ptr(b64), _ptr(z64), _ptr(wn64),
+                                  _ptr(cw64), _ptr(sl), _ptr(S64), _ptr(cs64), _ptr(out), B, H, d,
+                                  W, eps_l2, eps_norm)
+    if r != 0:
+        raise ValueError("malformed decode problem")
+    return out, S64, cs64
 
 
 def rne_bf16(x: np.ndarray) -> np.ndarray:

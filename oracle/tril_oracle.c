@@ -285,3 +285,99 @@ int64_t oracle_kkt_dense(const double *k, const double *g, const double *beta, d
     }
     return work;
 }
+
+/*
+ * One decode step of the fused KDA decode core (tokenspeed PR #1086,
+ * "perf(kimi3): fuse KDA decode core", PR description: single-token causal
+ * convolution with its state update, the KDA recurrent update and gated
+ * RMSNorm; its test plan names convolution, paged-state, padding and
+ * gated-RMSNorm references). The page gives no formulas; this is the plain
+ * reading of those parts for one new token per sequence, evaluated from the
+ * definitions in double precision:
+ *
+ *   for each projection p in (q, k, v) and channel c of head h:
+ *     y_c = sum_{w < W-1} cw[p][w][c] * cs[p][w][c] + cw[p][W-1][c] * x[p][c]
+ *     (cs: the W-1 previous inputs, oldest first), then cs shifts by one
+ *     and x becomes its newest entry; y_c = silu(y_c) = y_c / (1 + exp(-y_c))
+ *   q = y_q / sqrt(|y_q|^2 + eps_l2) / sqrt(d),  k = y_k / sqrt(|y_k|^2 + eps_l2),
+ *   v = y_v
+ *   S <- diag(exp(g)) S                  (S: d x d, key rows i, value columns j)
+ *   u_j = beta * (v_j - sum_i S[i][j] k_i)
+ *   S[i][j] <- S[i][j] + k_i u_j
+ *   o_j = sum_i S[i][j] q_i
+ *   out_j = o_j / sqrt(mean_j o_j^2 + eps_norm) * wn_j * sigmoid(z_j)
+ *
+ * Layouts (doubles): qkv [B, 3, H, d]; g [B, H, d]; beta [B, H]; z [B, H, d];
+ * wn [d]; cw [3, W, H, d] (tap-major); slot [B] (int32): the state slot of
+ * each batch entry, < 0 for padding; S [slots, H, d, d]; cs [slots, 3, H,
+ * W - 1, d]; out [B, H, d]. Padding entries get out = 0 and touch no state.
+ * S and cs are updated in place. Returns 0, or -1 on bad sizes.
+ */
+int oracle_kda_decode(const double *qkv, const double *g, const double *beta, const double *z,
+                      const double *wn, const double *cw, const int32_t *slot, double *S,
+                      double *cs, double *out, int64_t B, int32_t H, int d, int W,
+                      double eps_l2, double eps_norm) {
+    if (B < 0 || H <= 0 || d <= 0 || d > 256 || W < 2 || W > 8) return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int32_t h = 0; h < H; ++h) {
+            double *o_out = out + (b * H + h) * d;
+            const int32_t s = slot[b];
+            if (s < 0) {
+                for (int j = 0; j < d; ++j) o_out[j] = 0.0;
+                continue;
+            }
+            double y[3][256];
+            for (int p = 0; p < 3; ++p) {
+                double *st = cs + (((int64_t)s * 3 + p) * H + h) * (int64_t)(W - 1) * d;
+                const double *x = qkv + ((b * 3 + p) * H + h) * d;
+                for (int c = 0; c < d; ++c) {
+                    double acc = 0.0;
+                    for (int w = 0; w < W - 1; ++w)
+                        acc += cw[(((int64_t)p * W + w) * H + h) * d + c] * st[(int64_t)w * d + c];
+                    acc += cw[(((int64_t)p * W + (W - 1)) * H + h) * d + c] * x[c];
+                    for (int w = 0; w < W - 2; ++w) st[(int64_t)w * d + c] = st[(int64_t)(w + 1) * d + c];
+                    st[(int64_t)(W - 2) * d + c] = x[c];
+                    y[p][c] = acc / (1.0 + exp(-acc));
+                }
+            }
+            double nq = 0.0, nk = 0.0;
+            for (int c = 0; c < d; ++c) {
+                nq += y[0][c] * y[0][c];
+                nk += y[1][c] * y[1][c];
+            }
+            const double sq = 1.0 / sqrt(nq + eps_l2) / sqrt((double)d);
+            const double sk = 1.0 / sqrt(nk + eps_l2);
+            double q[256], k[256];
+            for (int c = 0; c < d; ++c) {
+                q[c] = y[0][c] * sq;
+                k[c] = y[1][c] * sk;
+            }
+            double *M = S + ((int64_t)s * H + h) * (int64_t)d * d;
+            const double *gg = g + (b * H + h) * d;
+            for (int i = 0; i < d; ++i) {
+                const double a = exp(gg[i]);
+                for (int j = 0; j < d; ++j) M[(int64_t)i * d + j] *= a;
+            }
+            const double bt = beta[b * H + h];
+            double u[256];
+            for (int j = 0; j < d; ++j) {
+                double r = 0.0;
+                for (int i = 0; i < d; ++i) r += M[(int64_t)i * d + j] * k[i];
+                u[j] = bt * (y[2][j] - r);
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) M[(int64_t)i * d + j] += k[i] * u[j];
+            double o[256], ms = 0.0;
+            for (int j = 0; j < d; ++j) {
+                double r = 0.0;
+                for (int i = 0; i < d; ++i) r += M[(int64_t)i * d + j] * q[i];
+                o[j] = r;
+                ms += r * r;
+            }
+            const double rn = 1.0 / sqrt(ms / d + eps_norm);
+            const double *zz = z + (b * H + h) * d;
+            for (int j = 0; j < d; ++j) o_out[j] = o[j] * rn * wn[j] / (1.0 + exp(-zz[j]));
+        }
+    }
+    return 0;
+}

@@ -318,3 +318,175 @@ def kkt_all(kkt):
     checks = {"scalar_key": check_kkt_scalar_key, "uniform_decay": check_kkt_uniform_decay,
               "brute_force": check_kkt_brute_force}
     return [n for n, f in checks.items() if not f(kkt)]
+
+
+# ---- the fused KDA decode step ---------------------------------------------
+#
+# Each check takes ``dec(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2,
+# eps_norm) -> (out, S_new, cs_new)`` on float64 arrays (layouts of
+# oracle.kda_decode).
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def _onehot_conv(H, d, W):
+    """Taps that pass the newest input through: y = x."""
+    cw = np.zeros((3, W, H, d))
+    cw[:, W - 1] = 1.0
+    return cw
+
+
+def check_dec_delta_rule(dec, d=16, W=4):
+    """Zero state, g = 0, beta = 1, q = k: one step stores k v^T (so the
+    output is RMSNorm(v) * wn * sigmoid(z) exactly up to eps), and a second
+    step with the same key and a new value replaces it: S = k v'^T."""
+    rng = np.random.default_rng(11)
+    H = 1
+    cw = _onehot_conv(H, d, W)
+    x = rng.standard_normal((1, 3, H, d))
+    x[:, 0] = x[:, 1]  # q = k
+    z = rng.standard_normal((1, H, d))
+    wn = rng.random(d) + 0.5
+    S = np.zeros((1, H, d, d))
+    cs = np.zeros((1, 3, H, W - 1, d))
+    out, S1, _ = dec(x, np.zeros((1, H, d)), np.ones((1, H)), z, wn, cw,
+                     np.array([0], np.int32), S, cs, 0.0, 0.0)
+    yk, yv = _silu(x[0, 1, 0]), _silu(x[0, 2, 0])
+    k = yk / np.linalg.norm(yk)
+    ok = np.abs(S1[0, 0] - np.outer(k, yv)).max() <= 1e-13
+    want = yv / np.sqrt(np.mean(yv ** 2)) * wn / (1.0 + np.exp(-z[0, 0]))
+    ok &= np.abs(out[0, 0] - want).max() <= 1e-12
+    x2 = x.copy()
+    x2[0, 2] = rng.standard_normal((H, d))
+    _, S2, _ = dec(x2, np.zeros((1, H, d)), np.ones((1, H)), z, wn, cw,
+                   np.array([0], np.int32), S1, np.zeros_like(cs), 0.0, 0.0)
+    ok &= np.abs(S2[0, 0] - np.outer(k, _silu(x2[0, 2, 0]))).max() <= 1e-12
+    return bool(ok)
+
+
+def check_dec_decay_only(dec, d=8, W=4):
+    """beta = 0: the state only decays, S_new = diag(exp(g)) S."""
+    rng = np.random.default_rng(12)
+    H, slots = 2, 2
+    S = rng.standard_normal((slots, H, d, d))
+    g = -rng.random((1, H, d))
+    _, S1, _ = dec(rng.standard_normal((1, 3, H, d)), g, np.zeros((1, H)),
+                   rng.standard_normal((1, H, d)), np.ones(d), rng.standard_normal((3, W, H, d)),
+                   np.array([1], np.int32), S, rng.standard_normal((slots, 3, H, W - 1, d)),
+                   1e-6, 1e-6)
+    want = S.copy()
+    want[1] = np.exp(g[0])[:, :, None] * S[1]
+    return bool(np.abs(S1 - want).max() <= 1e-14)
+
+
+def check_dec_conv_taps(dec, d=8, W=4):
+    """A one-hot tap t picks the t-th oldest input of the window (the new
+    token for t = W - 1), and the window shifts by one: check both through
+    the value path (zero state, q = k, beta = 1, g = 0: the output is the
+    normalised silu of the picked input) and the returned conv state."""
+    rng = np.random.default_rng(13)
+    H = 1
+    ok = True
+    for t in range(W):
+        cw = np.zeros((3, W, H, d))
+        cw[0, W - 1] = cw[1, W - 1] = 1.0
+        cw[2, t] = 1.0
+        x = rng.standard_normal((1, 3, H, d))
+        x[:, 0] = x[:, 1]
+        cs = rng.standard_normal((1, 3, H, W - 1, d))
+        out, _, cs1 = dec(x, np.zeros((1, H, d)), np.ones((1, H)), np.full((1, H, d), 40.0),
+                          np.ones(d), cw, np.array([0], np.int32), np.zeros((1, H, d, d)), cs,
+                          0.0, 0.0)
+        window = np.concatenate([cs[0, 2, 0], x[0, 2]], axis=0)  # oldest first, new last
+        yv = _silu(window[t])
+        ok &= np.abs(out[0, 0] - yv / np.sqrt(np.mean(yv ** 2))).max() <= 1e-12
+        shifted = np.concatenate([cs[0, :, 0, 1:], x[0, :, 0][:, None, :]], axis=1)
+        ok &= np.array_equal(cs1[0, :, 0], shifted)
+    return bool(ok)
+
+
+def check_dec_padding_and_slots(dec, d=8, W=4):
+    """Batch entries map to state slots; a negative slot is padding (output
+    0, no state touched); slots that no entry names are untouched."""
+    rng = np.random.default_rng(14)
+    H, slots = 2, 4
+    S = rng.standard_normal((slots, H, d, d))
+    cs = rng.standard_normal((slots, 3, H, W - 1, d))
+    slot = np.array([3, -1, 0], np.int32)
+    args = (rng.standard_normal((3, 3, H, d)), -rng.random((3, H, d)), rng.random((3, H)),
+            rng.standard_normal((3, H, d)), np.ones(d), rng.standard_normal((3, W, H, d)))
+    out, S1, cs1 = dec(*args, slot, S, cs, 1e-6, 1e-6)
+    ok = np.all(out[1] == 0)
+    ok &= np.array_equal(S1[[1, 2]], S[[1, 2]]) and np.array_equal(cs1[[1, 2]], cs[[1, 2]])
+    ok &= not np.array_equal(S1[3], S[3]) and not np.array_equal(S1[0], S[0])
+    # the same entries alone, each on a fresh copy, give the same result
+    for b, s in ((0, 3), (2, 0)):
+        one = tuple(a[b:b + 1] for a in args[:4]) + args[4:]
+        o1, Sb, _ = dec(*one, np.array([s], np.int32), S, cs, 1e-6, 1e-6)
+        ok &= np.array_equal(o1[0], out[b]) and np.array_equal(Sb[s], S1[s])
+    return bool(ok)
+
+
+def dec_brute_force(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2, eps_norm):
+    """The decode step with Python floats and loops, entry by entry."""
+    import math
+    B, _, H, d = qkv.shape
+    W = cw.shape[1]
+    S = [[[[float(S[s, h, i, j]) for j in range(d)] for i in range(d)] for h in range(H)]
+         for s in range(S.shape[0])]
+    cs = cs.astype(float).tolist()
+    out = [[[0.0] * d for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        s = int(slot[b])
+        if s < 0:
+            continue
+        for h in range(H):
+            y = []
+            for p in range(3):
+                row = []
+                for c in range(d):
+                    win = [cs[s][p][h][w][c] for w in range(W - 1)] + [float(qkv[b, p, h, c])]
+                    acc = sum(float(cw[p, w, h, c]) * win[w] for w in range(W))
+                    for w in range(W - 1):
+                        cs[s][p][h][w][c] = win[w + 1]
+                    row.append(acc / (1.0 + math.exp(-acc)))
+                y.append(row)
+            nq = math.sqrt(sum(t * t for t in y[0]) + eps_l2) * math.sqrt(d)
+            nk = math.sqrt(sum(t * t for t in y[1]) + eps_l2)
+            q = [t / nq for t in y[0]]
+            k = [t / nk for t in y[1]]
+            M = S[s][h]
+            for i in range(d):
+                a = math.exp(float(g[b, h, i]))
+                for j in range(d):
+                    M[i][j] *= a
+            u = [float(beta[b, h]) * (y[2][j] - sum(M[i][j] * k[i] for i in range(d)))
+                 for j in range(d)]
+            for i in range(d):
+                for j in range(d):
+                    M[i][j] += k[i] * u[j]
+            o = [sum(M[i][j] * q[i] for i in range(d)) for j in range(d)]
+            rn = math.sqrt(sum(t * t for t in o) / d + eps_norm)
+            out[b][h] = [o[j] / rn * float(wn[j]) / (1.0 + math.exp(-float(z[b, h, j])))
+                         for j in range(d)]
+    return np.array(out), np.array(S), np.array(cs)
+
+
+def check_dec_brute_force(dec, d=6, W=3):
+    rng = np.random.default_rng(15)
+    B, H, slots = 3, 2, 4
+    args = (rng.standard_normal((B, 3, H, d)), -rng.random((B, H, d)), rng.random((B, H)),
+            rng.standard_normal((B, H, d)), rng.random(d) + 0.5,
+            rng.standard_normal((3, W, H, d)) * 0.5, np.array([2, -1, 0], np.int32),
+            rng.standard_normal((slots, H, d, d)), rng.standard_normal((slots, 3, H, W - 1, d)))
+    got = dec(*args, 1e-6, 1e-3)
+    want = dec_brute_force(*args, 1e-6, 1e-3)
+    return all(np.abs(a - b).max() <= 1e-12 for a, b in zip(got, want))
+
+
+def dec_all(dec):
+    checks = {"delta_rule": check_dec_delta_rule, "decay_only": check_dec_decay_only,
+              "conv_taps": check_dec_conv_taps, "padding_and_slots": check_dec_padding_and_slots,
+              "brute_force": check_dec_brute_force}
+    return [n for n, f in checks.items() if not f(dec)]

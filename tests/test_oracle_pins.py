@@ -178,6 +178,15 @@ _MUTANTS = {
     "kkt_keeps_diagonal": ("for (int j = 0; j < i; ++j) {\n            double s = 0.0;",
                            "for (int j = 0; j <= i; ++j) {\n            double s = 0.0;"),
     "kkt_drops_last_channel": ("for (int d = 0; d < K; ++d)", "for (int d = 0; d < K - 1; ++d)"),
+    # the decode step
+    "dec_conv_window_reversed": ("* st[(int64_t)w * d + c];", "* st[(int64_t)(W - 2 - w) * d + c];"),
+    "dec_no_silu": ("y[p][c] = acc / (1.0 + exp(-acc));", "y[p][c] = acc;"),
+    "dec_no_beta": ("u[j] = bt * (y[2][j] - r);", "u[j] = (y[2][j] - r);"),
+    "dec_decay_sign": ("const double a = exp(gg[i]);", "const double a = exp(-gg[i]);"),
+    "dec_silu_gate": ("wn[j] / (1.0 + exp(-zz[j]));", "wn[j] * zz[j] / (1.0 + exp(-zz[j]));"),
+    "dec_padding_output": ("for (int j = 0; j < d; ++j) o_out[j] = 0.0;",
+                           "for (int j = 0; j < d; ++j) o_out[j] = 1.0;"),
+    "dec_no_q_scale": ("/ sqrt(nq + eps_l2) / sqrt((double)d);", "/ sqrt(nq + eps_l2);"),
 }
 
 
@@ -207,6 +216,9 @@ def _load_lib(c, so):
     lib.oracle_tril_inv_dense.restype = i64
     lib.oracle_kkt_packed.argtypes = [p, p, p, p, p, i64, i64, i32, ci, ci]
     lib.oracle_kkt_packed.restype = i64
+    lib.oracle_kda_decode.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i32, ci, ci,
+                                      ctypes.c_double, ctypes.c_double]
+    lib.oracle_kda_decode.restype = ci
     return lib
 
 
@@ -266,7 +278,21 @@ def _pins_fail(lib):
                               H, K, 1)
         return A
 
-    return bool(pins.kkt_all(kkt))
+    if pins.kkt_all(kkt):
+        return True
+
+    def dec(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2, eps_norm):
+        a = [np.ascontiguousarray(t, np.float64) for t in (qkv, g, beta, z, wn, cw)]
+        S = np.array(S, np.float64, copy=True)
+        cs = np.array(cs, np.float64, copy=True)
+        sl = np.ascontiguousarray(slot, np.int32)
+        B, _, H, d = a[0].shape
+        out = np.zeros((B, H, d))
+        lib.oracle_kda_decode(*[_ptr(t) for t in a], _ptr(sl), _ptr(S), _ptr(cs), _ptr(out), B,
+                              H, d, a[5].shape[1], eps_l2, eps_norm)
+        return out, S, cs
+
+    return bool(pins.dec_all(dec))
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -367,4 +393,30 @@ def test_kkt_dense_equals_packed_and_inverse_composes():
             M = np.tril(Ap[t0:t0 + L, h, :L], -1)
             ref = np.linalg.inv(np.eye(L) + M)
             assert np.abs(X[t0:t0 + L, h, :L] - ref).max() < 1e-12 * max(1.0, np.abs(ref).max())
+
+
+# ---- the fused KDA decode step -----------------------------------------------
+
+def _oracle_dec(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2, eps_norm):
+    return oracle.kda_decode(qkv, g, beta, z, wn, cw, slot, S, cs, "f64", eps_l2, eps_norm)
+
+
+@pytest.mark.parametrize("check", ["check_dec_delta_rule", "check_dec_decay_only",
+                                   "check_dec_conv_taps", "check_dec_padding_and_slots",
+                                   "check_dec_brute_force"])
+def test_decode_step_pins(check):
+    assert getattr(pins, check)(_oracle_dec)
+
+
+def test_decode_inputs_are_not_modified():
+    rng = np.random.default_rng(3)
+    B, H, d, W, slots = 2, 2, 8, 4, 2
+    S = rng.standard_normal((slots, H, d, d))
+    cs = rng.standard_normal((slots, 3, H, W - 1, d))
+    S0, cs0 = S.copy(), cs.copy()
+    oracle.kda_decode(rng.standard_normal((B, 3, H, d)), -rng.random((B, H, d)),
+                      rng.random((B, H)), rng.standard_normal((B, H, d)), np.ones(d),
+                      rng.standard_normal((3, W, H, d)), np.array([1, 0], np.int32), S, cs,
+                      "f64")
+    assert np.array_equal(S, S0) and np.array_equal(cs, cs0)
 
