@@ -226,6 +226,47 @@ kda_status kda_kkt_dense(const void *k, const float *g, const void *beta, kda_dt
                          void *A, kda_dtype a_dtype, int64_t B, int64_t T, int32_t H, int32_t K,
                          hipStream_t stream);
 
+/*
+ * Fused KDA decode core: one decode step (one new token per sequence) of
+ * the causal convolution with its rolling state, the KDA recurrent update and
+ * gated RMSNorm, in one kernel (tokenspeed PR #1086, "perf(kimi3): fuse KDA
+ * decode core", PR description; its test plan names convolution, paged-state,
+ * padding and gated-RMSNorm references). The page gives no formulas; per
+ * sequence b and head h (head dim d = head_dim, conv width W = conv_width)
+ * the step is:
+ *   for p in (q, k, v): y_p = silu(sum_{w<W} conv_w[p][w] * win_p[w]), where
+ *       win_p = (the W-1 previous inputs, oldest first; then the new x_p);
+ *       the window then drops its oldest entry and appends x_p
+ *   q = y_q / sqrt(|y_q|^2 + eps_l2) / sqrt(d),  k = y_k / sqrt(|y_k|^2 + eps_l2),  v = y_v
+ *   S = diag(exp(g)) S;  u = beta * (v - S^T k);  S = S + k u^T;  o = S^T q
+ *   out = o / sqrt(mean(o^2) + eps_norm) * norm_w * sigmoid(z)
+ * with S the d x d FP32 state (key rows, value columns). All arithmetic FP32.
+ *
+ *   qkv         [B, 3, H, d] of in_dtype: the new token's q, k, v before the
+ *               convolution.
+ *   z           [B, H, d] of in_dtype: output gate (before the sigmoid).
+ *   g           [B, H, d] FP32: log-decay of each key channel (<= 0 in KDA).
+ *   beta        [B, H] FP32: write strength.
+ *   norm_w      [d] FP32: RMSNorm weight.
+ *   conv_w      [3, W, H, d] FP32: depthwise taps, tap-major.
+ *   slot        [B] int32 (device): the state slot of each sequence. A slot
+ *               < 0 or >= num_slots marks a padding entry: its output is 0
+ *               and no state is touched. Slots of non-padding entries must
+ *               be distinct (entries sharing a slot race).
+ *   state       [num_slots, H, d, d] FP32, updated in place (16-byte aligned).
+ *   conv_state  [num_slots, 3, H, W - 1, d] FP32, updated in place.
+ *   out         [B, H, d] of out_dtype.
+ * head_dim must be 128 and 2 <= conv_width <= 4 (else KDA_ERR_UNSUPPORTED);
+ * eps_l2, eps_norm must be finite and >= 0. out must not overlap the state
+ * pools. B = 0 is a no-op.
+ */
+kda_status kda_decode_step(const void *qkv, const void *z, kda_dtype in_dtype, const float *g,
+                           const float *beta, const float *norm_w, const float *conv_w,
+                           const int32_t *slot, float *state, float *conv_state,
+                           int64_t num_slots, void *out, kda_dtype out_dtype, int64_t B,
+                           int32_t H, int32_t head_dim, int32_t conv_width, float eps_l2,
+                           float eps_norm, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);
 

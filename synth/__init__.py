@@ -56,6 +56,15 @@ CONFIGS = {
                                          a_dtype="f32", x_dtype="f32", seed=6, chunk=32),
 }
 
+# Workloads of the fused KDA decode core: one decode step for B sequences,
+# H = 32 heads of dim 128, conv width 4, bf16 activations in and out, state
+# pools with 2 B slots (the batch uses a permutation of half of them).
+DECODE_CONFIGS = {
+    f"decode_b{B}_h32_d128_w4_bf16": dict(B=B, H=32, d=128, W=4, slots=2 * B, in_dtype="bf16",
+                                          out_dtype="bf16", seed=20 + B)
+    for B in (2, 4, 8, 16, 32)
+}
+
 # Workloads of the path that builds A from keys k, decays g and write
 # strengths beta: k and beta in k_dtype, g in float32, X in x_dtype.
 KKT_CONFIGS = {
@@ -262,4 +271,34 @@ def make_kkt(name_or_cfg) -> dict:
         out["cu_seqlens"] = cu_seqlens(lengths)
     out["k"], out["g"], out["beta"] = k, g, beta
     return out
+
+
+def decode_inputs(B: int, H: int, d: int = 128, W: int = 4, slots: int | None = None,
+                  seed: int = 0, in_dtype: str = "f32", padding: int = 0) -> dict:
+    """Seeded inputs of one decode step: q, k, v and the gate z ~ N(0, 1)
+    (float32, or bfloat16 / binary16 bit patterns), log-decays
+    g = logsigmoid(N(0, 1) + 3) per key channel, beta = sigmoid(N(0, 1)),
+    RMSNorm weights 1 + N(0, 0.1), conv taps U(-0.5, 0.5), FP32 state pools
+    (S ~ N(0, 0.05), conv windows ~ N(0, 1)), and the slot of each sequence: a
+    random choice of distinct slots, the first ``padding`` entries -1."""
+    rng = np.random.default_rng([seed, 0xDEC])
+    slots = slots or 2 * B
+    qkv = rng.standard_normal((B, 3, H, d)).astype(np.float32)
+    z = rng.standard_normal((B, H, d)).astype(np.float32)
+    if in_dtype == "bf16":
+        qkv, z = to_bf16_bits(qkv), to_bf16_bits(z)
+    elif in_dtype == "f16":
+        qkv, z = to_f16_bits(qkv), to_f16_bits(z)
+    slot = rng.permutation(slots)[:B].astype(np.int32)
+    slot[:padding] = -1
+    return dict(
+        qkv=qkv, z=z,
+        g=(-np.logaddexp(0.0, -(rng.standard_normal((B, H, d)) + 3.0))).astype(np.float32),
+        beta=(1.0 / (1.0 + np.exp(-rng.standard_normal((B, H))))).astype(np.float32),
+        norm_w=(1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32),
+        conv_w=rng.uniform(-0.5, 0.5, (3, W, H, d)).astype(np.float32),
+        slot=slot,
+        state=(0.05 * rng.standard_normal((slots, H, d, d))).astype(np.float32),
+        conv_state=rng.standard_normal((slots, 3, H, W - 1, d)).astype(np.float32),
+        B=B, H=H, d=d, W=W, slots=slots, in_dtype=in_dtype)
 

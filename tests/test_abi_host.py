@@ -241,3 +241,31 @@ def test_kkt_argument_validation(kt):
         assert _kkt_p(kt, T=0, k=None, g=None, beta=None, X=None, cu=None, solve=solve) == kt.KDA_OK
         assert _kkt_d(kt, B=0, solve=solve) == kt.KDA_OK
         assert _kkt_d(kt, T=0, k=None, g=None, beta=None, X=None, solve=solve) == kt.KDA_OK
+
+
+# ---- the fused KDA decode core -----------------------------------------------
+
+def _dec(kt, qkv=0x10000, z=0x20000, ind=0, g=0x30000, beta=0x40000, wn=0x50000, cw=0x60000,
+         slot=0x70000, S=0x1000000, cs=0x80000, ns=4, out=0x90000000, outd=0, B=2, H=2, d=128,
+         W=4, e1=1e-6, e2=1e-6):
+    return kt._lib.kda_decode_step(P(qkv), P(z), ind, P(g), P(beta), P(wn), P(cw), P(slot), P(S),
+                                   P(cs), ns, P(out), outd, B, H, d, W, e1, e2, None)
+
+
+def test_decode_argument_validation(kt):
+    E, U = kt.KDA_ERR_INVALID_ARG, kt.KDA_ERR_UNSUPPORTED
+    assert _dec(kt, d=64) == U
+    assert _dec(kt, W=1) == U and _dec(kt, W=5) == U
+    assert _dec(kt, ind=3) == E and _dec(kt, outd=-1) == E
+    assert _dec(kt, H=0) == E and _dec(kt, B=-1) == E and _dec(kt, ns=-1) == E
+    assert _dec(kt, ns=0) == E
+    assert _dec(kt, e1=-1.0) == E and _dec(kt, e2=float("nan")) == E
+    assert _dec(kt, e2=float("inf")) == E
+    for name in ("qkv", "z", "g", "beta", "wn", "cw", "slot", "S", "cs", "out"):
+        assert _dec(kt, **{name: None}) == E, name
+    assert _dec(kt, S=0x1000008) == E                # state not 16-byte aligned
+    assert _dec(kt, g=0x30002) == E                  # fp32 not 4-byte aligned
+    assert _dec(kt, ind=1, qkv=0x10001) == E         # bf16 not 2-byte aligned
+    assert _dec(kt, out=0x1000000 + 4 * 2 * 128 * 128 * 4 - 64) == E  # out overlaps state
+    assert _dec(kt, B=0) == kt.KDA_OK                # no-op before any pointer is used
+    assert _dec(kt, B=0, qkv=None, out=None) == kt.KDA_OK

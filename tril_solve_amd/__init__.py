@@ -63,10 +63,15 @@ for _n in ("kda_kkt_tril_inv_dense", "kda_kkt_dense"):
     getattr(_lib, _n).argtypes = [_p, _p, _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i32,
                                   _i32, _p]
 
+_lib.kda_decode_step.restype = ctypes.c_int
+_lib.kda_decode_step.argtypes = [_p, _p, ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _i64, _p,
+                                 ctypes.c_int, _i64, _i32, _i32, _i32, ctypes.c_float,
+                                 ctypes.c_float, _p]
+
 EXPORTED = ("kda_tril_inv_workspace_size", "kda_tril_inv_dense", "kda_tril_inv_packed",
             "kda_status_string", "kda_tril_auto_plan", "kda_tril_inv_dense_chunk",
             "kda_tril_inv_packed_chunk", "kda_kkt_tril_inv_packed", "kda_kkt_tril_inv_dense",
-            "kda_kkt_packed", "kda_kkt_dense")
+            "kda_kkt_packed", "kda_kkt_dense", "kda_decode_step")
 CHUNK_SIZES = (16, 32, 64)
 
 
@@ -308,4 +313,40 @@ def kkt_tril_inv(k, g, beta, cu_seqlens=None, out_dtype=None, chunk_indices=None
     X = torch.empty(k.shape[:-1] + (64,), dtype=out_dtype or torch.float32, device=k.device)
     kda_kkt_tril_inv(k, g, beta, X, cu_seqlens, chunk_indices, stream)
     return X
+
+
+# ---- the fused KDA decode core --------------------------------------------
+
+def _decode_args(qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out, eps_l2,
+                 eps_norm, stream):
+    import torch
+    for t in (qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out):
+        assert t.is_contiguous()
+    assert z.dtype == qkv.dtype and slot.dtype == torch.int32
+    for t in (g, beta, norm_w, conv_w, state, conv_state):
+        assert t.dtype == torch.float32
+    B, three, H, d = qkv.shape
+    W = conv_w.shape[1]
+    assert three == 3 and z.shape == (B, H, d) and g.shape == (B, H, d) and beta.shape == (B, H)
+    assert conv_w.shape == (3, W, H, d) and state.shape[1:] == (H, d, d)
+    assert conv_state.shape == (state.shape[0], 3, H, W - 1, d) and out.shape == (B, H, d)
+    return (_ptr(qkv), _ptr(z), _dtype_code(qkv), _ptr(g), _ptr(beta), _ptr(norm_w),
+            _ptr(conv_w), _ptr(slot), _ptr(state), _ptr(conv_state), state.shape[0], _ptr(out),
+            _dtype_code(out), B, H, d, W, float(eps_l2), float(eps_norm), _stream_ptr(stream))
+
+
+def kda_decode_step(qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out,
+                    eps_l2=1e-6, eps_norm=1e-6, stream=None) -> None:
+    """One decode step of the fused KDA decode core (see include/kda_tril.h);
+    state and conv_state are updated in place, out is written."""
+    _check(_lib.kda_decode_step(*_decode_args(qkv, z, g, beta, norm_w, conv_w, slot, state,
+                                              conv_state, out, eps_l2, eps_norm, stream)))
+
+
+def prepare_decode(qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out, eps_l2=1e-6,
+                   eps_norm=1e-6, stream=None):
+    """Marshalled form of one kda_decode_step call."""
+    return _prepared(_lib.kda_decode_step,
+                     _decode_args(qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out,
+                                  eps_l2, eps_norm, stream))
 

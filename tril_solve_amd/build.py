@@ -19,7 +19,7 @@ PROBE_LIB = os.path.join(HERE, "libkda_bench_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "plan.cpp", "launch_common.cpp", "tril_fused.hip", "tril_split.hip",
-           "tril_small.hip", "tril_kkt.hip"]
+           "tril_small.hip", "tril_kkt.hip", "kda_decode.hip"]
 PROBE_SOURCES = ["bench_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -343,4 +343,54 @@ kda_status kda_kkt_dense(const void *k, const float *g, const void *beta, kda_dt
     return kkt_dense(k, g, beta, k_dtype, A, a_dtype, B, T, H, K, false, stream);
 }
 
+kda_status kda_decode_step(const void *qkv, const void *z, kda_dtype in_dtype, const float *g,
+                           const float *beta, const float *norm_w, const float *conv_w,
+                           const int32_t *slot, float *state, float *conv_state,
+                           int64_t num_slots, void *out, kda_dtype out_dtype, int64_t B,
+                           int32_t H, int32_t head_dim, int32_t conv_width, float eps_l2,
+                           float eps_norm, hipStream_t stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
+    if (B < 0 || H <= 0 || num_slots < 0) return KDA_ERR_INVALID_ARG;
+    if (!(eps_l2 >= 0.0f) || !(eps_norm >= 0.0f) || eps_l2 > 1e30f || eps_norm > 1e30f)
+        return KDA_ERR_INVALID_ARG;  // negative, NaN or infinite
+    if (head_dim != 128 || conv_width < 2 || conv_width > 4) return KDA_ERR_UNSUPPORTED;
+    if (B > INT32_MAX / H || num_slots > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (num_slots == 0) return KDA_ERR_INVALID_ARG;
+    if (!qkv || !z || !g || !beta || !norm_w || !conv_w || !slot || !state || !conv_state || !out)
+        return KDA_ERR_INVALID_ARG;
+    const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    if (!aligned16(state) || ((uintptr_t)conv_state & 3u) || ((uintptr_t)g & 3u) ||
+        ((uintptr_t)beta & 3u) || ((uintptr_t)norm_w & 3u) || ((uintptr_t)conv_w & 3u) ||
+        ((uintptr_t)slot & 3u) || ((uintptr_t)qkv % ib) || ((uintptr_t)z % ib) ||
+        ((uintptr_t)out % ob))
+        return KDA_ERR_INVALID_ARG;
+    const size_t n_state = (size_t)num_slots * (size_t)H * 128 * 128 * 4;
+    const size_t n_conv = (size_t)num_slots * 3 * (size_t)H * (size_t)(conv_width - 1) * 128 * 4;
+    const size_t n_out = (size_t)B * (size_t)H * 128 * ob;
+    if (overlap(out, n_out, state, n_state) || overlap(out, n_out, conv_state, n_conv) ||
+        overlap(state, n_state, conv_state, n_conv))
+        return KDA_ERR_INVALID_ARG;
+    DecodeProblem p;
+    memset(&p, 0, sizeof(p));
+    p.qkv = qkv;
+    p.z = z;
+    p.g = g;
+    p.beta = beta;
+    p.norm_w = norm_w;
+    p.conv_w = conv_w;
+    p.slot = slot;
+    p.state = state;
+    p.conv_state = conv_state;
+    p.out = out;
+    p.B = (int32_t)B;
+    p.H = H;
+    p.W = conv_width;
+    p.num_slots = (int32_t)num_slots;
+    p.eps_l2 = eps_l2;
+    p.eps_norm = eps_norm;
+    return launch_decode(p, (int)in_dtype, (int)out_dtype, stream) == hipSuccess ? KDA_OK
+                                                                               : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -33,6 +33,23 @@ struct KktProblem {
     int32_t K;         // channels, a multiple of 16
 };
 
+// One step of the fused KDA decode core (head dim 128), layouts as in the
+// C ABI's kda_decode_step.
+struct DecodeProblem {
+    const void *qkv;       // [B, 3, H, 128], element type in_dt
+    const void *z;         // [B, H, 128], element type in_dt
+    const float *g;        // [B, H, 128]
+    const float *beta;     // [B, H]
+    const float *norm_w;   // [128]
+    const float *conv_w;   // [3, W, H, 128]
+    const int32_t *slot;   // [B]
+    float *state;          // [num_slots, H, 128, 128]
+    float *conv_state;     // [num_slots, 3, H, W - 1, 128]
+    void *out;             // [B, H, 128], element type out_dt
+    int32_t B, H, W, num_slots;
+    float eps_l2, eps_norm;
+};
+
 constexpr int kFusedWaves = 4;  // independent wavefronts per workgroup
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
@@ -48,6 +65,8 @@ hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t s
 hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream);
 // A from keys, decays and write strengths; inverted (solve) or stored.
 hipError_t launch_kkt(const KktProblem &q, bool solve, int k_dt, int x_dt, hipStream_t stream);
+// One decode step of the fused KDA decode core.
+hipError_t launch_decode(const DecodeProblem &p, int in_dt, int out_dt, hipStream_t stream);
 
 // Calls f.template operator()<EI, EO>() for the element types of the codes.
 template <class EF32, class EBF16, class EF16, class F>
