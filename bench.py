@@ -41,7 +41,11 @@ SOLVE_WORKLOADS = ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32", "packed_
                    "packed_ragged48_h64_f32_bf16", "packed_1x131072_h64_f32",
                    "packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"]
 KKT_WORKLOADS = ["packed_16x512_h64_k128_kkt_bf16_f32", "packed_16x512_h64_k128_kkt_f32_f32"]
-WORKLOADS = SOLVE_WORKLOADS + KKT_WORKLOADS
+DECODE_WORKLOADS = [f"decode_b{B}_h32_d128_w4_bf16" for B in (2, 4, 8, 16, 32)]
+WORKLOADS = SOLVE_WORKLOADS + KKT_WORKLOADS + DECODE_WORKLOADS
+# The decode page's per-layer medians of its fused GFX950 kernel, by batch
+# size (graph replay; model shapes not stated): context, not a target.
+DECODE_PAGES_US = {2: 11.19, 4: 11.78, 8: 13.30, 16: 15.25, 32: 22.14}
 MAIN_WORKLOAD = "packed_16x512_h64_f32"
 METRIC = "64x64 tril inverses/sec + achieved HBM GB/s (% peak), 8192 tok x 64 heads"
 COPY_KERNEL = "kda_probe_copy_kernel"
@@ -57,6 +61,8 @@ def kernel_of(workload: str):
     The pattern is matched against rocprofv3's demangled kernel names."""
     if workload in KKT_WORKLOADS:  # the fused kernel, not the matrix-only one
         return r"tril_kkt<.*, true>", ["tril_device.h", "tril_kkt.hip", "tril_launch.h"]
+    if workload in DECODE_WORKLOADS:
+        return r"kda_decode_step_kernel<", ["tril_device.h", "kda_decode.hip", "tril_launch.h"]
     import synth
     C = synth.CONFIGS[workload].get("chunk", 64)
     if C == 64:
@@ -71,6 +77,9 @@ def copy_bytes_of(workload: str) -> int:
     if workload in KKT_WORKLOADS:
         cfg = synth.KKT_CONFIGS[workload]
         return int(sum(synth.config_lengths(cfg))) * cfg["H"] * cfg["K"] * 4
+    if workload in DECODE_WORKLOADS:  # the state pool of one set
+        cfg = synth.DECODE_CONFIGS[workload]
+        return cfg["slots"] * cfg["H"] * cfg["d"] * cfg["d"] * 4
     cfg = synth.CONFIGS[workload]
     return (int(sum(synth.config_lengths(cfg))) * cfg["H"] * cfg.get("chunk", 64) *
             dtype_bytes(cfg["a_dtype"]))
@@ -483,6 +492,72 @@ def run_kkt(args, torch, np, dev, stream):
     return 0
 
 
+def decode_algorithmic_bytes(B, H, d, W, in_bytes, out_bytes, padding=0) -> int:
+    """One decode step: per non-padding (sequence, head) the d x d FP32 state
+    and the three (W - 1) x d conv windows read and written, the new q, k, v,
+    gate, decays, write strength read and the output written; per head the
+    conv taps, and once the norm weights."""
+    per = (2 * d * d * 4 + 2 * 3 * (W - 1) * d * 4 + 3 * d * in_bytes + d * in_bytes + d * 4 +
+           4 + d * out_bytes)
+    return (B - padding) * H * per + H * 3 * W * d * 4 + d * 4
+
+
+def run_decode(args, torch, np, dev, stream):
+    """The fused KDA decode core: one step for B sequences, rotating over
+    several state pools (one per layer) so that the states come from HBM."""
+    import synth
+    import tril_solve_amd as kt
+
+    cfg = synth.DECODE_CONFIGS[args.workload]
+    B, H, d, W = cfg["B"], cfg["H"], cfg["d"], cfg["W"]
+    ib, ob = dtype_bytes(cfg["in_dtype"]), dtype_bytes(cfg["out_dtype"])
+    bytes_alg = decode_algorithmic_bytes(B, H, d, W, ib, ob)
+    touched = B * H * d * d * 4  # state bytes one step touches
+    nsets = args.sets or max(2, min(64, -(-(1 << 30) // touched)))
+    x_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["out_dtype"], torch.float32)
+    in_dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg["in_dtype"], torch.float32)
+
+    def to_in(a):
+        if in_dt != torch.float32:
+            return torch.from_numpy(a.view(np.int16)).view(in_dt).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    sets = []
+    for i in range(nsets):
+        inp = synth.decode_inputs(B, H, d, W, cfg["slots"], cfg["seed"] + 1000 * i,
+                                  cfg["in_dtype"])
+        t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+             for k in ("g", "beta", "norm_w", "conv_w", "slot", "state", "conv_state")}
+        t["qkv"], t["z"] = to_in(inp["qkv"]), to_in(inp["z"])
+        t["out"] = torch.empty((B, H, d), dtype=x_dt, device=dev)
+        sets.append(t)
+    torch.cuda.synchronize()
+
+    copy = CopyProbe(torch, stream, dev)
+    if args.probe == "copy":
+        return copy.only([t["state"] for t in sets], args)
+
+    calls = [kt.prepare_decode(t["qkv"], t["z"], t["g"], t["beta"], t["norm_w"], t["conv_w"],
+                               t["slot"], t["state"], t["conv_state"], t["out"]) for t in sets]
+    el, k_avg, dist = Timer(torch, stream).run(calls, args.steps, args.warmup)
+    copy_gbs = copy.rate_gbs([t["state"] for t in sets[:4]])
+    out = base_line(args, el, k_avg, dist, B, bytes_alg, len(sets),
+                    "fused KDA decode core: sequences decoded per second through one layer "
+                    "+ achieved HBM GB/s (% peak)", None,
+                    {"workload": f"decode step, {B} sequences, {H} heads of dim {d}, conv width "
+                                 f"{W}, {cfg['in_dtype']} activations -> {cfg['out_dtype']} "
+                                 f"output, FP32 state pools of {cfg['slots']} slots",
+                     "batch": B, "heads": H, "head_dim": d, "conv_width": W,
+                     "in_dtype": cfg["in_dtype"], "out_dtype": cfg["out_dtype"]})
+    out["unit"] = "sequences/s"
+    out["roofline"]["traffic"] = load_traffic(args.workload)
+    out["pages_gfx950_fused_us_context"] = DECODE_PAGES_US.get(B)
+    out["copy_roofline_gbs"] = copy_gbs
+    out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -518,10 +593,12 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    if args.workload in KKT_WORKLOADS:
+    if args.workload in KKT_WORKLOADS or args.workload in DECODE_WORKLOADS:
         if args.algo not in ("auto", "fused"):
-            log("bench.py: the build-A path has a single kernel (algo auto or fused)")
+            log("bench.py: this workload has a single kernel (algo auto or fused)")
             return 2
+        if args.workload in DECODE_WORKLOADS:
+            return run_decode(args, torch, np, dev, stream)
         return run_kkt(args, torch, np, dev, stream)
     return run_solve(args, torch, np, dev, stream)
 

@@ -18,7 +18,8 @@
 //
 // One workgroup of 256 threads per (sequence, head). The state dominates the
 // traffic (64 KiB read and 64 KiB written per step), so its loads are issued
-// first and the convolution and norms run while they are in flight. Thread
+// right after the convolution's few inputs, and the convolution and norms run
+// while they are in flight. Thread
 // (c, r), c = t % 32, r = t / 32, holds columns 4c..4c+3 of rows 16r..16r+15
 // in registers for the whole step: one pass gives both reductions S^T k and
 // S^T q of the decayed state (partial sums over its 16 rows, combined over
@@ -92,43 +93,71 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
         return;
     }
 
-    // 1. the state tile of this thread, issued before anything else
+    // 1. the small inputs of the convolution first: the memory counter waits
+    //    in issue order, so loads issued after the state tile could only be
+    //    used once the whole tile had arrived. Threads 0..127 handle the q
+    //    and k channels, threads 128..255 the v channels; conv widths 2..4.
+    //    The loads are unconditional (indices past the width or the thread's
+    //    projections are clamped to valid ones and their values unused), so
+    //    they form one block the state loads can follow with no wait between.
+    const int c = t & (kDecD - 1);
+    const int W = p.W;
+    // wavefront-uniform (waves 0-1 vs 2-3)
+    const bool low = __builtin_amdgcn_readfirstlane(t) < kDecD;
+    const int pfirst = low ? 0 : 2, pn = low ? 2 : 1;
+    const typename EI::T *qkv = static_cast<const typename EI::T *>(p.qkv);
+    float xin[2], win[2][3], tap[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int p3 = k < pn ? pfirst + k : pfirst;
+        xin[k] = ld_elem<EI>(qkv, (((long)b * 3 + p3) * p.H + h) * kDecD + c);
+        const float *ws = p.conv_state + (((long)slot * 3 + p3) * p.H + h) * (long)(W - 1) * kDecD;
+        const float *cw = p.conv_w + ((long)p3 * W * p.H + h) * kDecD + c;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w < 3) win[k][w] = ws[(long)(w < W - 1 ? w : 0) * kDecD + c];
+            tap[k][w] = cw[(long)(w < W ? w : 0) * p.H * kDecD];
+        }
+    }
+    const float graw = p.g[((long)b * p.H + h) * kDecD + c];
+
+    // 2. then the state tile of this thread
     const int c4 = (t & 31) * 4, r0 = (t >> 5) * kDecRows;
     float *S = p.state + ((long)slot * p.H + h) * kDecD * kDecD;
     f4 s[kDecRows];
 #pragma unroll
     for (int r = 0; r < kDecRows; ++r)
         s[r] = *reinterpret_cast<const f4 *>(&S[(long)(r0 + r) * kDecD + c4]);
+    __builtin_amdgcn_sched_barrier(0);  // keep every use of the loads below this point
 
-    // 2. causal convolution of q, k (threads 0..127) and v (threads 128..255)
-    //    over the window of the W - 1 previous inputs and the new one; the
-    //    window then shifts by one
-    {
-        const int c = t & (kDecD - 1);
-        const int W = p.W;
-        const typename EI::T *qkv = static_cast<const typename EI::T *>(p.qkv);
-        for (int p3 = (t < kDecD ? 0 : 2); p3 < (t < kDecD ? 2 : 3); ++p3) {
-            const float x = ld_elem<EI>(qkv, (((long)b * 3 + p3) * p.H + h) * kDecD + c);
-            float *win = p.conv_state + (((long)slot * 3 + p3) * p.H + h) * (long)(W - 1) * kDecD;
-            const float *cw = p.conv_w + ((long)p3 * W * p.H + h) * kDecD + c;
+    // 3. causal convolution over the window of the W - 1 previous inputs and
+    //    the new one; the window then shifts by one (oldest entry dropped)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (k < pn) {
+            const int p3 = pfirst + k;
+            float *ws = p.conv_state + (((long)slot * 3 + p3) * p.H + h) * (long)(W - 1) * kDecD;
             float acc = 0.0f;
-            for (int w = 0; w < W - 1; ++w) {  // W >= 2: the window is never empty
-                const float v = win[(long)w * kDecD + c];
-                acc = __builtin_fmaf(cw[(long)w * p.H * kDecD], v, acc);
-                if (w > 0) win[(long)(w - 1) * kDecD + c] = v;  // shift left by one
-            }
-            acc = __builtin_fmaf(cw[(long)(W - 1) * p.H * kDecD], x, acc);
-            win[(long)(W - 2) * kDecD + c] = x;
+#pragma unroll
+            for (int w = 0; w < 3; ++w)
+                if (w < W - 1) acc = __builtin_fmaf(tap[k][w], win[k][w], acc);
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if (w == W - 1) acc = __builtin_fmaf(tap[k][w], xin[k], acc);
+#pragma unroll
+            for (int w = 1; w < 3; ++w)
+                if (w < W - 1) ws[(long)(w - 1) * kDecD + c] = win[k][w];
+            ws[(long)(W - 2) * kDecD + c] = xin[k];
             const float y = acc / (1.0f + __expf(-acc));  // silu
             if (p3 == 0) yq[c] = y;
             if (p3 == 1) yk[c] = y;
             if (p3 == 2) yv[c] = y;
         }
-        if (t < kDecD) gq[t] = __expf(p.g[((long)b * p.H + h) * kDecD + t]);
     }
+    if (low) gq[c] = __expf(graw);
     __syncthreads();
 
-    // 3. squared norms of y_q, y_k and their dot product (waves 0 and 1)
+    // 4. squared norms of y_q, y_k and their dot product (waves 0 and 1)
     if (t < kDecD) {
         const float a = yq[t], bk = yk[t];
         const float s0 = wave_sum(a * a), s1 = wave_sum(bk * bk), s2 = wave_sum(a * bk);
@@ -144,7 +173,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     const float sq = 1.0f / (__builtin_sqrtf(nq + p.eps_l2) * __builtin_sqrtf((float)kDecD));
     const float sk = 1.0f / __builtin_sqrtf(nk + p.eps_l2);
 
-    // 4. decay, then partial S^T k and S^T q over this thread's 16 rows
+    // 5. decay, then partial S^T k and S^T q over this thread's 16 rows
     f4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = pa;
 #pragma unroll
     for (int r = 0; r < kDecRows; ++r) {
@@ -158,7 +187,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     *reinterpret_cast<f4 *>(&part[1][t >> 5][c4]) = pb;
     __syncthreads();
 
-    // 5. u = beta (v - S^T k) and o = S^T q + (k . q) u per value column
+    // 6. u = beta (v - S^T k) and o = S^T q + (k . q) u per value column
     if (t < kDecD) {
         float a = 0.0f, bq = 0.0f;
 #pragma unroll
@@ -172,7 +201,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     }
     __syncthreads();
 
-    // 6. state update S += k u^T, written back in place
+    // 7. state update S += k u^T, written back in place
     {
         const f4 u4 = *reinterpret_cast<const f4 *>(&uo[0][c4]);
 #pragma unroll
@@ -182,7 +211,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
         }
     }
 
-    // 7. gated RMSNorm of o
+    // 8. gated RMSNorm of o
     if (t < kDecD) {
         const float o = uo[1][t];
         const float ss = wave_sum(o * o);
