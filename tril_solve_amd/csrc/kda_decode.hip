@@ -17,15 +17,17 @@
 // paged pools indexed by a per-sequence slot (negative: padding entry).
 //
 // One workgroup of 256 threads per (sequence, head). The state dominates the
-// traffic (64 KiB read and 64 KiB written per step), so its loads are issued
-// right after the convolution's few inputs, and the convolution and norms run
-// while they are in flight. Thread
-// (c, r), c = t % 32, r = t / 32, holds columns 4c..4c+3 of rows 16r..16r+15
-// in registers for the whole step: one pass gives both reductions S^T k and
-// S^T q of the decayed state (partial sums over its 16 rows, combined over
-// the 8 row groups through LDS), then the update is applied to the same
-// registers and written back. Since S_new^T q = (decayed S)^T q + (k . q) u,
-// the state is read and written exactly once.
+// traffic (64 KiB read and 64 KiB written per step), so every other input is
+// loaded first and the state tile right after, before any wait; the
+// convolution and the norms then run while the tile is in flight. The state
+// is split by value columns: wavefront w owns columns 32w..32w+31 of all 128
+// key rows (lane l: columns 32w + 4(l % 8) .. +3 of rows 16(l / 8) .. +15), so the
+// reductions over key rows (S^T k and S^T q of the decayed state) stay inside
+// the wavefront (per-lane sums over 16 rows, then lanes xor 8, 16, 32) and
+// each wavefront updates and writes back its columns as soon as its own
+// tile has arrived, with no barrier in between. Since
+// S_new^T q = (decayed S)^T q + (k . q) u, the state is read and written
+// exactly once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,8 +38,10 @@ namespace kda {
 
 constexpr int kDecD = 128;         // head dim (keys = values)
 constexpr int kDecThreads = 256;
-constexpr int kDecRows = 16;       // state rows per thread
-constexpr int kDecGroups = 8;      // row groups (16 rows each)
+constexpr int kDecRows = 16;       // state rows per lane
+constexpr int kDecPad = kDecD + kDecD / 16;
+
+__device__ __forceinline__ int pad_row(int r) { return r + (r >> 4); }
 
 template <class E>
 __device__ __forceinline__ float ld_elem(const typename E::T *p, long i);
@@ -79,38 +83,40 @@ __device__ __forceinline__ float wave_sum(float v) {
 // One step for one (sequence, head); layouts as in the C ABI.
 template <class EI, class EO>
 __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProblem p) {
-    __shared__ float yq[kDecD], yk[kDecD], yv[kDecD], gq[kDecD];
-    __shared__ float part[2][kDecGroups][kDecD];
-    __shared__ float red[4][4];
-    __shared__ float uo[2][kDecD];
+    // per key row: padded (row r at r + r / 16), so the 8 rows a wavefront
+    // reads at once (16 apart) fall in distinct banks
+    __shared__ float yq[kDecPad], yk[kDecPad], gq[kDecPad];
+    __shared__ __align__(16) float yv[kDecD], zs[kDecD], nws[kDecD];  // per value column
+    __shared__ float red[kDecThreads / kWave];
 
     const int t = threadIdx.x;
     const int b = blockIdx.x / p.H, h = blockIdx.x - b * p.H;
+    const long bh = (long)b * p.H + h;
     const int slot = p.slot[b];
-    typename EO::T *out = static_cast<typename EO::T *>(p.out) + ((long)b * p.H + h) * kDecD;
+    typename EO::T *out = static_cast<typename EO::T *>(p.out) + bh * kDecD;
     if (slot < 0 || slot >= p.num_slots) {  // padding (or a slot outside the pool)
         if (t < kDecD) st_elem<EO>(out, t, 0.0f);
         return;
     }
 
-    // 1. the small inputs of the convolution first: the memory counter waits
-    //    in issue order, so loads issued after the state tile could only be
-    //    used once the whole tile had arrived. Threads 0..127 handle the q
-    //    and k channels, threads 128..255 the v channels; conv widths 2..4.
-    //    The loads are unconditional (indices past the width or the thread's
+    // 1. every small input first: the memory counter waits in issue order, so
+    //    a load issued after the state tile could only be used once the whole
+    //    tile had arrived. Threads 0..127 handle the q and k channels of the
+    //    convolution, threads 128..255 the v channels; conv widths 2..4. The
+    //    loads are unconditional (indices past the width or the thread's
     //    projections are clamped to valid ones and their values unused), so
-    //    they form one block the state loads can follow with no wait between.
+    //    they form one block that the state loads follow with no wait between.
     const int c = t & (kDecD - 1);
     const int W = p.W;
-    // wavefront-uniform (waves 0-1 vs 2-3)
-    const bool low = __builtin_amdgcn_readfirstlane(t) < kDecD;
+    const int wv = __builtin_amdgcn_readfirstlane(t) / kWave;  // wavefront index
+    const bool low = wv < 2;
     const int pfirst = low ? 0 : 2, pn = low ? 2 : 1;
     const typename EI::T *qkv = static_cast<const typename EI::T *>(p.qkv);
     float xin[2], win[2][3], tap[2][4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int p3 = k < pn ? pfirst + k : pfirst;
-        xin[k] = ld_elem<EI>(qkv, (((long)b * 3 + p3) * p.H + h) * kDecD + c);
+        xin[k] = ld_elem<EI>(qkv, ((long)b * 3 + p3) * p.H * kDecD + (long)h * kDecD + c);
         const float *ws = p.conv_state + (((long)slot * 3 + p3) * p.H + h) * (long)(W - 1) * kDecD;
         const float *cw = p.conv_w + ((long)p3 * W * p.H + h) * kDecD + c;
 #pragma unroll
@@ -119,15 +125,21 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
             tap[k][w] = cw[(long)(w < W ? w : 0) * p.H * kDecD];
         }
     }
-    const float graw = p.g[((long)b * p.H + h) * kDecD + c];
+    const float graw = p.g[bh * kDecD + c];
+    const float beta = p.beta[bh];
+    // z (threads 0..127) and norm_w (threads 128..255), kept in LDS until the end
+    const float zraw = ld_elem<EI>(static_cast<const typename EI::T *>(p.z), bh * kDecD + c);
+    const float nwraw = p.norm_w[c];
+    // this lane's 4 value columns and its 16 consecutive key rows
+    const int l = t & (kWave - 1);
+    const int col = 32 * wv + 4 * (l & 7), row0 = 16 * (l >> 3);
 
-    // 2. then the state tile of this thread
-    const int c4 = (t & 31) * 4, r0 = (t >> 5) * kDecRows;
-    float *S = p.state + ((long)slot * p.H + h) * kDecD * kDecD;
+    // 2. then the state tile of this lane
+    float *S = p.state + ((long)slot * p.H + h) * kDecD * kDecD + col;
     f4 s[kDecRows];
 #pragma unroll
-    for (int r = 0; r < kDecRows; ++r)
-        s[r] = *reinterpret_cast<const f4 *>(&S[(long)(r0 + r) * kDecD + c4]);
+    for (int i = 0; i < kDecRows; ++i)
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(long)(row0 + i) * kDecD]));
     __builtin_amdgcn_sched_barrier(0);  // keep every use of the loads below this point
 
     // 3. causal convolution over the window of the W - 1 previous inputs and
@@ -149,82 +161,75 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
                 if (w < W - 1) ws[(long)(w - 1) * kDecD + c] = win[k][w];
             ws[(long)(W - 2) * kDecD + c] = xin[k];
             const float y = acc / (1.0f + __expf(-acc));  // silu
-            if (p3 == 0) yq[c] = y;
-            if (p3 == 1) yk[c] = y;
+            if (p3 == 0) yq[pad_row(c)] = y;
+            if (p3 == 1) yk[pad_row(c)] = y;
             if (p3 == 2) yv[c] = y;
         }
     }
-    if (low) gq[c] = __expf(graw);
-    __syncthreads();
-
-    // 4. squared norms of y_q, y_k and their dot product (waves 0 and 1)
-    if (t < kDecD) {
-        const float a = yq[t], bk = yk[t];
-        const float s0 = wave_sum(a * a), s1 = wave_sum(bk * bk), s2 = wave_sum(a * bk);
-        if ((t & (kWave - 1)) == 0) {
-            red[t / kWave][0] = s0;
-            red[t / kWave][1] = s1;
-            red[t / kWave][2] = s2;
-        }
+    if (low) {
+        gq[pad_row(c)] = __expf(graw);
+        zs[c] = zraw;
+    } else {
+        nws[c] = nwraw;
     }
     __syncthreads();
-    const float nq = red[0][0] + red[1][0], nk = red[0][1] + red[1][1];
-    const float dqk = red[0][2] + red[1][2];
-    const float sq = 1.0f / (__builtin_sqrtf(nq + p.eps_l2) * __builtin_sqrtf((float)kDecD));
-    const float sk = 1.0f / __builtin_sqrtf(nk + p.eps_l2);
 
-    // 5. decay, then partial S^T k and S^T q over this thread's 16 rows
+    // 4. squared norms of y_q, y_k and their dot product, in every wavefront
+    float sq, sk, dqk;
+    {
+        const float a0 = yq[pad_row(l)], a1 = yq[pad_row(l + kWave)];
+        const float k0 = yk[pad_row(l)], k1 = yk[pad_row(l + kWave)];
+        const float nq = wave_sum(a0 * a0 + a1 * a1), nk = wave_sum(k0 * k0 + k1 * k1);
+        dqk = wave_sum(a0 * k0 + a1 * k1);
+        sq = 1.0f / (__builtin_sqrtf(nq + p.eps_l2) * __builtin_sqrtf((float)kDecD));
+        sk = 1.0f / __builtin_sqrtf(nk + p.eps_l2);
+    }
+
+    // 5. decay, then S^T k and S^T q over the 128 rows of this lane's columns
     f4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = pa;
 #pragma unroll
-    for (int r = 0; r < kDecRows; ++r) {
-        const int i = r0 + r;
-        s[r] *= gq[i];
-        const float ki = yk[i] * sk, qi = yq[i] * sq;
-        pa += s[r] * ki;
-        pb += s[r] * qi;
+    for (int i = 0; i < kDecRows; ++i) {
+        const int r = pad_row(row0 + i);
+        s[i] *= gq[r];
+        pa += s[i] * yk[r];
+        pb += s[i] * yq[r];
     }
-    *reinterpret_cast<f4 *>(&part[0][t >> 5][c4]) = pa;
-    *reinterpret_cast<f4 *>(&part[1][t >> 5][c4]) = pb;
-    __syncthreads();
-
-    // 6. u = beta (v - S^T k) and o = S^T q + (k . q) u per value column
-    if (t < kDecD) {
-        float a = 0.0f, bq = 0.0f;
 #pragma unroll
-        for (int r = 0; r < kDecGroups; ++r) {
-            a += part[0][r][t];
-            bq += part[1][r][t];
-        }
-        const float u = p.beta[(long)b * p.H + h] * (yv[t] - a);
-        uo[0][t] = u;
-        uo[1][t] = bq + dqk * sq * sk * u;
-    }
-    __syncthreads();
-
-    // 7. state update S += k u^T, written back in place
-    {
-        const f4 u4 = *reinterpret_cast<const f4 *>(&uo[0][c4]);
+    for (int o = 8; o < kWave; o <<= 1) {
 #pragma unroll
-        for (int r = 0; r < kDecRows; ++r) {
-            const float ki = yk[r0 + r] * sk;
-            *reinterpret_cast<f4 *>(&S[(long)(r0 + r) * kDecD + c4]) = s[r] + ki * u4;
+        for (int j = 0; j < 4; ++j) {
+            pa[j] += __shfl_xor(pa[j], o, kWave);
+            pb[j] += __shfl_xor(pb[j], o, kWave);
         }
     }
 
-    // 8. gated RMSNorm of o
-    if (t < kDecD) {
-        const float o = uo[1][t];
-        const float ss = wave_sum(o * o);
-        if ((t & (kWave - 1)) == 0) red[t / kWave][3] = ss;
+    // 6. u = beta (v - S^T k), state update S += k u^T written back in place,
+    //    o = S^T q + (k . q) u
+    const f4 v4 = *reinterpret_cast<const f4 *>(&yv[col]);
+    const f4 u = beta * (v4 - pa * sk);
+#pragma unroll
+    for (int i = 0; i < kDecRows; ++i) {
+        const float ki = yk[pad_row(row0 + i)] * sk;
+        __builtin_nontemporal_store(s[i] + ki * u, reinterpret_cast<f4 *>(&S[(long)(row0 + i) * kDecD]));
     }
+    const f4 o = pb * sq + (dqk * sq * sk) * u;
+
+    // 7. gated RMSNorm of o over the 128 value columns
+    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+    if (l == 0) red[wv] = ss;
     __syncthreads();
-    if (t < kDecD) {
-        const float ms = (red[0][3] + red[1][3]) / kDecD;
+    if (l < 8) {
+        const float ms = (red[0] + red[1] + red[2] + red[3]) / kDecD;
         const float rn = 1.0f / __builtin_sqrtf(ms + p.eps_norm);
-        const typename EI::T *z = static_cast<const typename EI::T *>(p.z);
-        const float zz = ld_elem<EI>(z, ((long)b * p.H + h) * kDecD + t);
-        const float gate = 1.0f / (1.0f + __expf(-zz));
-        st_elem<EO>(out, t, uo[1][t] * rn * p.norm_w[t] * gate);
+        const f4 z4 = *reinterpret_cast<const f4 *>(&zs[col]);
+        const f4 w4 = *reinterpret_cast<const f4 *>(&nws[col]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float gate = 1.0f / (1.0f + __expf(-z4[j]));
+            st_elem<EO>(out, col + j, o[j] * rn * w4[j] * gate);
+        }
     }
 }
 
