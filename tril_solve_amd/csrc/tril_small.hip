@@ -28,6 +28,26 @@
 
 namespace kda {
 
+// load1 with the nontemporal policy, for the 16-token kernel whose every
+// line is read by exactly one load instruction (a line read again by a later
+// instruction would be fetched twice, so the other kernels keep the default
+// policy).
+template <class E>
+__device__ __forceinline__ float load1_once(Rsrc r, uint32_t off);
+template <>
+__device__ __forceinline__ float load1_once<F32>(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNontemporal));
+}
+template <>
+__device__ __forceinline__ float load1_once<BF16>(Rsrc r, uint32_t off) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNontemporal));
+}
+template <>
+__device__ __forceinline__ float load1_once<F16>(Rsrc r, uint32_t off) {
+    return (float)__builtin_bit_cast(_Float16,
+                                     __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNontemporal));
+}
+
 // --------------------------------------------------------------- 16 tokens
 
 constexpr int kHeads16 = 4;  // heads per wavefront (4 x 16 columns = 64 lanes)
@@ -81,7 +101,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c16(Problem p) {
         const uint32_t offa = (uint32_t)lane * EI::kBytes | mask;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            a[i] = load1<EI>(ra, offa + (uint32_t)(i * rstride * EI::kBytes));
+            a[i] = load1_once<EI>(ra, offa + (uint32_t)(i * rstride * EI::kBytes));
 
         float x[16];
 #pragma unroll
