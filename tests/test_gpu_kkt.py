@@ -105,6 +105,26 @@ def test_dtype_matrix(kt, k_dtype, x_dtype):
     assert e <= 0, f"A exceeds tolerance by {e:.3g}"
 
 
+@pytest.mark.parametrize("K", [16, 32, 48, 80, 256])
+@pytest.mark.parametrize("k_dtype", ["bf16", "f16"])
+def test_half_precision_keys_slice_tails(kt, k_dtype, K):
+    """16-bit keys (a 32-channel slice is half of each key line, and the
+    decays are read with their own cache policy) over K of one half slice,
+    one slice, a slice and a half, two and a half slices and eight slices."""
+    print(f"\n[kkt] {k_dtype} keys K={K}", flush=True)
+    H = 3
+    k, g, beta = _inputs(LENGTHS, H, K, k_dtype, seed=80 + K)
+    cu = synth.cu_seqlens(LENGTHS)
+    dv = _dev(k, g, beta, k_dtype)
+    got = gh.to_numpy_f64(_solve(kt, *dv, cu))
+    ref = oracle.kkt_tril_inv_packed(k, g, beta, cu, k_dtype)
+    e = gh.excess(got, ref, "f32")
+    assert e <= 0, f"X exceeds tolerance by {e:.3g}"
+    gotA = gh.to_numpy_f64(_solve(kt, *dv, cu, solve=False))
+    e = gh.excess(gotA, oracle.kkt_packed(k, g, beta, cu, k_dtype), "f32")
+    assert e <= 0, f"A exceeds tolerance by {e:.3g}"
+
+
 @pytest.mark.parametrize("k_dtype", ["f32", "bf16"])
 def test_fused_equals_unfused_bitwise(kt, k_dtype):
     """X from the fused call equals, bit for bit, the 64-token solver applied

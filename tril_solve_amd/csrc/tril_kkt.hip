@@ -67,6 +67,17 @@ struct Raw4<F32> {
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
 };
+// The FP32 decays as loaded. Each decay line is used up by the iteration
+// that loads it; a 16-bit key line is only half used by one slice, so with
+// 16-bit keys the decays take the nontemporal policy and L2 evicts them
+// first, which keeps more key lines for the next slice (HBM reads per launch
+// at 16 x 512 tokens, 64 heads, K = 128: 510 -> 448 MB). FP32 key lines are
+// used up in one slice, and the default policy stays.
+template <class EK>
+__device__ __forceinline__ u4 load_decays(Rsrc r, uint32_t off) {
+    constexpr int policy = EK::kBytes == 2 ? kNontemporal : 0;
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, policy));
+}
 template <class E>
 __device__ __forceinline__ f4 widen4(typename Raw4<E>::T v);
 template <>
@@ -155,7 +166,7 @@ struct SliceSrc {
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                s.g[b][t] = Raw4<F32>::load(rg, offgb[b] + (d0 + 4 * t) * F32::kBytes - gback);
+                s.g[b][t] = load_decays<EK>(rg, offgb[b] + (d0 + 4 * t) * F32::kBytes - gback);
                 s.k[b][t] =
                     Raw4<EK>::load(rk, (offk + b * blk_k + (d0 + 4 * t) * EK::kBytes) | kmask);
             }
