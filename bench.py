@@ -12,9 +12,10 @@ bytes than the 256 MB Infinity Cache) so that no step reads its input from
 the cache.
 
 Other workloads (--workload) are diagnostics: the other batch shapes, the
-16- and 32-token branches, and the path that builds A from keys, decays and
+16- and 32-token branches, the path that builds A from keys, decays and
 write strengths inside the solver (timed beside the unfused pair: A stored,
-then solved).
+then solved), and the fused KDA decode core. --oracle-table times the CPU
+oracle alone on the five solver batch shapes.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
@@ -198,6 +199,36 @@ def cpu_baseline(d, budget_s=12.0):
             "sample": f"whole workload ({d['num_chunks'] * d['H']} matrices) solved {n}x "
                       f"by the fp64 oracle in {el:.1f} s",
             "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def oracle_table(budget_s: float = 3.0) -> int:
+    """Times the fp64 oracle on the five solver configurations (the same
+    inputs the GPU legs use), with all host threads and with one, and prints
+    one JSON line per configuration. No GPU use."""
+    import oracle
+    import synth
+    for name in SOLVE_WORKLOADS[:5]:
+        log(f"[oracle] {name}")
+        d = synth.make(name)
+        mats = d["num_chunks"] * d["H"]
+        row = {"workload": name, "matrices": mats, "cpu_model": _cpu_model(),
+               "nproc": os.cpu_count()}
+        for label, nth in (("all_threads", 0), ("one_thread", 1)):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                if d["layout"] == "dense":
+                    oracle.tril_inv_dense(d["A"], d["a_dtype"], nthreads=nth)
+                else:
+                    oracle.tril_inv_packed(d["A"], d["cu_seqlens"], d["a_dtype"], nthreads=nth)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+            row[label] = {"threads": oracle.num_threads() if nth == 0 else 1, "calls": n,
+                          "ms_per_call": 1e3 * el / n, "inverses_per_s": mats * n / el}
+        print(json.dumps(row), flush=True)
+        del d
+    return 0
 
 
 def _cpu_model() -> str:
@@ -575,8 +606,13 @@ def main() -> int:
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
                     help="write the HBM-traffic summary of --workload from rocprofv3 counter "
                          "CSVs (no GPU use)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the CPU oracle on the five solver configurations, all host "
+                         "threads and one (no GPU use)")
     args = ap.parse_args()
 
+    if args.oracle_table:
+        return oracle_table()
     if args.record_traffic:
         t = record_traffic(args.workload, args.record_traffic[:4], args.record_traffic[4])
         log(json.dumps(t))

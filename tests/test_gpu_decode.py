@@ -66,7 +66,7 @@ def _check(kt, inp, d, out, x_dtype="f32"):
 
 
 @pytest.mark.parametrize("W", [2, 3, 4])
-@pytest.mark.parametrize("B,H", [(1, 1), (3, 4), (8, 2)])
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 4), (8, 2), (96, 3)])
 def test_step_parity(kt, B, H, W):
     print(f"\n[decode] B={B} H={H} W={W}", flush=True)
     inp = synth.decode_inputs(B, H, W=W, seed=100 + B * 10 + H + W)
@@ -192,3 +192,31 @@ def test_bench_launch_configuration(kt):
     torch.cuda.synchronize()
     for inp, d, o in zip(sets, devs, outs):
         _check(kt, inp, d, o, "bf16")
+
+
+def test_slots_past_4gib_of_state(kt):
+    """A state pool of 2100 slots x 32 heads (4.4 GB): slots near its end,
+    whose byte offsets need more than 32 bits, against the oracle on a
+    compact pool of the used slots; a slot no entry names keeps its bits."""
+    B, H, n_slots = 4, 32, 2100
+    print(f"\n[decode] pool of {n_slots} slots x {H} heads", flush=True)
+    inp = synth.decode_inputs(B, H, seed=125, slots=B)  # compact pool: slots 0..B-1
+    where = np.array([2099, 2050, 1, 2098])  # compact slot c lives in pool slot where[c]
+    d = _dev(inp)
+    S = torch.zeros((n_slots, H, 128, 128), device=DEV)
+    cs = torch.zeros((n_slots, 3, H, 3, 128), device=DEV)
+    for c in range(B):
+        S[where[c]] = d["state"][c]
+        cs[where[c]] = d["conv_state"][c]
+    S[2000] = 7.0
+    d["state"], d["conv_state"] = S, cs
+    d["slot"] = torch.from_numpy(where[inp["slot"]].astype(np.int32)).to(DEV)
+    out = _step(kt, d)
+    ref_out, ref_S, ref_cs = _ref(inp)
+    assert gh.excess(gh.to_numpy_f64(out), ref_out, "f32") <= 0
+    idx = torch.from_numpy(where).to(DEV)
+    e = gh.excess(S[idx].cpu().numpy().astype(np.float64), ref_S, "f32")
+    assert e <= 0, f"state exceeds tolerance by {e:.3g}"
+    e = gh.excess(cs[idx].cpu().numpy().astype(np.float64), ref_cs, "f32")
+    assert e <= 0, f"conv windows exceed tolerance by {e:.3g}"
+    assert bool((S[2000] == 7.0).all())
