@@ -102,11 +102,23 @@ def load_copy_probe():
     return lib
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so a
+    comment edit leaves the kernel hash unchanged (the sources hold no string
+    literals with comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash(workload: str) -> str:
+    """Hash of the code (comments aside) of the sources a workload's kernel
+    is built from."""
     h = hashlib.sha256()
     for f in kernel_of(workload)[1]:
-        with open(os.path.join(ROOT, "tril_solve_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tril_solve_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

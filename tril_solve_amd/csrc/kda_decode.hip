@@ -14,7 +14,8 @@
 //   out = o / sqrt(mean(o^2) + eps_norm) * wn * sigmoid(z)
 //
 // with S (D x D FP32, key rows, value columns) and the conv windows kept in
-// paged pools indexed by a per-sequence slot (negative: padding entry).
+// paged pools indexed by a per-sequence slot (negative or past the pool: a
+// padding entry).
 //
 // One workgroup of 256 threads per (sequence, head). The state dominates the
 // traffic (64 KiB read and 64 KiB written per step), so every other input is
