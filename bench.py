@@ -308,6 +308,42 @@ class Timer:
         return el, avg, dist
 
 
+def graph_replay(torch, launch_all, n_calls, replays=50):
+    """Per-call time of n_calls launches captured once into a HIP graph (the
+    graph-replay setting) and replayed: launch_all() issues the calls on the
+    current stream. Returns (average over back-to-back replays, median of
+    individually bracketed replays), both in microseconds per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        launch_all()  # warm-up outside the graph
+    side.synchronize()
+    with torch.cuda.graph(g):
+        launch_all()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) * 1e3 / (replays * n_calls)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 / n_calls for a, b in ev)
+    return avg, per[len(per) // 2]
+
+
 class CopyProbe:
     """A plain streaming copy (read N, write N bytes) of a tensor's bytes into
     a destination of its own, marshalled once per source."""
@@ -584,6 +620,12 @@ def run_decode(args, torch, np, dev, stream):
                                t["slot"], t["state"], t["conv_state"], t["out"]) for t in sets]
     el, k_avg, dist = Timer(torch, stream).run(calls, args.steps, args.warmup)
     copy_gbs = copy.rate_gbs([t["state"] for t in sets[:4]])
+
+    def launch_all():  # one step per state pool, on the current stream
+        for t in sets:
+            kt.kda_decode_step(t["qkv"], t["z"], t["g"], t["beta"], t["norm_w"], t["conv_w"],
+                               t["slot"], t["state"], t["conv_state"], t["out"])
+    graph_avg, graph_median = graph_replay(torch, launch_all, len(sets))
     out = base_line(args, el, k_avg, dist, B, bytes_alg, len(sets),
                     "fused KDA decode core: sequences decoded per second through one layer "
                     "+ achieved HBM GB/s (% peak)", None,
@@ -594,6 +636,8 @@ def run_decode(args, torch, np, dev, stream):
                      "in_dtype": cfg["in_dtype"], "out_dtype": cfg["out_dtype"]})
     out["unit"] = "sequences/s"
     out["roofline"]["traffic"] = load_traffic(args.workload)
+    # the same steps captured once in a HIP graph (one per pool) and replayed
+    out["graph_replay_us_per_launch"] = {"avg": graph_avg, "median_of_replays": graph_median}
     out["pages_gfx950_fused_us_context"] = DECODE_PAGES_US.get(B)
     out["copy_roofline_gbs"] = copy_gbs
     out["cpu_baseline"] = None
