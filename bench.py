@@ -470,10 +470,15 @@ def run_solve(args, torch, np, dev, stream):
     if args.probe == "copy":
         return copy.only([A for A, _ in sets], args)
 
+    cmap = None
+    if args.chunk_map and not dense:  # built once on the host, reused by every call
+        cmap = torch.tensor([(s, c) for s, L in enumerate(d0["lengths"])
+                             for c in range(-(-int(L) // C))], dtype=torch.int32, device=dev)
     if dense:
         calls = [kt.prepare_dense(A, X, workspace=ws, algo=args.algo) for A, X in sets]
     else:
-        calls = [kt.prepare_packed(A, X, cu, workspace=ws, algo=args.algo) for A, X in sets]
+        calls = [kt.prepare_packed(A, X, cu, workspace=ws, algo=args.algo, chunk_indices=cmap)
+                 for A, X in sets]
     el, k_avg, dist = Timer(torch, stream).run(calls, args.steps, args.warmup)
 
     # measured copy roofline: a plain streaming copy of A's byte count, read
@@ -488,7 +493,8 @@ def run_solve(args, torch, np, dev, stream):
                     {"workload": describe(d0), "tokens": T, "heads": H,
                      "requests": len(d0["lengths"]), "matrices": mats,
                      "a_dtype": cfg["a_dtype"], "x_dtype": cfg["x_dtype"],
-                     "algo": args.algo, "plan": chosen})
+                     "algo": args.algo, "plan": chosen,
+                     "chunks_from": "caller chunk map" if cmap is not None else "cu_seqlens scan"})
     if args.algo in ("auto", "fused") and chosen == "fused":
         out["roofline"]["traffic"] = load_traffic(args.workload)
     out["copy_roofline_gbs"] = copy_gbs
@@ -662,6 +668,9 @@ def main() -> int:
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
                     help="write the HBM-traffic summary of --workload from rocprofv3 counter "
                          "CSVs (no GPU use)")
+    ap.add_argument("--chunk-map", action="store_true",
+                    help="packed solver workloads: pass a chunk map built once on the host "
+                         "instead of letting the kernels scan cu_seqlens")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on the five solver configurations, all host "
                          "threads and one (no GPU use)")
