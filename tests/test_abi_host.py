@@ -269,3 +269,36 @@ def test_decode_argument_validation(kt):
     assert _dec(kt, out=0x1000000 + 4 * 2 * 128 * 128 * 4 - 64) == E  # out overlaps state
     assert _dec(kt, B=0) == kt.KDA_OK                # no-op before any pointer is used
     assert _dec(kt, B=0, qkv=None, out=None) == kt.KDA_OK
+
+
+def test_binding_refuses_host_tensors_and_bad_shapes(kt):
+    """The Python binding refuses host (CPU) tensors before any library call,
+    since a kernel would dereference their host addresses, and reports
+    malformed arguments as ValueError."""
+    torch = pytest.importorskip("torch")
+    A = torch.zeros((64, 2, 64))
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="cuda tensor"):
+        kt.tril_inv(A, cu)
+    with pytest.raises(ValueError, match="cuda tensor"):
+        kt.tril_inv(A.view(1, 64, 2, 64))
+    with pytest.raises(ValueError, match="chunk size"):
+        kt.kda_tril_inv_packed(torch.zeros((64, 2, 48)), torch.zeros((64, 2, 48)), cu)
+    with pytest.raises(ValueError, match="int32"):
+        kt.kda_tril_inv_packed(A, torch.zeros_like(A), cu.long())
+    k = torch.zeros((64, 2, 16))
+    with pytest.raises(ValueError, match="cuda tensor"):
+        kt.kda_kkt_tril_inv(k, torch.zeros_like(k), torch.zeros((64, 2)),
+                            torch.zeros((64, 2, 64)), cu)
+    with pytest.raises(ValueError, match="float32"):
+        kt.kda_kkt_tril_inv(k, torch.zeros_like(k, dtype=torch.float64), torch.zeros((64, 2)),
+                            torch.zeros((64, 2, 64)), cu)
+    B, H, d, W, S = 2, 1, 128, 4, 3
+    dec = dict(qkv=torch.zeros((B, 3, H, d)), z=torch.zeros((B, H, d)), g=torch.zeros((B, H, d)),
+               beta=torch.zeros((B, H)), norm_w=torch.zeros(d), conv_w=torch.zeros((3, W, H, d)),
+               slot=torch.zeros(B, dtype=torch.int32), state=torch.zeros((S, H, d, d)),
+               conv_state=torch.zeros((S, 3, H, W - 1, d)), out=torch.zeros((B, H, d)))
+    with pytest.raises(ValueError, match="cuda tensor"):
+        kt.kda_decode_step(**dec)
+    with pytest.raises(ValueError, match="norm_w"):
+        kt.kda_decode_step(**dict(dec, norm_w=torch.zeros((H, d))))

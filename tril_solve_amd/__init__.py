@@ -127,8 +127,19 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _require(cond, what: str) -> None:
+    """Argument check of the binding (kept under python -O, unlike assert)."""
+    if not cond:
+        raise ValueError(what)
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a cuda tensor. Host tensors are refused: the kernels
+    would dereference a host address."""
+    if t is None:
+        return None
+    _require(t.is_cuda, f"expected a cuda tensor, got one on {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _ws_bytes(ws):
@@ -136,22 +147,26 @@ def _ws_bytes(ws):
 
 
 def _dense_args(A, X, workspace, algo, stream):
-    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 4 and A.shape == X.shape
+    _require(A.is_contiguous() and X.is_contiguous(), "A and X must be contiguous")
+    _require(A.dim() == 4 and A.shape == X.shape, "A and X must both be [B, T, H, C]")
     B, T, H, C = A.shape
-    assert C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)"
+    _require(C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)")
     return (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), B, T, H, C, _ptr(workspace),
             _ws_bytes(workspace), _algo(algo), _stream_ptr(stream))
 
 
 def _packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream):
     import torch
-    assert A.is_contiguous() and X.is_contiguous() and A.dim() == 3 and A.shape == X.shape
-    assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    _require(A.is_contiguous() and X.is_contiguous(), "A and X must be contiguous")
+    _require(A.dim() == 3 and A.shape == X.shape, "A and X must both be [T, H, C]")
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous(),
+             "cu_seqlens must be contiguous int32")
     T, H, C = A.shape
-    assert C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)"
+    _require(C in CHUNK_SIZES, f"chunk size {C} (16, 32 or 64)")
     nch = 0
     if chunk_indices is not None:
-        assert chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous()
+        _require(chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous(),
+                 "chunk_indices must be contiguous int32")
         nch = chunk_indices.numel() // 2
     return (_ptr(A), _dtype_code(A), _ptr(X), _dtype_code(X), _ptr(cu_seqlens),
             cu_seqlens.numel() - 1, T, H, C, _ptr(chunk_indices), nch, _ptr(workspace),
@@ -190,7 +205,7 @@ def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, al
 def kda_tril_inv_dense_chunk(A, X, chunk_size, workspace=None, algo="auto", stream=None) -> None:
     """kda_tril_inv_dense_chunk itself (any C, including 64)."""
     args = _dense_args(A, X, workspace, algo, stream)
-    assert args[7] == chunk_size
+    _require(args[7] == chunk_size, f"A's last dimension {args[7]} is not chunk_size")
     _check(_lib.kda_tril_inv_dense_chunk(*args))
 
 
@@ -198,7 +213,7 @@ def kda_tril_inv_packed_chunk(A, X, cu_seqlens, chunk_size, chunk_indices=None, 
                               algo="auto", stream=None) -> None:
     """kda_tril_inv_packed_chunk itself (any C, including 64)."""
     args = _packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream)
-    assert args[8] == chunk_size
+    _require(args[8] == chunk_size, f"A's last dimension {args[8]} is not chunk_size")
     _check(_lib.kda_tril_inv_packed_chunk(*args))
 
 
@@ -260,21 +275,26 @@ def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None
 
 def _kkt_args(k, g, beta, out, cu_seqlens, chunk_indices, stream):
     import torch
-    assert k.is_contiguous() and g.is_contiguous() and beta.is_contiguous() and out.is_contiguous()
-    assert g.dtype == torch.float32 and beta.dtype == k.dtype
+    _require(all(t.is_contiguous() for t in (k, g, beta, out)), "inputs must be contiguous")
+    _require(g.dtype == torch.float32 and beta.dtype == k.dtype,
+             "g must be float32 and beta of k's dtype")
     lead = k.shape[:-1]
     K = k.shape[-1]
-    assert g.shape == k.shape and beta.shape == lead and out.shape == lead + (64,)
+    _require(g.shape == k.shape and beta.shape == lead and out.shape == lead + (64,),
+             "shapes: k, g [.., H, K], beta [.., H], out [.., H, 64]")
     H = k.shape[-2]
     if cu_seqlens is None:
-        assert k.dim() == 4
+        _require(k.dim() == 4, "dense inputs are [B, T, H, K]")
         B, T = k.shape[0], k.shape[1]
         return (_ptr(k), _ptr(g), _ptr(beta), _dtype_code(k), _ptr(out), _dtype_code(out), B, T, H,
                 K, _stream_ptr(stream))
-    assert k.dim() == 3 and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    _require(k.dim() == 3, "packed inputs are [T, H, K]")
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous(),
+             "cu_seqlens must be contiguous int32")
     nch = 0
     if chunk_indices is not None:
-        assert chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous()
+        _require(chunk_indices.dtype == torch.int32 and chunk_indices.is_contiguous(),
+                 "chunk_indices must be contiguous int32")
         nch = chunk_indices.numel() // 2
     return (_ptr(k), _ptr(g), _ptr(beta), _dtype_code(k), _ptr(out), _dtype_code(out),
             _ptr(cu_seqlens), cu_seqlens.numel() - 1, k.shape[0], H, K, _ptr(chunk_indices), nch,
@@ -320,16 +340,22 @@ def kkt_tril_inv(k, g, beta, cu_seqlens=None, out_dtype=None, chunk_indices=None
 def _decode_args(qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out, eps_l2,
                  eps_norm, stream):
     import torch
-    for t in (qkv, z, g, beta, norm_w, conv_w, slot, state, conv_state, out):
-        assert t.is_contiguous()
-    assert z.dtype == qkv.dtype and slot.dtype == torch.int32
-    for t in (g, beta, norm_w, conv_w, state, conv_state):
-        assert t.dtype == torch.float32
+    _require(all(t.is_contiguous() for t in (qkv, z, g, beta, norm_w, conv_w, slot, state,
+                                              conv_state, out)), "inputs must be contiguous")
+    _require(z.dtype == qkv.dtype and slot.dtype == torch.int32,
+             "z must have qkv's dtype and slot must be int32")
+    _require(all(t.dtype == torch.float32 for t in (g, beta, norm_w, conv_w, state, conv_state)),
+             "g, beta, norm_w, conv_w, state and conv_state must be float32")
+    _require(qkv.dim() == 4 and conv_w.dim() == 4, "qkv is [B, 3, H, d], conv_w [3, W, H, d]")
     B, three, H, d = qkv.shape
     W = conv_w.shape[1]
-    assert three == 3 and z.shape == (B, H, d) and g.shape == (B, H, d) and beta.shape == (B, H)
-    assert conv_w.shape == (3, W, H, d) and state.shape[1:] == (H, d, d)
-    assert conv_state.shape == (state.shape[0], 3, H, W - 1, d) and out.shape == (B, H, d)
+    _require(three == 3 and z.shape == (B, H, d) and g.shape == (B, H, d) and
+             beta.shape == (B, H) and norm_w.shape == (d,) and slot.shape == (B,),
+             "shapes: z, g [B, H, d], beta [B, H], norm_w [d], slot [B]")
+    _require(conv_w.shape == (3, W, H, d) and state.dim() == 4 and state.shape[1:] == (H, d, d),
+             "shapes: conv_w [3, W, H, d], state [slots, H, d, d]")
+    _require(conv_state.shape == (state.shape[0], 3, H, W - 1, d) and out.shape == (B, H, d),
+             "shapes: conv_state [slots, 3, H, W - 1, d], out [B, H, d]")
     return (_ptr(qkv), _ptr(z), _dtype_code(qkv), _ptr(g), _ptr(beta), _ptr(norm_w),
             _ptr(conv_w), _ptr(slot), _ptr(state), _ptr(conv_state), state.shape[0], _ptr(out),
             _dtype_code(out), B, H, d, W, float(eps_l2), float(eps_norm), _stream_ptr(stream))
