@@ -178,7 +178,7 @@ struct SliceSrc {
 // together.
 template <class EK>
 __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[4],
-                                               const u4 (&graw)[4], int pI, int pJ,
+                                               const u4 (&graw)[4], const f4 &wsel,
                                                f4 (&acc)[4][4]) {
     f4 gl[4], gr[4];
 #pragma unroll
@@ -188,13 +188,18 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
 #pragma unroll
         for (int s = 0; s < 4; ++s) gr[b][s] = row_bcast<0>(gl[b][s]);
     }
-    // c for this lane's pair; every pair's c reaches the row by broadcast
+    // c for this lane's pair (I, J), every pair's c reaching the row by
+    // broadcast: the exponent gr[I] - gr[J] as sum_b wsel[b] gr[b] with
+    // wsel[b] = [b == I] - [b == J], which for finite decays is that
+    // difference bit for bit (the zero terms add exact zeros, the two others
+    // round once); a select on the lane's pair compiled to divergent branches.
     f4 cv;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const float hi = pI == 1 ? gr[1][s] : pI == 2 ? gr[2][s] : gr[3][s];
-        const float lo = pJ == 0 ? gr[0][s] : pJ == 1 ? gr[1][s] : gr[2][s];
-        cv[s] = __builtin_amdgcn_exp2f(hi - lo);
+        float a = wsel[0] * gr[0][s];
+#pragma unroll
+        for (int b = 1; b < 4; ++b) a = __builtin_fmaf(wsel[b], gr[b][s], a);
+        cv[s] = __builtin_amdgcn_exp2f(a);
     }
     f4 P[4];
     // all ten products, also for blocks past a partial chunk (their P and Q
@@ -219,7 +224,7 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
 }
 
 template <class EK>
-__device__ __forceinline__ void accumulate_slice(const Slice<EK> &sl, int pI, int pJ,
+__device__ __forceinline__ void accumulate_slice(const Slice<EK> &sl, const f4 &wsel,
                                                  f4 (&acc)[4][4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -230,7 +235,7 @@ __device__ __forceinline__ void accumulate_slice(const Slice<EK> &sl, int pI, in
             kr[b] = sl.k[b][t];
             graw[b] = sl.g[b][t];
         }
-        accumulate_sub<EK>(kr, graw, pI, pJ, acc);
+        accumulate_sub<EK>(kr, graw, wsel, acc);
     }
 }
 
@@ -266,6 +271,9 @@ __device__ __forceinline__ void build_blocks(const KktViews<EK> &v, int K, int l
     const int pn = n < 6 ? n : 0;
     const int pI = pn == 0 ? 1 : pn < 3 ? 2 : 3;
     const int pJ = pn == 0 || pn == 1 || pn == 3 ? 0 : pn == 2 || pn == 4 ? 1 : 2;
+    f4 wsel;  // +1 at block I, -1 at block J of this lane's pair
+#pragma unroll
+    for (int b = 0; b < 4; ++b) wsel[b] = (float)((b == pI) - (b == pJ));
     // Each iteration issues all loads of a 32-channel slice (whole lines)
     // before any use; other wavefronts cover their latency.
 #pragma unroll 1
@@ -273,7 +281,7 @@ __device__ __forceinline__ void build_blocks(const KktViews<EK> &v, int K, int l
         Slice<EK> sl;
         src.load(sl, d0, d0 + 32 > K);
         __builtin_amdgcn_sched_barrier(0);
-        accumulate_slice<EK>(sl, pI, pJ, acc);
+        accumulate_slice<EK>(sl, wsel, acc);
     }
     // -beta of this lane's row in each block row; strictly-lower mask on the
     // diagonal blocks (column 4g + s < row n), by select
