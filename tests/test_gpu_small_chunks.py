@@ -228,6 +228,30 @@ def test_full_workload(kt, name):
     assert gh.residual_chunks(A64, got, pick) <= gh.RESIDUAL_TOL
 
 
+@pytest.mark.parametrize("name", ["packed_16x512_h64_c16_f32", "packed_16x512_h64_c32_f32"])
+def test_bench_launch_configuration(kt, name):
+    """The launch pattern the benchmark times: calls prepared once per buffer
+    set and issued back to back over rotating sets with no synchronisation;
+    every set's X against the oracle."""
+    print(f"\n[small] bench configuration {name}", flush=True)
+    cfg = dict(synth.CONFIGS[name])
+    sets = []
+    for i in range(3):
+        c = dict(cfg)
+        c["seed"] = cfg["seed"] + 100 * i
+        d = synth.make(c)
+        A = _dev(d["A"])
+        sets.append((d, A, torch.empty_like(A)))
+    cu = torch.from_numpy(sets[0][0]["cu_seqlens"]).to(DEV)
+    calls = [kt.prepare_packed(A, X, cu) for _, A, X in sets]
+    for i in range(9):
+        calls[i % 3]()
+    torch.cuda.synchronize()
+    for d, _, X in sets:
+        e = gh.excess(gh.to_numpy_f64(X), oracle.tril_inv_packed(d["A"], d["cu_seqlens"]), "f32")
+        assert e <= 0, f"seed {d['seed']}: exceeds tolerance by {e:.3g}"
+
+
 @pytest.mark.parametrize("C", SIZES)
 def test_graph_capture_replay(kt, C):
     """A captured call replays correctly several times, with eager work and
