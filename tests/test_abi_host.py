@@ -302,3 +302,40 @@ def test_binding_refuses_host_tensors_and_bad_shapes(kt):
         kt.kda_decode_step(**dec)
     with pytest.raises(ValueError, match="norm_w"):
         kt.kda_decode_step(**dict(dec, norm_w=torch.zeros((H, d))))
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "kda_tril.h"
+
+int main(void) {
+    size_t bytes = 0;
+    kda_algo chosen = KDA_ALGO_AUTO;
+    kda_status s = kda_tril_inv_workspace_size(8192, 16, 0, 64, KDA_ALGO_SPLIT, &bytes, &chosen);
+    printf("%d %zu %d %s\n", (int)s, bytes, (int)chosen, kda_status_string(s));
+    return s == KDA_OK ? 0 : 1;
+}
+"""
+
+
+def test_header_serves_a_plain_c_caller(kt, tmp_path):
+    """include/kda_tril.h compiles as C11 (no C++ needed), and a C program
+    linked against the library makes a host-only call through it."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are missing")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(kt.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror=implicit-function-declaration",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe), "-L", libdir,
+                    "-lkda_tril", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out[0] == "0" and out[3] == "KDA_OK"
+    want_bytes, want_algo = kt.kda_tril_inv_workspace_size(8192, 16, 0, 64, "split")
+    assert int(out[1]) == want_bytes
+    assert kt.ALGO_NAMES[int(out[2])] == want_algo
