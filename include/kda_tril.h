@@ -256,7 +256,8 @@ kda_status kda_kkt_dense(const void *k, const float *g, const void *beta, kda_dt
  *   state       [num_slots, H, d, d] FP32, updated in place (16-byte aligned).
  *   conv_state  [num_slots, 3, H, W - 1, d] FP32, updated in place.
  *   out         [B, H, d] of out_dtype.
- * head_dim must be 128 and 2 <= conv_width <= 4 (else KDA_ERR_UNSUPPORTED);
+ * head_dim must be 128, 2 <= conv_width <= 4 and B x H < 2^24 (one workgroup
+ * of 256 threads per sequence and head), else KDA_ERR_UNSUPPORTED;
  * eps_l2, eps_norm must be finite and >= 0. out must not overlap the state
  * pools. B = 0 is a no-op.
  */

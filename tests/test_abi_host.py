@@ -256,6 +256,7 @@ def test_decode_argument_validation(kt):
     E, U = kt.KDA_ERR_INVALID_ARG, kt.KDA_ERR_UNSUPPORTED
     assert _dec(kt, d=64) == U
     assert _dec(kt, W=1) == U and _dec(kt, W=5) == U
+    assert _dec(kt, B=1 << 23, H=2) == U and _dec(kt, B=1 << 24, H=1) == U  # grid past 2^32 threads
     assert _dec(kt, ind=3) == E and _dec(kt, outd=-1) == E
     assert _dec(kt, H=0) == E and _dec(kt, B=-1) == E and _dec(kt, ns=-1) == E
     assert _dec(kt, ns=0) == E

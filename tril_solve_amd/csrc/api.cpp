@@ -354,7 +354,9 @@ kda_status kda_decode_step(const void *qkv, const void *z, kda_dtype in_dtype, c
     if (!(eps_l2 >= 0.0f) || !(eps_norm >= 0.0f) || eps_l2 > 1e30f || eps_norm > 1e30f)
         return KDA_ERR_INVALID_ARG;  // negative, NaN or infinite
     if (head_dim != 128 || conv_width < 2 || conv_width > 4) return KDA_ERR_UNSUPPORTED;
-    if (B > INT32_MAX / H || num_slots > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    // one workgroup of 256 threads per (sequence, head): the launch must stay
+    // below 2^32 threads
+    if (B > (int64_t)(UINT32_MAX / 256) / H || num_slots > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (B == 0) return KDA_OK;
     if (num_slots == 0) return KDA_ERR_INVALID_ARG;
     if (!qkv || !z || !g || !beta || !norm_w || !conv_w || !slot || !state || !conv_state || !out)
