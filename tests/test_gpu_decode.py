@@ -178,12 +178,15 @@ def test_graph_capture_replay(kt):
         assert torch.equal(d["conv_state"], twin["conv_state"])
 
 
-def test_bench_launch_configuration(kt):
+@pytest.mark.parametrize("B", [8, 32])
+def test_bench_launch_configuration(kt, B):
     """Prepared calls over rotating state pools (one per layer), back to
-    back with no synchronisation, as the benchmark times them."""
-    sets = [synth.decode_inputs(8, 32, seed=130 + i, in_dtype="bf16") for i in range(3)]
+    back with no synchronisation, as the benchmark times them (B = 32 is the
+    benchmark's largest batch)."""
+    print(f"\n[decode] bench configuration B={B}", flush=True)
+    sets = [synth.decode_inputs(B, 32, seed=130 + B + i, in_dtype="bf16") for i in range(3)]
     devs = [_dev(s) for s in sets]
-    outs = [torch.empty((8, 32, 128), dtype=torch.bfloat16, device=DEV) for _ in sets]
+    outs = [torch.empty((B, 32, 128), dtype=torch.bfloat16, device=DEV) for _ in sets]
     calls = [kt.prepare_decode(d["qkv"], d["z"], d["g"], d["beta"], d["norm_w"], d["conv_w"],
                                d["slot"], d["state"], d["conv_state"], o)
              for d, o in zip(devs, outs)]
