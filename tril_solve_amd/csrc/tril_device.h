@@ -218,14 +218,28 @@ struct Chunk {
     int32_t len;    // valid rows, 1..C (0: nothing to do)
 };
 
-// wave-wide inclusive prefix sum of an int
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+// Wave-wide inclusive prefix sum of an int, on DPP lane moves (no LDS round
+// trips): a Hillis-Steele scan inside each 16-lane row (row_shr by 1, 2, 4,
+// 8; lanes shifted in from outside the row read 0), then the last lane of
+// row 0 / 2 is added to row 1 / 3 (row_bcast:15) and the last lane of row 1
+// to rows 2 and 3 (row_bcast:31). Lanes a move does not write keep 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += dpp_or_zero<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_or_zero<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_or_zero<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_or_zero<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
+}
+
+// Value of v in lane `src` (wave-uniform) for the whole wave.
+__device__ __forceinline__ int lane_value(int v, int src) {
+    return __builtin_amdgcn_readlane(v, src);
 }
 
 // Resolve chunk slot k (wave-uniform) to rows of A/X for chunks of C tokens.
@@ -262,15 +276,15 @@ __device__ __forceinline__ Chunk resolve_chunk(const Problem &p, int k, int lane
                 e0 = p.cu[s + 1];
                 cnt = e0 > b0 ? (e0 - b0 + C - 1) / C : 0;
             }
-            const int incl = wave_incl_scan(cnt, lane);
-            const int total = __shfl(incl, kWave - 1, kWave);
+            const int incl = wave_incl_scan(cnt);
+            const int total = lane_value(incl, kWave - 1);
             if (k < base + total) {
                 const bool hit = (k >= base + incl - cnt) && (k < base + incl);
                 const unsigned long long m = __ballot(hit);
                 const int src = __builtin_ctzll(m);
-                const int first = base + __shfl(incl - cnt, src, kWave);
-                bos = __shfl(b0, src, kWave) + (k - first) * C;
-                eos = __shfl(e0, src, kWave);
+                const int first = base + lane_value(incl - cnt, src);
+                bos = lane_value(b0, src) + (k - first) * C;
+                eos = lane_value(e0, src);
                 found = true;
                 break;
             }

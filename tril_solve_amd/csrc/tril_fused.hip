@@ -158,10 +158,8 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 
 template <class K>
 static hipError_t launch_walk(K kernel, const Problem &p, hipStream_t stream) {
-    const long waves = (long)p.slots * p.heads;
-    const long need = (waves + kFusedWaves - 1) / kFusedWaves;
-    const long cap = resident_blocks(reinterpret_cast<const void *>(kernel), kFusedThreads);
-    const long blocks = cap > 0 && cap < need ? cap : need;
+    const long blocks = walk_blocks(reinterpret_cast<const void *>(kernel),
+                                    (long)p.slots * p.heads, min_chunks(p, kChunk) * p.heads);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
 }

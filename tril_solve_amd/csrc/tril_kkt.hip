@@ -383,10 +383,9 @@ __global__ __launch_bounds__(kFusedThreads) void tril_kkt(KktProblem q) {
 
 template <class Kern>
 static hipError_t launch_kkt_kernel(Kern kernel, const KktProblem &q, hipStream_t stream) {
-    const long waves = (long)q.p.slots * q.p.heads;
-    const long need = (waves + kFusedWaves - 1) / kFusedWaves;
-    const long cap = resident_blocks(reinterpret_cast<const void *>(kernel), kFusedThreads);
-    const long blocks = cap > 0 && cap < need ? cap : need;
+    const long blocks = walk_blocks(reinterpret_cast<const void *>(kernel),
+                                    (long)q.p.slots * q.p.heads,
+                                    min_chunks(q.p, kChunk) * q.p.heads);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, q);
     return hipGetLastError();
 }

@@ -54,8 +54,20 @@ constexpr int kFusedWaves = 4;  // independent wavefronts per workgroup
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
 // Workgroups of `threads` threads of kernel `fn` that the current device
-// holds at once (occupancy x compute units); 0 when unknown. Cached.
+// holds at once (occupancy x compute units; KDA_TRIL_BLOCKS_PER_CU, when set,
+// replaces the occupancy); 0 when unknown. Cached.
 long resident_blocks(const void *fn, int threads);
+
+// Grid of a grid-stride kernel with kFusedWaves independent wavefronts per
+// workgroup and at most `waves` wavefront work items (at least `min_waves` of
+// them real; the rest are chunk slots past the last chunk, which end after
+// the lookup): one wavefront per item, capped at what the device holds at
+// once, the wavefronts then walking the items in rounds. When the device
+// holds b workgroups per compute unit, b - 1 is used instead if that leaves
+// fewer idle wavefront slots in the last round and still 16 or more
+// wavefronts per CU: wavefronts with one item fewer than the rest leave the
+// memory system with fewer requests in flight while the others finish.
+long walk_blocks(const void *fn, long waves, long min_waves);
 
 // Element-type codes of A and X: the kda_dtype values (0 f32, 1 bf16, 2 f16).
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
@@ -67,6 +79,14 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
 hipError_t launch_kkt(const KktProblem &q, bool solve, int k_dt, int x_dt, hipStream_t stream);
 // One decode step of the fused KDA decode core.
 hipError_t launch_decode(const DecodeProblem &p, int in_dt, int out_dt, hipStream_t stream);
+
+// Lower bound on the chunks of a call with chunks of C tokens: exact for the
+// dense layout and for a caller chunk map (p.slots); for packed inputs without
+// a map, every chunk holds at most C tokens.
+inline long min_chunks(const Problem &p, int C) {
+    if (p.cu != nullptr && p.cmap == nullptr) return ((long)p.total_tokens + C - 1) / C;
+    return p.slots;
+}
 
 // Calls f.template operator()<EI, EO>() for the element types of the codes.
 template <class EF32, class EBF16, class EF16, class F>

@@ -228,20 +228,19 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
 // ------------------------------------------------------------------ launch
 
 template <class K>
-static hipError_t launch_groups(K kernel, const Problem &p, int heads_per_wave,
+static hipError_t launch_groups(K kernel, const Problem &p, int chunk, int heads_per_wave,
                                 hipStream_t stream) {
     const long groups = (p.heads + heads_per_wave - 1) / heads_per_wave;
-    const long need = ((long)p.slots * groups + kFusedWaves - 1) / kFusedWaves;
-    const long cap = resident_blocks(reinterpret_cast<const void *>(kernel), kFusedThreads);
-    const long blocks = cap > 0 && cap < need ? cap : need;
+    const long blocks = walk_blocks(reinterpret_cast<const void *>(kernel), (long)p.slots * groups,
+                                    min_chunks(p, chunk) * groups);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream) {
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
-        if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, kHeads16, stream);
-        if (chunk == 32) return launch_groups(tril_inv_c32<EI, EO>, p, kHeads32, stream);
+        if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, 16, kHeads16, stream);
+        if (chunk == 32) return launch_groups(tril_inv_c32<EI, EO>, p, 32, kHeads32, stream);
         return hipErrorInvalidValue;
     });
 }
