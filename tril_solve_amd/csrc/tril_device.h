@@ -385,19 +385,59 @@ __device__ __forceinline__ void diag_inverses(float *xs, const float (&arow)[16]
     wave_sync();
 }
 
-// Lane (b, i) loads row 16b + i, columns 16b..16b+15 (the row of diagonal
+// Lane (g, m) loads row 16b + m, columns 16b + 4g..16b + 4g + 3 of diagonal
+// block b into d[b], b = 0..3, so every load instruction covers 16 rows x 64
+// contiguous bytes (as the off-diagonal loads do) rather than 64 rows x 16
+// bytes. Rows past the chunk read as 0.
+template <class E>
+__device__ __forceinline__ void load_diag_blocks(f4 (&d)[4], const TileView<E> &A, int lane) {
+    const int g = lane >> 4, m = lane & 15;
+    const uint32_t off = (uint32_t)(m * A.rstride + 4 * g) * E::kBytes;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) d[b] = load4<E>(A.rows_from(16 * b), off + 16 * b * E::kBytes);
+}
+
+// load_diag_blocks' layout -> one row per lane: lane (b, i) gets row i of
+// diagonal block b, column c in arow[c]. Taking d[b] in 16-lane row g as
+// entry (g, b) of a 4 x 4 matrix (each entry a float4), this is the matrix's
+// transpose, done by lane swaps between registers without LDS:
+// v_permlane32_swap exchanges lane rows 2-3 of d[b] with lane rows 0-1 of
+// d[b + 2] (b = 0, 1), then v_permlane16_swap exchanges lane rows 1 and 3 of
+// d[b] with lane rows 0 and 2 of d[b + 1] (b = 0, 2).
+//
+// The swaps are written as instructions rather than through the compiler's
+// two-result builtins, whose second result this compiler lost (it folded the
+// swapped values of elements 1-3 away). Both registers are read and written
+// by each swap; the s_nop pairs keep two wait states around it (the hardware
+// needs them between a swap's results and their next read).
+__device__ __forceinline__ void lane_swap32(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap16(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void diag_rows_from_blocks(const f4 (&d)[4], float (&arow)[16]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float r0 = d[0][e], r1 = d[1][e], r2 = d[2][e], r3 = d[3][e];
+        lane_swap32(r0, r2);
+        lane_swap32(r1, r3);
+        lane_swap16(r0, r1);
+        lane_swap16(r2, r3);
+        arow[e] = r0;
+        arow[4 + e] = r1;
+        arow[8 + e] = r2;
+        arow[12 + e] = r3;
+    }
+}
+
+// Lane (b, i) gets row 16b + i, columns 16b..16b+15 (the row of diagonal
 // block b); rows past the chunk read as 0.
 template <class E>
 __device__ __forceinline__ void load_diag_rows(float (&arow)[16], const TileView<E> &A, int lane) {
-    const int b = lane >> 4, i = lane & 15;
-    const Rsrc r = A.rows_from(0);
-    const uint32_t off = (uint32_t)((16 * b + i) * A.rstride + 16 * b) * E::kBytes;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f4 v = load4<E>(r, off + 4 * q * E::kBytes);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) arow[4 * q + e] = v[e];
-    }
+    f4 d[4];
+    load_diag_blocks<E>(d, A, lane);
+    diag_rows_from_blocks(d, arow);
 }
 
 template <int BS, int CS>
@@ -429,16 +469,17 @@ __device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], const TileV
     }
 }
 
-// Registers of one chunk-head's input tile: the rows of the diagonal blocks
-// (load_diag_rows layout) and the six blocks below the diagonal (OPND_A).
+// Registers of one chunk-head's input tile as loaded: the diagonal blocks
+// (load_diag_blocks layout; diag_rows_from_blocks turns them into rows once
+// they have arrived) and the six blocks below the diagonal (OPND_A).
 struct Tile {
-    float arow[16];
+    f4 dg[4];
     f4 blk[4][4];  // blk[I][K] for K < I
 };
 
 template <class E>
 __device__ __forceinline__ void load_tile(Tile &t, const TileView<E> &A, int lane) {
-    load_diag_rows<E>(t.arow, A, lane);
+    load_diag_blocks<E>(t.dg, A, lane);
     load_offdiag_blocks<E>(t.blk, A, lane);
 }
 

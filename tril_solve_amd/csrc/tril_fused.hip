@@ -49,7 +49,9 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
     const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
                              ((long)it.ch.start * p.heads + it.h) * kChunk,
                          p.heads * kChunk, it.ch.len, kChunk};
-    diag_inverses(xs, t.arow, lane);
+    float arow[16];
+    diag_rows_from_blocks(t.dg, arow);
+    diag_inverses(xs, arow, lane);
     merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
 }
 
