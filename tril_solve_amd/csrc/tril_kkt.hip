@@ -32,8 +32,8 @@
 // Each product is computed transposed, D = (P_J c_IJ) Q_I^T: the MFMA
 // accumulator then holds row i of A_IJ, columns 4g..4g+3, in lane (g, i),
 // which is the layout the merge consumes (OPND_A) with no data movement.
-// The diagonal blocks go through LDS once to become the row-per-lane layout
-// of the diagonal solve.
+// The diagonal blocks reach the row-per-lane layout of the diagonal solve by
+// lane swaps between registers.
 #include "tril_device.h"
 #include "tril_launch.h"
 
@@ -207,8 +207,11 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const f4 kb = widen4<EK>(kr[b]);
-        P[b] = scaled(kb, gr[b] - gl[b]);
-        const f4 Q = scaled(kb, gl[b] - gr[b]);
+        // the two exponents are exact negations of each other: one
+        // subtraction, the second exponential takes it negated
+        const f4 t = gr[b] - gl[b];
+        P[b] = scaled(kb, t);
+        const f4 Q = scaled(kb, -t);
         acc[b][b] = mma_kq(P[b], Q, acc[b][b]);
         if (b == 1) acc[1][0] = mma_kq(P[0] * pair_factor<0>(cv), Q, acc[1][0]);
         if (b == 2) {
@@ -349,21 +352,13 @@ __global__ __launch_bounds__(kFusedThreads) void tril_kkt(KktProblem q) {
         const TileView<EO> X{static_cast<typename EO::T *>(p.X) + row0 * kChunk,
                              p.heads * kChunk, ch.len, kChunk};
         if constexpr (SOLVE) {
-            // diagonal blocks to the row-per-lane layout of the diagonal solve
-            const int g4 = lane >> 4, n = lane & 15;
-            wave_sync();
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                *reinterpret_cast<f4 *>(&xs[b * kXsBlock + n * kXsCol + 4 * g4]) = acc[b][b];
-            wave_sync();
+            // diagonal blocks to the row-per-lane layout of the diagonal solve:
+            // acc[b][b] holds row n, columns 4g..4g+3 of block b in lane (g, n),
+            // the layout diag_rows_from_blocks transposes with lane swaps
+            const f4 dg[4] = {acc[0][0], acc[1][1], acc[2][2], acc[3][3]};
             float arow[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f4 r = *reinterpret_cast<const f4 *>(&xs[g4 * kXsBlock + n * kXsCol + 4 * q4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * q4 + e] = r[e];
-            }
-            wave_sync();
+            diag_rows_from_blocks(dg, arow);
+            wave_sync();  // the previous item's last LDS reads are done
             const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
             diag_inverses(xs, arow, lane);
             merge_and_store<EO, kXsBlock, kXsCol>(eng, acc, xs, xs, X, lane);
