@@ -431,6 +431,18 @@ __device__ __forceinline__ void diag_rows_from_blocks(const f4 (&d)[4], float (&
     }
 }
 
+// Lane (b, i) loads row 16b + i, columns 16b + 4q..16b + 4q + 3 into r[q]
+// (the row of diagonal block b as four float4): one row per lane, so each of
+// the four load instructions touches 64 rows, and the rows need no transpose.
+template <class E>
+__device__ __forceinline__ void load_diag_row_quads(f4 (&r)[4], const TileView<E> &A, int lane) {
+    const int b = lane >> 4, i = lane & 15;
+    const Rsrc rs = A.rows_from(0);
+    const uint32_t off = (uint32_t)((16 * b + i) * A.rstride + 16 * b) * E::kBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = load4<E>(rs, off + 4 * q * E::kBytes);
+}
+
 // Lane (b, i) gets row 16b + i, columns 16b..16b+15 (the row of diagonal
 // block b); rows past the chunk read as 0.
 template <class E>
@@ -469,18 +481,45 @@ __device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], const TileV
     }
 }
 
-// Registers of one chunk-head's input tile as loaded: the diagonal blocks
-// (load_diag_blocks layout; diag_rows_from_blocks turns them into rows once
-// they have arrived) and the six blocks below the diagonal (OPND_A).
+// Registers of one chunk-head's input tile as loaded: the diagonal blocks and
+// the six blocks below the diagonal (OPND_A). Two layouts of the diagonal
+// blocks, chosen per launch:
+//   ROWS = false: load_diag_blocks (16 rows x 64 bytes per load instruction);
+//     diag_rows_from_blocks turns them into rows once they have arrived.
+//     Fewer lines per instruction: the faster layout when wavefronts walk
+//     several items and memory throughput decides.
+//   ROWS = true: load_diag_row_quads (one row per lane, no transpose): fewer
+//     dependent steps between the loads and the diagonal solve, the faster
+//     layout when every item has its own wavefront and latency decides.
 struct Tile {
     f4 dg[4];
     f4 blk[4][4];  // blk[I][K] for K < I
 };
 
-template <class E>
+template <class E, bool ROWS>
 __device__ __forceinline__ void load_tile(Tile &t, const TileView<E> &A, int lane) {
-    load_diag_blocks<E>(t.dg, A, lane);
+    if constexpr (ROWS)
+        load_diag_row_quads<E>(t.dg, A, lane);
+    else
+        load_diag_blocks<E>(t.dg, A, lane);
+    // the diagonal blocks are issued first, so that the diagonal solve waits
+    // for four loads and not for the ones it does not need (otherwise the
+    // compiler groups the loads by descriptor)
+    __builtin_amdgcn_sched_barrier(0);
     load_offdiag_blocks<E>(t.blk, A, lane);
+}
+
+// The diagonal rows of a loaded tile in the layout of diag_inverses.
+template <bool ROWS>
+__device__ __forceinline__ void tile_diag_rows(const Tile &t, float (&arow)[16]) {
+    if constexpr (ROWS) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) arow[4 * q + e] = t.dg[q][e];
+    } else {
+        diag_rows_from_blocks(t.dg, arow);
+    }
 }
 
 // Writes rows 16I..16I+15 of X (those inside the descriptor) through the LDS

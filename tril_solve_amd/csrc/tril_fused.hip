@@ -26,7 +26,7 @@ struct Item {
     int32_t h;
 };
 
-template <class EI>
+template <class EI, bool ROWS>
 __device__ __forceinline__ Item fetch(const Problem &p, long w, Tile &t, int lane) {
     Item it;
     const int slot = (int)(w / p.heads);
@@ -36,12 +36,12 @@ __device__ __forceinline__ Item fetch(const Problem &p, long w, Tile &t, int lan
         const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
                                  ((long)it.ch.start * p.heads + it.h) * kChunk,
                              p.heads * kChunk, it.ch.len, kChunk};
-        load_tile<EI>(t, A, opaque_lane(lane));
+        load_tile<EI, ROWS>(t, A, opaque_lane(lane));
     }
     return it;
 }
 
-template <class EI, class EO, class Eng>
+template <class EI, class EO, bool ROWS, class Eng>
 __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Tile &t, float *xs,
                                       float *stage, const Eng &eng, int lane) {
     if (it.ch.len <= 0) return;
@@ -50,7 +50,7 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
                              ((long)it.ch.start * p.heads + it.h) * kChunk,
                          p.heads * kChunk, it.ch.len, kChunk};
     float arow[16];
-    diag_rows_from_blocks(t.dg, arow);
+    tile_diag_rows<ROWS>(t, arow);
     diag_inverses(xs, arow, lane);
     merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
 }
@@ -59,19 +59,19 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
 // solving the current one was measured too: the second register tile costs
 // more occupancy than the overlap gains on MI355X, so each item is loaded
 // when its wavefront reaches it, and other wavefronts cover the latency.)
-template <class EI, class EO, class Eng>
+template <class EI, class EO, bool ROWS, class Eng>
 __device__ __forceinline__ void walk(const Problem &p, float *xs, float *stage, const Eng &eng,
                                      long w, int lane) {
     const long total = (long)p.slots * p.heads;
     const long G = (long)gridDim.x * kFusedWaves;
     for (; w < total; w += G) {
         Tile t;
-        const Item it = fetch<EI>(p, w, t, lane);
-        solve<EI, EO>(p, it, t, xs, stage, eng, lane);
+        const Item it = fetch<EI, ROWS>(p, w, t, lane);
+        solve<EI, EO, ROWS>(p, it, t, xs, stage, eng, lane);
     }
 }
 
-template <class EI, class EO>
+template <class EI, class EO, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) {
     __shared__ float lds_all[kFusedWaves * kLdsPerWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
     float *xs = lds_all + wid * kLdsPerWave;
     float *stage = xs;  // the staging reuses the diagonal-inverse region
     const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
-    walk<EI, EO>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
+    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -144,7 +144,7 @@ struct ValuEngine {
     }
 };
 
-template <class EI, class EO>
+template <class EI, class EO, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) {
     __shared__ float lds_all[kFusedWaves * kLdsPerWaveValu];
     const int lane = threadIdx.x & (kWave - 1);
@@ -153,28 +153,38 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
     float *stage = xs;
     float *ps = xs + kLdsPerWave;
     const ValuEngine eng{xs, ps, ps + 16 * kScr, lane};
-    walk<EI, EO>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
+    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
 }
 
 // ------------------------------------------------------------------ launch
 
-template <class K>
-static hipError_t launch_walk(K kernel, const Problem &p, hipStream_t stream) {
-    const long blocks = walk_blocks(reinterpret_cast<const void *>(kernel),
-                                    (long)p.slots * p.heads, min_chunks(p, kChunk) * p.heads);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
+// The throughput variant (ROWS = false) sizes the grid. When that grid gives
+// every work item its own wavefront (one round: latency decides), the
+// row-per-lane variant runs instead (same registers, same LDS).
+template <class KT, class KR>
+static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t stream) {
+    const long waves = (long)p.slots * p.heads;
+    const long blocks = walk_blocks(reinterpret_cast<const void *>(ktput), waves,
+                                    min_chunks(p, kChunk) * p.heads);
+    const bool one_round = blocks * kFusedWaves >= waves;
+    if (one_round)
+        hipLaunchKernelGGL(krows, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(ktput, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
-        return launch_walk(tril_inv_fused_mfma<EI, EO>, p, stream);
+        return launch_walk(tril_inv_fused_mfma<EI, EO, false>, tril_inv_fused_mfma<EI, EO, true>,
+                           p, stream);
     });
 }
 
 hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
-        return launch_walk(tril_inv_fused_valu<EI, EO>, p, stream);
+        return launch_walk(tril_inv_fused_valu<EI, EO, false>, tril_inv_fused_valu<EI, EO, true>,
+                           p, stream);
     });
 }
 
