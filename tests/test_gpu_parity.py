@@ -287,6 +287,34 @@ def test_dtype_matrix(kt, a_dtype, x_dtype):
         assert gh.excess(gh.to_numpy_f64(X), ref, x_dtype) <= 0, algo
 
 
+_MULTI_ROUND = {}
+
+
+@pytest.mark.parametrize("a_dtype", ["f32", "bf16", "f16"])
+def test_dtype_matrix_multi_round(kt, a_dtype):
+    """The fused kernels pick their diagonal-block load layout per launch: one
+    row per lane when every work item has its own wavefront, 16 rows per
+    instruction plus a lane-swap transpose when wavefronts walk several items.
+    The small cases above run in one round; this one has 10,240 tokens x 64
+    heads (2.5 rounds of a 256-CU MI355X at 16 wavefronts per CU), ragged
+    requests included, through every output type and both merge engines."""
+    lengths = [5000, 3000, 2240]
+    H = 64
+    if "A" not in _MULTI_ROUND:
+        _MULTI_ROUND["A"] = synth.delta_rule_A(lengths, H, seed=61)
+    A32 = _MULTI_ROUND["A"]
+    A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
+    cu = synth.cu_seqlens(lengths)
+    ref = oracle.tril_inv_packed(A, cu, a_dtype)
+    Ad = gh.to_torch_input(A, a_dtype, DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    for algo in ("fused", "fused_valu"):
+        for x_dtype in ("f32", "bf16", "f16"):
+            X = kt.tril_inv(Ad, cud, out_dtype=gh.out_torch_dtype(x_dtype), algo=algo)
+            e = gh.excess(gh.to_numpy_f64(X), ref, x_dtype)
+            assert e <= 0, f"{algo} {a_dtype}->{x_dtype}: exceeds tolerance by {e:.3g}"
+
+
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
 def test_bf16_input(kt, x_dtype):
     lengths = [200, 64, 1]

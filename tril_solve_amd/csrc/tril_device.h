@@ -483,14 +483,11 @@ __device__ __forceinline__ void load_offdiag_blocks(f4 (&blk)[4][4], const TileV
 
 // Registers of one chunk-head's input tile as loaded: the diagonal blocks and
 // the six blocks below the diagonal (OPND_A). Two layouts of the diagonal
-// blocks, chosen per launch:
+// blocks, chosen per launch by measurement (the fused kernel's launcher):
 //   ROWS = false: load_diag_blocks (16 rows x 64 bytes per load instruction);
 //     diag_rows_from_blocks turns them into rows once they have arrived.
-//     Fewer lines per instruction: the faster layout when wavefronts walk
-//     several items and memory throughput decides.
 //   ROWS = true: load_diag_row_quads (one row per lane, no transpose): fewer
-//     dependent steps between the loads and the diagonal solve, the faster
-//     layout when every item has its own wavefront and latency decides.
+//     dependent steps between the loads and the diagonal solve.
 struct Tile {
     f4 dg[4];
     f4 blk[4][4];  // blk[I][K] for K < I
