@@ -317,12 +317,17 @@ __device__ __forceinline__ void store_rows_a(const TileView<E> &X, const f4 (&bl
     const int r4 = lane >> 4, c4 = (lane & 15) * 4;
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t off = (uint32_t)(r4 * X.rstride + c4) * E::kBytes;
+    // Lanes right of the block row read column 0 of the staging (any value
+    // in the wave's LDS would do) and store zeros: the read is unconditional,
+    // so the compiler does not split each store into two partial-wave
+    // stores under exec masks (each store instruction covers four whole rows).
+    const bool in_row = c4 < 16 * (I + 1);
+    const int cs = in_row ? c4 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * i + r4;
-        f4 v = z;
-        if (c4 < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * S + c4]);
-        store4<E>(X.rows_from(16 * I + 4 * i), off, v);
+        const f4 sv = *reinterpret_cast<const f4 *>(&stage[row * S + cs]);
+        store4<E>(X.rows_from(16 * I + 4 * i), off, in_row ? sv : z);
     }
     wave_sync();
 }

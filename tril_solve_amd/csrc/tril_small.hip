@@ -62,13 +62,21 @@ __device__ __forceinline__ float col_dot(const float (&a)[16], const float (&x)[
     return acc;
 }
 
+template <int I>
+__device__ __forceinline__ float select_below(float v, float keep, int c) {
+    return (I > c) ? v : keep;
+}
+
 // Forward substitution for column c of (I + A)^-1 (rows in increasing order;
 // only rows below the diagonal are computed, so A's own diagonal and upper
 // part are never read).
 template <int... I>
 __device__ __forceinline__ void col_subst(const float (&a)[16], float (&x)[16], int c,
                                           std::integer_sequence<int, I...>) {
-    ((x[I] = (I > c) ? -col_dot<I>(a, x, std::make_integer_sequence<int, I>{}) : x[I]), ...);
+    // the dot product is taken on every lane and then selected (same bits):
+    // a conditional evaluation compiled to one exec-masked branch per row
+    ((x[I] = select_below<I>(-col_dot<I>(a, x, std::make_integer_sequence<int, I>{}), x[I], c)),
+     ...);
 }
 
 template <class EI, class EO>
@@ -142,12 +150,15 @@ __device__ __forceinline__ void store_pair_rows(const TileView<E> &X, const f4 (
     const int r4 = lane >> 4, c4 = (lane & 15) * 4;
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t off = (uint32_t)(r4 * X.rstride + c4) * E::kBytes | (c4 >= 32 ? mask_hi : 0u);
+    // unconditional staging read (lanes right of the block row read column 0
+    // and store zeros), so each store stays one full-wave instruction
+    const bool in_row = (c4 & 31) < 16 * (I + 1);
+    const int cs = in_row ? c4 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * i + r4;
-        f4 v = z;
-        if ((c4 & 31) < 16 * (I + 1)) v = *reinterpret_cast<const f4 *>(&stage[row * kStage32 + c4]);
-        store4<E>(X.rows_from(16 * I + 4 * i), off, v);
+        const f4 sv = *reinterpret_cast<const f4 *>(&stage[row * kStage32 + cs]);
+        store4<E>(X.rows_from(16 * I + 4 * i), off, in_row ? sv : z);
     }
     wave_sync();
 }
