@@ -74,11 +74,41 @@ __device__ __forceinline__ void st_elem<F16>(uint16_t *p, long i, float v) {
     p[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// Cross-lane sums on DPP moves and lane swaps (no LDS round trips; the
+// shuffle-based butterflies compiled to one ds_bpermute per step). Each step
+// adds the value of a partner lane; partners are paired both ways, so every
+// lane of a group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                                  0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;   // lane i <-> 7 - i within each 8 lanes
+constexpr int kRowMirror = 0x140;    // lane i <-> 15 - i within each 16-lane row
+constexpr int kRowRor8 = 0x128;      // lane i <-> i + 8 (mod 16) within each row
+// 16-lane rows 0 + 1 and 2 + 3, lanes at the same position in their rows
+__device__ __forceinline__ float rows_pair_add(float v) {
+    float a = v, b = v;
+    lane_swap16(a, b);
+    return a + b;
+}
+// rows 0 + 2 and 1 + 3
+__device__ __forceinline__ float rows_half_add(float v) {
+    float a = v, b = v;
+    lane_swap32(a, b);
+    return a + b;
+}
+
 // Sum over the 64 lanes of a wavefront (result in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v = dpp_add<kQuadXor1>(v);
+    v = dpp_add<kQuadXor2>(v);
+    v = dpp_add<kHalfMirror>(v);
+    v = dpp_add<kRowMirror>(v);
+    v = rows_pair_add(v);
+    return rows_half_add(v);
 }
 
 // One step for one (sequence, head); layouts as in the C ABI.
@@ -195,13 +225,11 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
         pa += s[i] * yk[r];
         pb += s[i] * yq[r];
     }
+    // sums over the eight lanes with the same l % 8 (l, l ^ 8, l ^ 16, ...)
 #pragma unroll
-    for (int o = 8; o < kWave; o <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pa[j] += __shfl_xor(pa[j], o, kWave);
-            pb[j] += __shfl_xor(pb[j], o, kWave);
-        }
+    for (int j = 0; j < 4; ++j) {
+        pa[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pa[j])));
+        pb[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pb[j])));
     }
 
     // 6. u = beta (v - S^T k), state update S += k u^T written back in place,
@@ -217,8 +245,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
 
     // 7. gated RMSNorm of o over the 128 value columns
     float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+    ss = dpp_add<kHalfMirror>(dpp_add<kQuadXor2>(dpp_add<kQuadXor1>(ss)));  // over 8 lanes
     if (l == 0) red[wv] = ss;
     __syncthreads();
     if (l < 8) {
