@@ -246,6 +246,22 @@ def test_dense_equals_packed(kt, T):
     assert torch.equal(Xs, Xd)
 
 
+def test_dense_equals_packed_multi_round(kt):
+    """The dense layout's arithmetic chunk lookup in a launch whose wavefronts
+    walk several items (B = 2, T = 5100 with a partial last chunk, 64 heads:
+    10,240 work items), against the same data through the packed scan, bit
+    for bit, for the fused and the split plans."""
+    B, T, H = 2, 5100, 64
+    A = synth.delta_rule_A([T] * B, H, seed=37)
+    Ad = torch.from_numpy(A).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens([T] * B)).to(DEV)
+    Xp = kt.tril_inv(Ad, cu, algo="fused")
+    Xd = kt.tril_inv(Ad.view(B, T, H, 64), None, algo="fused")
+    assert torch.equal(Xp.view(B, T, H, 64), Xd)
+    Xs = kt.tril_inv(Ad.view(B, T, H, 64), None, algo="split")
+    assert torch.equal(Xs, Xd)
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_bf16_output_is_rne_of_fp32_output(kt, algo):
     lengths = [512, 300, 64, 7]
