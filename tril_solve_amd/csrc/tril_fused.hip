@@ -55,6 +55,15 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
     merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
 }
 
+// Wavefronts per workgroup: four independent ones for the launches that walk
+// several items each; one for the launches in which every item has its own
+// wavefront (ROWS), so that those items spread over as many compute units as
+// possible (64 matrices: 64 CUs instead of 16).
+template <bool ROWS>
+__host__ __device__ constexpr int waves_per_block() {
+    return ROWS ? 1 : kFusedWaves;
+}
+
 // Grid-stride walk over the work items. (Loading the next tile before
 // solving the current one was measured too: the second register tile costs
 // more occupancy than the overlap gains on MI355X, so each item is loaded
@@ -63,7 +72,7 @@ template <class EI, class EO, bool ROWS, class Eng>
 __device__ __forceinline__ void walk(const Problem &p, float *xs, float *stage, const Eng &eng,
                                      long w, int lane) {
     const long total = (long)p.slots * p.heads;
-    const long G = (long)gridDim.x * kFusedWaves;
+    const long G = (long)gridDim.x * waves_per_block<ROWS>();
     for (; w < total; w += G) {
         Tile t;
         const Item it = fetch<EI, ROWS>(p, w, t, lane);
@@ -73,13 +82,13 @@ __device__ __forceinline__ void walk(const Problem &p, float *xs, float *stage, 
 
 template <class EI, class EO, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) {
-    __shared__ float lds_all[kFusedWaves * kLdsPerWave];
+    __shared__ float lds_all[waves_per_block<ROWS>() * kLdsPerWave];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wid = ROWS ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *xs = lds_all + wid * kLdsPerWave;
     float *stage = xs;  // the staging reuses the diagonal-inverse region
     const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
-    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
+    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * waves_per_block<ROWS>() + wid, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -146,14 +155,14 @@ struct ValuEngine {
 
 template <class EI, class EO, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) {
-    __shared__ float lds_all[kFusedWaves * kLdsPerWaveValu];
+    __shared__ float lds_all[waves_per_block<ROWS>() * kLdsPerWaveValu];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wid = ROWS ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *xs = lds_all + wid * kLdsPerWaveValu;
     float *stage = xs;
     float *ps = xs + kLdsPerWave;
     const ValuEngine eng{xs, ps, ps + 16 * kScr, lane};
-    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * kFusedWaves + wid, lane);
+    walk<EI, EO, ROWS>(p, xs, stage, eng, (long)blockIdx.x * waves_per_block<ROWS>() + wid, lane);
 }
 
 // ------------------------------------------------------------------ launch
@@ -172,8 +181,8 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
     const long blocks = walk_blocks(reinterpret_cast<const void *>(ktput), waves,
                                     min_chunks(p, kChunk) * p.heads);
     const bool one_round = blocks * kFusedWaves >= waves;
-    if (one_round)
-        hipLaunchKernelGGL(krows, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
+    if (one_round)  // one item per workgroup of one wavefront
+        hipLaunchKernelGGL(krows, dim3((unsigned)waves), dim3(kWave), 0, stream, p);
     else
         hipLaunchKernelGGL(ktput, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
