@@ -163,7 +163,7 @@ __device__ __forceinline__ void store_pair_rows(const TileView<E> &X, const f4 (
     wave_sync();
 }
 
-template <class EI, class EO>
+template <class EI, class EO, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
     __shared__ float lds_all[kFusedWaves * kLdsPerWave];
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -189,21 +189,32 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
         const uint32_t mask_hi = hv > 1 ? 0u : kOffMasked;  // second head missing
 
         // Diagonal rows: lane (b, i), b = 2m + d, holds row 16d + i, columns
-        // 16d..16d+15 of head m (block d of head m goes to LDS block b).
-        float arow[16];
-        {
+        // 16d..16d+15 of head m (block d of head m goes to LDS block b). As in
+        // the 64-token kernel, launches in which wavefronts walk several items
+        // load each block as 16 rows x 64 bytes per instruction and transpose
+        // with lane swaps (ROWS = false); one-round launches load one row per
+        // lane (ROWS = true).
+        f4 dgb[4];
+        if constexpr (ROWS) {
             const int b = lane >> 4, i = lane & 15, m = b >> 1, d = b & 1;
             const uint32_t off =
                 (uint32_t)((16 * d + i) * rstride + 32 * m + 16 * d) * EI::kBytes |
                 (m > 0 ? mask_hi : 0u);
             const Rsrc r = A.rows_from(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4 v = load4<EI>(r, off + 4 * q * EI::kBytes);
+            for (int q = 0; q < 4; ++q) dgb[q] = load4<EI>(r, off + 4 * q * EI::kBytes);
+        } else {
+            const int g = lane >> 4, mr = lane & 15;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * q + e] = v[e];
+            for (int b = 0; b < 4; ++b) {
+                const int m = b >> 1, d = b & 1;
+                const uint32_t off =
+                    (uint32_t)(mr * rstride + 32 * m + 16 * d + 4 * g) * EI::kBytes |
+                    (m > 0 ? mask_hi : 0u);
+                dgb[b] = load4<EI>(A.rows_from(16 * d), off);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);  // diagonal loads first
         // A_10 of both heads in OPND_A layout (row 16 + m', columns 4g..4g+3)
         f4 a10[2];
         {
@@ -214,6 +225,15 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
             a10[1] = load4<EI>(r, (off + 32 * EI::kBytes) | mask_hi);
         }
 
+        float arow[16];
+        if constexpr (ROWS) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * q + e] = dgb[q][e];
+        } else {
+            diag_rows_from_blocks(dgb, arow);
+        }
         diag_inverses(xs, arow, lane);
         // Everything the merge needs from the diagonal copies is read into
         // registers before the first staging, which reuses the same LDS.
@@ -251,7 +271,18 @@ static hipError_t launch_groups(K kernel, const Problem &p, int chunk, int heads
 hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream) {
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
         if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, 16, kHeads16, stream);
-        if (chunk == 32) return launch_groups(tril_inv_c32<EI, EO>, p, 32, kHeads32, stream);
+        if (chunk == 32) {
+            // the ROWS = false variant sizes the grid; one-round launches run
+            // the row-per-lane variant
+            const long groups = (p.heads + kHeads32 - 1) / kHeads32;
+            const long items = (long)p.slots * groups;
+            const long blocks =
+                walk_blocks(reinterpret_cast<const void *>(tril_inv_c32<EI, EO, false>), items,
+                            min_chunks(p, 32) * groups);
+            if (blocks * kFusedWaves >= items)
+                return launch_groups(tril_inv_c32<EI, EO, true>, p, 32, kHeads32, stream);
+            return launch_groups(tril_inv_c32<EI, EO, false>, p, 32, kHeads32, stream);
+        }
         return hipErrorInvalidValue;
     });
 }
