@@ -139,18 +139,23 @@ __device__ __forceinline__ f4 load4<F16>(Rsrc r, uint32_t off) {
     return o;
 }
 
-// float4 -> four consecutive elements at byte offset `off`, as a nontemporal
-// store (X is written once and not read again here, so it should not displace
-// cached lines); dropped past the descriptor's range. bf16 uses the hardware
-// round to nearest even (v_cvt_pk_bf16_f32), binary16 the IEEE conversion in
-// the default round-to-nearest-even mode.
-constexpr int kNontemporal = 2;  // cache-policy bit of buffer stores
+// float4 -> four consecutive elements at byte offset `off`; dropped past the
+// descriptor's range. X is written once and never read again here: the stores
+// carry the nontemporal bit and device scope, so the lines go out through L2
+// without displacing cached lines (on 16 x 512 tokens, 64 heads: 1.6% faster
+// than nontemporal alone, 4% faster than the default write-back policy; device
+// scope alone was no better than the default). bf16 uses the hardware round
+// to nearest even (v_cvt_pk_bf16_f32), binary16 the IEEE conversion in the
+// default round-to-nearest-even mode.
+constexpr int kNontemporal = 2;   // cache-policy bit: nontemporal (loads and stores)
+constexpr int kScopeDevice = 16;  // cache-policy bit: device scope
+constexpr int kStorePolicy = kScopeDevice | kNontemporal;
 template <class E>
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, f4 v);
 template <>
 __device__ __forceinline__ void store4<F32>(Rsrc r, uint32_t off, f4 v) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kStorePolicy);
 }
 template <>
 __device__ __forceinline__ void store4<BF16>(Rsrc r, uint32_t off, f4 v) {
@@ -159,7 +164,7 @@ __device__ __forceinline__ void store4<BF16>(Rsrc r, uint32_t off, f4 v) {
     const b2 lo = {(__bf16)v[0], (__bf16)v[1]};
     const b2 hi = {(__bf16)v[2], (__bf16)v[3]};
     const u2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-    __builtin_amdgcn_raw_buffer_store_b64(o, r, off, 0, kNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(o, r, off, 0, kStorePolicy);
 }
 template <>
 __device__ __forceinline__ void store4<F16>(Rsrc r, uint32_t off, f4 v) {
@@ -168,7 +173,7 @@ __device__ __forceinline__ void store4<F16>(Rsrc r, uint32_t off, f4 v) {
     h4 h;
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];  // v_cvt_f16_f32, round to nearest even
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, h), r, off, 0, kNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, h), r, off, 0, kStorePolicy);
 }
 
 // Single elements, for the kernels that give every lane one column of a
@@ -193,17 +198,17 @@ __device__ __forceinline__ void store1(Rsrc r, uint32_t off, float v);
 template <>
 __device__ __forceinline__ void store1<F32>(Rsrc r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0,
-                                          kNontemporal);
+                                          kStorePolicy);
 }
 template <>
 __device__ __forceinline__ void store1<BF16>(Rsrc r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, 0,
-                                          kNontemporal);
+                                          kStorePolicy);
 }
 template <>
 __device__ __forceinline__ void store1<F16>(Rsrc r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), r, off, 0,
-                                          kNontemporal);
+                                          kStorePolicy);
 }
 
 // Byte offset that is out of range of every descriptor above (their ranges
