@@ -236,19 +236,10 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     //    o = S^T q + (k . q) u
     const f4 v4 = *reinterpret_cast<const f4 *>(&yv[col]);
     const f4 u = beta * (v4 - pa * sk);
-    // written back through a buffer descriptor over this (slot, head)'s 64 KiB
-    // state block, with the solver's store policy (nontemporal, device scope)
-    {
-        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-        float *Sblock = p.state + ((long)slot * p.H + h) * kDecD * kDecD;  // wave-uniform
-        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(Sblock, 0, kDecD * kDecD * 4, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < kDecRows; ++i) {
-            const float ki = yk[pad_row(row0 + i)] * sk;
-            const uint32_t off = (uint32_t)((row0 + i) * kDecD + col) * 4u;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, s[i] + ki * u), rs, off, 0,
-                                                   kStorePolicy);
-        }
+    for (int i = 0; i < kDecRows; ++i) {
+        const float ki = yk[pad_row(row0 + i)] * sk;
+        __builtin_nontemporal_store(s[i] + ki * u, reinterpret_cast<f4 *>(&S[(long)(row0 + i) * kDecD]));
     }
     const f4 o = pb * sq + (dqk * sq * sk) * u;
 
