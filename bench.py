@@ -397,7 +397,13 @@ class CopyProbe:
         return 0
 
 
-def base_line(args, el, k_avg, dist, mats, bytes_alg, nsets, metric, vs_baseline, config):
+def base_line(args, el, k_avg, dist, mats, bytes_alg, nsets, metric, vs_baseline, config,
+              io_dtype):
+    """The JSON line's common fields. `dtype` is the arithmetic type of every
+    kernel (FP32); `io_dtype` names the element types of the inputs and the
+    output. roofline.achieved counts algorithmic bytes (what the operation
+    must move by definition); the measured HBM rate, from the committed
+    counter summary, is added by with_measured_hbm."""
     achieved = bytes_alg / k_avg / 1e9
     return {
         "metric": metric,
@@ -411,14 +417,27 @@ def base_line(args, el, k_avg, dist, mats, bytes_alg, nsets, metric, vs_baseline
         "scaling": "weak",
         "vs_baseline": vs_baseline,
         "dtype": "f32",
+        "io_dtype": io_dtype,
         "data": f"synthetic (seeded delta-rule generator, {nsets} rotating buffer sets)",
         "config": config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes": "algorithmic"},
         "kernel_us_avg": k_avg * 1e6,
         "kernel_us_per_launch": dist,
         "algorithmic_bytes_per_launch": bytes_alg,
     }
+
+
+def with_measured_hbm(out, traffic):
+    """Sets roofline.traffic and, when it is known, the HBM rate the kernel
+    achieves in measured bytes (counter bytes per launch / kernel time)."""
+    out["roofline"]["traffic"] = traffic
+    if traffic:
+        gbs = traffic / (out["kernel_us_avg"] * 1e-6) / 1e9
+        out["hbm_measured"] = {"bytes_per_launch": traffic, "achieved": gbs,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    return out
 
 
 def run_solve(args, torch, np, dev, stream):
@@ -494,9 +513,10 @@ def run_solve(args, torch, np, dev, stream):
                      "requests": len(d0["lengths"]), "matrices": mats,
                      "a_dtype": cfg["a_dtype"], "x_dtype": cfg["x_dtype"],
                      "algo": args.algo, "plan": chosen,
-                     "chunks_from": "caller chunk map" if cmap is not None else "cu_seqlens scan"})
+                     "chunks_from": "caller chunk map" if cmap is not None else "cu_seqlens scan"},
+                    f"{cfg['a_dtype']} A -> {cfg['x_dtype']} X")
     if args.algo in ("auto", "fused") and chosen == "fused":
-        out["roofline"]["traffic"] = load_traffic(args.workload)
+        with_measured_hbm(out, load_traffic(args.workload))
     out["copy_roofline_gbs"] = copy_gbs
     if not args.no_cpu_baseline and args.workload == MAIN_WORKLOAD:
         log("timing the CPU oracle ...")
@@ -565,8 +585,9 @@ def run_kkt(args, torch, np, dev, stream):
                     f"(K={K}) + achieved HBM GB/s (% peak)", None,
                     {"workload": describe(d0), "tokens": T, "heads": H, "key_dim": K,
                      "requests": len(d0["lengths"]), "matrices": mats,
-                     "k_dtype": cfg["k_dtype"], "x_dtype": cfg["x_dtype"], "plan": "fused"})
-    out["roofline"]["traffic"] = load_traffic(args.workload)
+                     "k_dtype": cfg["k_dtype"], "x_dtype": cfg["x_dtype"], "plan": "fused"},
+                    f"{cfg['k_dtype']} k and beta, f32 g -> {cfg['x_dtype']} X")
+    with_measured_hbm(out, load_traffic(args.workload))
     out["mfma_fp32"] = {"tflops": flops / k_avg / 1e12, "peak": MFMA_F32_PEAK_TFLOPS,
                         "frac": flops / k_avg / 1e12 / MFMA_F32_PEAK_TFLOPS}
     out["unfused_pair_us_avg"] = pair_avg * 1e6
@@ -639,9 +660,10 @@ def run_decode(args, torch, np, dev, stream):
                                  f"{W}, {cfg['in_dtype']} activations -> {cfg['out_dtype']} "
                                  f"output, FP32 state pools of {cfg['slots']} slots",
                      "batch": B, "heads": H, "head_dim": d, "conv_width": W,
-                     "in_dtype": cfg["in_dtype"], "out_dtype": cfg["out_dtype"]})
+                     "in_dtype": cfg["in_dtype"], "out_dtype": cfg["out_dtype"]},
+                    f"{cfg['in_dtype']} activations, f32 state -> {cfg['out_dtype']} output")
     out["unit"] = "sequences/s"
-    out["roofline"]["traffic"] = load_traffic(args.workload)
+    with_measured_hbm(out, load_traffic(args.workload))
     # the same steps captured once in a HIP graph (one per pool) and replayed
     out["graph_replay_us_per_launch"] = {"avg": graph_avg, "median_of_replays": graph_median}
     out["pages_gfx950_fused_us_context"] = DECODE_PAGES_US.get(B)

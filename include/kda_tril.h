@@ -113,7 +113,9 @@ typedef enum {
  *                      *bytes bytes would run (AUTO resolved).
  * The SPLIT workspace is 4 tiles x 16 x 16 FP32 = 4096 bytes per chunk-head.
  * Returns KDA_ERR_WORKSPACE when SPLIT is forced but ineligible (its scratch
- * would exceed the FP32 input size).
+ * would exceed the FP32 input size). A call that runs SPLIT returns
+ * KDA_ERR_INVALID_ARG when the workspace is not 16-byte aligned or overlaps A
+ * or X.
  */
 kda_status kda_tril_inv_workspace_size(int64_t total_tokens, int64_t num_seqs,
                                        int64_t num_chunks, int32_t num_heads, kda_algo algo,
@@ -272,7 +274,18 @@ kda_status kda_decode_step(const void *qkv, const void *z, kda_dtype in_dtype, c
 const char *kda_status_string(kda_status s);
 
 /* Plan AUTO would choose for a problem with these sizes and workspace
- * (host only; same rule the calls apply). */
+ * (host only; same rule the calls apply). The rule follows LightLLM PR #1703,
+ * "perf(kda): parallelize diagonal solves in Prefill": the PR description
+ * selects splitting by an FP32 workspace budget (scratch at most the FP32
+ * input size) and a minimum input length; the commit summary selects it by
+ * chunk occupancy, to bound scratch. SPLIT is chosen when the scratch of
+ * 4096 bytes per chunk-head fits both the budget and workspace_bytes and
+ * total_tokens reaches the minimum length, else FUSED. The minimum length is
+ * the fused/split crossover measured on MI355X (none was found, so by default
+ * AUTO never splits); two environment variables, read on every call, tune the
+ * rule: KDA_TRIL_SPLIT_MIN_TOKENS sets the minimum length, and KDA_TRIL_ALGO
+ * (fused, split or fused_valu) replaces the rule's choice for calls that ask
+ * for AUTO (an ineligible split still falls back to FUSED). */
 kda_algo kda_tril_auto_plan(int64_t total_tokens, int64_t num_chunks, int32_t num_heads,
                             size_t workspace_bytes);
 

@@ -139,6 +139,43 @@ def test_forced_split_workspace_errors(kt):
     assert _packed(kt, algo=2, ws=0x4004, wsb=2**30) == kt.KDA_ERR_INVALID_ARG
 
 
+def test_split_workspace_must_not_overlap_a_or_x(kt):
+    """The split plan's diagonal kernel writes the workspace before the merge
+    kernel reads A, so a workspace that overlaps A (or X) is refused before
+    any launch; the fused plans ignore the workspace."""
+    E = kt.KDA_ERR_INVALID_ARG
+    a_bytes = 64 * 2 * 64 * 4                 # A: 64 tokens x 2 heads x 64 fp32
+    need = 1 * 2 * 4096                       # one chunk, two heads
+    big = 2**30
+    # workspace inside A, straddling A's end, inside X, straddling X's start
+    for ws in (0x10000, 0x10000 + a_bytes - 16, 0x90000000, 0x90000000 - need + 16):
+        assert _packed(kt, algo=2, ws=ws, wsb=big) == E, hex(ws)
+        assert _dense(kt, algo=2, ws=ws, wsb=big) == E, hex(ws)
+    # the bytes checked are the ones the split plan uses for these sizes
+    assert kt.kda_tril_inv_workspace_size(64, 1, 0, 2, "split") == (need + 2 * 4096, "split")
+    assert kt.kda_tril_inv_workspace_size(64, 1, 1, 2, "split") == (need, "split")
+
+
+def test_algo_override_applies_to_auto_only(kt, monkeypatch):
+    """KDA_TRIL_ALGO replaces AUTO's choice (read on every call); calls that
+    name a plan keep it, and an ineligible split still falls back to fused."""
+    ws = kt.kda_tril_inv_workspace_size
+    monkeypatch.setenv("KDA_TRIL_ALGO", "split")
+    assert ws(8192, 16, 128, 64, "auto") == (32 * 2**20, "split")
+    assert kt.kda_tril_auto_plan(8192, 128, 64, 2**40) == "split"
+    assert kt.kda_tril_auto_plan(8192, 128, 64, 100) == "fused"       # workspace short
+    assert kt.kda_tril_auto_plan(8192, 1000, 64, 2**40) == "fused"    # over the budget
+    assert ws(8192, 16, 128, 64, "fused") == (0, "fused")
+    monkeypatch.setenv("KDA_TRIL_ALGO", "fused_valu")
+    assert ws(8192, 16, 128, 64, "auto") == (0, "fused_valu")
+    assert ws(8192, 16, 128, 64, "split") == (32 * 2**20, "split")
+    for v in ("fused", "auto", "", "nonsense"):
+        monkeypatch.setenv("KDA_TRIL_ALGO", v)
+        assert ws(8192, 16, 128, 64, "auto") == (0, "fused"), v
+    monkeypatch.delenv("KDA_TRIL_ALGO")
+    assert ws(8192, 16, 128, 64, "auto") == (0, "fused")
+
+
 def test_empty_problems_are_noops(kt):
     assert _packed(kt, T=0) == kt.KDA_OK
     assert _packed(kt, nseq=0) == kt.KDA_OK

@@ -161,3 +161,22 @@ def test_multi_gpu_refused(argv, env):
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_line_labels_algorithmic_and_measured_rates():
+    """roofline.achieved is algorithmic bytes over the kernel time and says
+    so; the measured HBM rate uses the counter bytes over the same time."""
+    import types
+    args = types.SimpleNamespace(steps=10, warmup=1)
+    k_avg = 45e-6
+    out = bench.base_line(args, 10 * 46e-6, k_avg, {}, 8192, 268435456, 4, bench.METRIC, None,
+                          {"workload": "w"}, "f32 A -> f32 X")
+    assert out["roofline"]["bytes"] == "algorithmic"
+    assert out["roofline"]["achieved"] == pytest.approx(268435456 / 45e-6 / 1e9)
+    assert out["dtype"] == "f32" and out["io_dtype"] == "f32 A -> f32 X"
+    assert "hbm_measured" not in bench.with_measured_hbm(dict(out), None)
+    bench.with_measured_hbm(out, 235368201)
+    assert out["roofline"]["traffic"] == 235368201
+    m = out["hbm_measured"]
+    assert m["achieved"] == pytest.approx(235368201 / 45e-6 / 1e9)
+    assert m["frac"] == pytest.approx(m["achieved"] / 8000.0)

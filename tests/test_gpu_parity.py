@@ -448,6 +448,47 @@ def test_non_default_stream(kt):
     assert torch.equal(X, ref)
 
 
+def test_split_on_a_stream_that_is_not_current(kt, monkeypatch):
+    """tril_inv(..., stream=side) with the split plan while `side` is not the
+    current stream: the workspace it allocates must belong to `side`, so once
+    tril_inv returns and frees it, the caching allocator cannot hand the block
+    to work on the current stream while the split kernels may still use it.
+    The side stream is held behind a slow computation on a third stream, and
+    a same-sized allocation on the current stream is filled meanwhile; X must
+    equal the fused result bit for bit, and that allocation must not be the
+    workspace's block."""
+    lengths = [512] * 8
+    H = 16
+    A = torch.from_numpy(synth.delta_rule_A(lengths, H, seed=93)).to(DEV)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    ref = kt.tril_inv(A, cu, algo="fused")
+    torch.cuda.synchronize()
+    seen = {}
+    real = kt.kda_tril_inv_packed
+
+    def spy(A_, X_, cu_, chunk_indices=None, workspace=None, algo="auto", stream=None):
+        seen["ws"] = (workspace.data_ptr(), workspace.numel())
+        return real(A_, X_, cu_, chunk_indices=chunk_indices, workspace=workspace, algo=algo,
+                    stream=stream)
+
+    monkeypatch.setattr(kt, "kda_tril_inv_packed", spy)
+    gate, side = torch.cuda.Stream(), torch.cuda.Stream()
+    M = torch.randn(2048, 2048, device=DEV)
+    gate.wait_stream(torch.cuda.current_stream())
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gate):
+        for _ in range(20):
+            M = torch.tanh(M @ M)
+    side.wait_stream(gate)
+    X = kt.tril_inv(A, cu, algo="split", stream=side)
+    ptr, n = seen["ws"]
+    Y = torch.empty(n, dtype=torch.float32, device=DEV)  # current stream
+    Y.fill_(float("nan"))
+    assert Y.data_ptr() != ptr
+    torch.cuda.synchronize()
+    assert torch.equal(X, ref)
+
+
 def test_empty_problems_are_noops(kt):
     A = torch.zeros((0, 4, 64), device=DEV)
     X = torch.zeros((0, 4, 64), device=DEV)

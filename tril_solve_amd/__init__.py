@@ -239,6 +239,15 @@ def prepare_dense(A, X, workspace=None, algo="auto", stream=None):
     return _prepared(*_dense_fn(_dense_args(A, X, workspace, algo, stream)))
 
 
+def _alloc_stream(stream):
+    """Context in which torch allocations belong to `stream` (the current
+    stream when None)."""
+    import contextlib
+
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None, out=None,
              stream=None):
     """X = (I + A)^-1 per chunk of C = A.shape[-1] tokens (16, 32 or 64) and
@@ -251,7 +260,8 @@ def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None
     """
     import torch
     out_dtype = out_dtype or torch.float32
-    X = out if out is not None else torch.empty(A.shape, dtype=out_dtype, device=A.device)
+    with _alloc_stream(stream):
+        X = out if out is not None else torch.empty(A.shape, dtype=out_dtype, device=A.device)
     C = A.shape[-1]
     nbytes = 0
     if C == 64:
@@ -262,7 +272,11 @@ def tril_inv(A, cu_seqlens=None, out_dtype=None, algo="auto", chunk_indices=None
             T, H, _ = A.shape
             nch = 0 if chunk_indices is None else chunk_indices.numel() // 2
             nbytes, _chosen = kda_tril_inv_workspace_size(T, cu_seqlens.numel() - 1, nch, H, algo)
-    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=A.device) if nbytes else None
+    # the workspace belongs to the stream the kernels run on: it is freed when
+    # this function returns, and torch's caching allocator only reuses a block
+    # in the order of the stream it was allocated on
+    with _alloc_stream(stream):
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=A.device) if nbytes else None
     if cu_seqlens is None:
         kda_tril_inv_dense(A, X, workspace=ws, algo=algo, stream=stream)
     else:
@@ -330,7 +344,8 @@ def prepare_kkt(k, g, beta, out, cu_seqlens=None, solve=True, stream=None):
 def kkt_tril_inv(k, g, beta, cu_seqlens=None, out_dtype=None, chunk_indices=None, stream=None):
     """Convenience form of kda_kkt_tril_inv: allocates X with torch."""
     import torch
-    X = torch.empty(k.shape[:-1] + (64,), dtype=out_dtype or torch.float32, device=k.device)
+    with _alloc_stream(stream):
+        X = torch.empty(k.shape[:-1] + (64,), dtype=out_dtype or torch.float32, device=k.device)
     kda_kkt_tril_inv(k, g, beta, X, cu_seqlens, chunk_indices, stream)
     return X
 

@@ -80,7 +80,11 @@ kda_status check_common(const void *A, kda_dtype a_dtype, const void *X, kda_dty
     return KDA_OK;
 }
 
+// Plan of a call. A SPLIT plan's workspace must be aligned and must not
+// overlap A or X: the diagonal kernel writes it before the merge kernel reads
+// A, so an overlap would corrupt the input with no error.
 kda_status plan_call(int64_t rows, int64_t slots, int32_t H, int32_t C, kda_algo algo,
+                     const void *A, size_t a_bytes, const void *X, size_t x_bytes,
                      void *workspace, size_t workspace_bytes, kda_algo *chosen) {
     if (C != 64) {  // one kernel per small chunk size, no workspace
         *chosen = KDA_ALGO_FUSED;
@@ -89,8 +93,17 @@ kda_status plan_call(int64_t rows, int64_t slots, int32_t H, int32_t C, kda_algo
     const size_t offered = workspace ? workspace_bytes : 0;
     kda_status st = resolve_plan(rows, slots, H, algo, offered, chosen);
     if (st != KDA_OK) return st;
-    if (*chosen == KDA_ALGO_SPLIT && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
+    if (*chosen == KDA_ALGO_SPLIT) {
+        const size_t need = (size_t)split_workspace_bytes(slots, H);
+        if (!aligned16(workspace)) return KDA_ERR_INVALID_ARG;
+        if (overlap(workspace, need, A, a_bytes) || overlap(workspace, need, X, x_bytes))
+            return KDA_ERR_INVALID_ARG;
+    }
     return KDA_OK;
+}
+
+size_t tensor_bytes(int64_t rows, int32_t H, int32_t C, kda_dtype d) {
+    return (size_t)rows * (size_t)H * (size_t)C * dtype_bytes(d);
 }
 
 kda_status dense_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype, int64_t B,
@@ -104,7 +117,8 @@ kda_status dense_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dty
     const int64_t slots = B * ((T + C - 1) / C);
     if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
     kda_algo chosen = KDA_ALGO_FUSED;
-    st = plan_call(rows, slots, H, C, algo, workspace, workspace_bytes, &chosen);
+    st = plan_call(rows, slots, H, C, algo, A, tensor_bytes(rows, H, C, a_dtype), X,
+                   tensor_bytes(rows, H, C, x_dtype), workspace, workspace_bytes, &chosen);
     if (st != KDA_OK) return st;
     Problem p;
     memset(&p, 0, sizeof(p));
@@ -137,7 +151,9 @@ kda_status packed_call(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dt
     const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks, C);
     if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
     kda_algo chosen = KDA_ALGO_FUSED;
-    st = plan_call(total_tokens, slots, H, C, algo, workspace, workspace_bytes, &chosen);
+    st = plan_call(total_tokens, slots, H, C, algo, A, tensor_bytes(total_tokens, H, C, a_dtype),
+                   X, tensor_bytes(total_tokens, H, C, x_dtype), workspace, workspace_bytes,
+                   &chosen);
     if (st != KDA_OK) return st;
     Problem p;
     memset(&p, 0, sizeof(p));

@@ -11,6 +11,7 @@
 
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 namespace kda {
 
@@ -28,6 +29,19 @@ int64_t split_min_tokens() {
         if (end && *end == '\0' && v >= 0) return (int64_t)v;
     }
     return kDefaultSplitMinTokens;
+}
+
+// Tuning override of AUTO: KDA_TRIL_ALGO = fused | split | fused_valu makes
+// calls that ask for AUTO run that plan instead (a split that is not eligible
+// still falls back to fused, as AUTO does); unset, empty or "auto" keeps the
+// rule. Calls that name a plan are never overridden.
+static kda_algo auto_override() {
+    const char *e = getenv("KDA_TRIL_ALGO");
+    if (e == nullptr || *e == '\0') return KDA_ALGO_AUTO;
+    if (strcmp(e, "fused") == 0) return KDA_ALGO_FUSED;
+    if (strcmp(e, "split") == 0) return KDA_ALGO_SPLIT;
+    if (strcmp(e, "fused_valu") == 0) return KDA_ALGO_FUSED_VALU;
+    return KDA_ALGO_AUTO;
 }
 
 int64_t chunk_slots(int64_t total_tokens, int64_t num_seqs, int64_t num_chunks, int chunk) {
@@ -56,10 +70,18 @@ kda_status resolve_plan(int64_t total_tokens, int64_t slots, int32_t heads, kda_
         case KDA_ALGO_SPLIT:
             if (!budget_ok || !ws_ok) return KDA_ERR_WORKSPACE;
             break;
-        case KDA_ALGO_AUTO:
-            out = (budget_ok && ws_ok && total_tokens >= split_min_tokens()) ? KDA_ALGO_SPLIT
-                                                                              : KDA_ALGO_FUSED;
+        case KDA_ALGO_AUTO: {
+            const kda_algo forced = auto_override();
+            if (forced == KDA_ALGO_SPLIT)
+                out = (budget_ok && ws_ok) ? KDA_ALGO_SPLIT : KDA_ALGO_FUSED;
+            else if (forced != KDA_ALGO_AUTO)
+                out = forced;
+            else
+                out = (budget_ok && ws_ok && total_tokens >= split_min_tokens())
+                          ? KDA_ALGO_SPLIT
+                          : KDA_ALGO_FUSED;
             break;
+        }
         default:
             return KDA_ERR_INVALID_ARG;
     }
