@@ -270,6 +270,37 @@ kda_status kda_decode_step(const void *qkv, const void *z, kda_dtype in_dtype, c
                            int32_t H, int32_t head_dim, int32_t conv_width, float eps_l2,
                            float eps_norm, hipStream_t stream);
 
+/*
+ * Allocation-free form of kda_tril_inv_packed, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It always runs the SPLIT plan, with the
+ * workspace taken from a scratch array the library keeps in device memory:
+ * KDA_TRIL_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the library runs on,
+ * held until the process ends, found on a device's first call. The call
+ * itself allocates and frees nothing.
+ *   Arguments, layout, ownership of A, X, cu_seqlens and chunk_indices, and
+ *   results: as kda_tril_inv_packed with algo = KDA_ALGO_SPLIT (X bit for bit
+ *   equal to it).
+ *   Size limit: the split workspace, 4096 bytes x H x chunk slots (num_chunks
+ *   when chunk_indices is given, else floor(total_tokens / 64) + num_seqs),
+ *   must not exceed KDA_TRIL_NOALLOC_SCRATCH_BYTES (16,384 chunk-heads), and
+ *   the split plan must be eligible (workspace <= FP32 input size); otherwise
+ *   KDA_ERR_WORKSPACE before any device call.
+ *   Concurrency: every call on one GPU uses that GPU's one array. Calls in
+ *   order on one stream are safe; calls that overlap in time on one GPU (on
+ *   different streams or from different host threads) race on it and give
+ *   wrong results. Nothing in the array needs to start at zero: each call
+ *   writes every tile it later reads.
+ *   KDA_ERR_HIP: the device address of the array could not be found, or a
+ *   launch failed.
+ */
+#define KDA_TRIL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_tril_inv_packed_noalloc(const void *A, kda_dtype a_dtype, void *X,
+                                       kda_dtype x_dtype, const int32_t *cu_seqlens,
+                                       int64_t num_seqs, int64_t total_tokens, int32_t H,
+                                       const int32_t *chunk_indices, int64_t num_chunks,
+                                       hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);
 

@@ -377,3 +377,35 @@ def test_header_serves_a_plain_c_caller(kt, tmp_path):
     want_bytes, want_algo = kt.kda_tril_inv_workspace_size(8192, 16, 0, 64, "split")
     assert int(out[1]) == want_bytes
     assert kt.ALGO_NAMES[int(out[2])] == want_algo
+
+
+# ---- the allocation-free entry point -----------------------------------------
+
+def _noalloc(kt, A=0x10000, ad=0, X=0x90000000, xd=0, cu=0x2000, nseq=1, T=64, H=2, cmap=None,
+             nch=0):
+    return kt._lib.kda_tril_inv_packed_noalloc(P(A), ad, P(X), xd, P(cu), nseq, T, H, P(cmap),
+                                               nch, None)
+
+
+def test_noalloc_refuses_before_any_device_call(kt):
+    """Every refusal of kda_tril_inv_packed_noalloc happens on the host: bad
+    arguments, a split workspace past the 64 MiB scratch, or a split past the
+    FP32-input budget."""
+    E, W = kt.KDA_ERR_INVALID_ARG, kt.KDA_ERR_WORKSPACE
+    assert kt.NOALLOC_SCRATCH_BYTES == 64 * 2**20
+    assert _noalloc(kt, ad=3) == E and _noalloc(kt, H=0) == E and _noalloc(kt, A=None) == E
+    assert _noalloc(kt, cu=None) == E and _noalloc(kt, cmap=0x3000, nch=0) == E
+    assert _noalloc(kt, X=0x10000 + 64 * 2 * 64 * 4 - 16) == E
+    assert _noalloc(kt, T=2**31) == kt.KDA_ERR_UNSUPPORTED
+    # 16,384 chunk-heads fit exactly (with a chunk map giving the exact count);
+    # one more head per chunk does not
+    mib64 = 64 * 2**20
+    assert 256 * 64 * 4096 == mib64
+    assert _noalloc(kt, T=256 * 64, nseq=1, H=65, cmap=0x3000, nch=256) == W
+    # without a map the slot bound floor(T/64) + num_seqs is what must fit
+    assert _noalloc(kt, T=256 * 64, nseq=1, H=64) == W
+    # budget: 64 one-token requests, occupancy 1
+    assert _noalloc(kt, T=64, nseq=64, H=2) == W
+    # empty problems are no-ops that never look up the scratch
+    assert _noalloc(kt, T=0, A=None, X=None, cu=None) == kt.KDA_OK
+    assert _noalloc(kt, nseq=0) == kt.KDA_OK

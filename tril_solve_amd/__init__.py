@@ -54,6 +54,10 @@ _lib.kda_tril_inv_packed_chunk.restype = ctypes.c_int
 _lib.kda_tril_inv_packed_chunk.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64,
                                            _i32, _i32, _p, _i64, _p, _sz, ctypes.c_int, _p]
 
+_lib.kda_tril_inv_packed_noalloc.restype = ctypes.c_int
+_lib.kda_tril_inv_packed_noalloc.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64,
+                                             _i32, _p, _i64, _p]
+
 for _n in ("kda_kkt_tril_inv_packed", "kda_kkt_packed"):
     getattr(_lib, _n).restype = ctypes.c_int
     getattr(_lib, _n).argtypes = [_p, _p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64, _i32,
@@ -71,7 +75,8 @@ _lib.kda_decode_step.argtypes = [_p, _p, ctypes.c_int, _p, _p, _p, _p, _p, _p, _
 EXPORTED = ("kda_tril_inv_workspace_size", "kda_tril_inv_dense", "kda_tril_inv_packed",
             "kda_status_string", "kda_tril_auto_plan", "kda_tril_inv_dense_chunk",
             "kda_tril_inv_packed_chunk", "kda_kkt_tril_inv_packed", "kda_kkt_tril_inv_dense",
-            "kda_kkt_packed", "kda_kkt_dense", "kda_decode_step")
+            "kda_kkt_packed", "kda_kkt_dense", "kda_decode_step", "kda_tril_inv_packed_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 CHUNK_SIZES = (16, 32, 64)
 
 
@@ -200,6 +205,16 @@ def kda_tril_inv_packed(A, X, cu_seqlens, chunk_indices=None, workspace=None, al
     C = 16, 32 or 64."""
     fn, args = _packed_fn(_packed_args(A, X, cu_seqlens, chunk_indices, workspace, algo, stream))
     _check(fn(*args))
+
+
+def kda_tril_inv_packed_noalloc(A, X, cu_seqlens, chunk_indices=None, stream=None) -> None:
+    """kda_tril_inv_packed_noalloc: the split plan with the library's own
+    device scratch (no workspace argument, nothing allocated). A, X
+    [T, H, 64]."""
+    args = _packed_args(A, X, cu_seqlens, chunk_indices, None, "split", stream)
+    _require(args[8] == 64, "the allocation-free entry point takes 64-token chunks")
+    # drop chunk size, workspace pointer and size, and plan
+    _check(_lib.kda_tril_inv_packed_noalloc(*(args[:8] + args[9:11] + args[14:])))
 
 
 def kda_tril_inv_dense_chunk(A, X, chunk_size, workspace=None, algo="auto", stream=None) -> None:

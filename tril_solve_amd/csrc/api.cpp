@@ -328,6 +328,30 @@ kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
                        stream);
 }
 
+kda_status kda_tril_inv_packed_noalloc(const void *A, kda_dtype a_dtype, void *X,
+                                       kda_dtype x_dtype, const int32_t *cu_seqlens,
+                                       int64_t num_seqs, int64_t total_tokens, int32_t H,
+                                       const int32_t *chunk_indices, int64_t num_chunks,
+                                       hipStream_t stream) {
+    // every host check first, so that a refused call never touches the device
+    if (num_seqs < 0 || total_tokens < 0 || num_chunks < 0) return KDA_ERR_INVALID_ARG;
+    if ((chunk_indices == nullptr) != (num_chunks == 0)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs > kMaxTokens || num_chunks > kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    kda_status st = check_common(A, a_dtype, X, x_dtype, total_tokens, H, 64, KDA_ALGO_SPLIT);
+    if (st != KDA_OK || total_tokens == 0 || num_seqs == 0) return st;
+    if (cu_seqlens == nullptr) return KDA_ERR_INVALID_ARG;
+    const int64_t slots = chunk_slots(total_tokens, num_seqs, num_chunks, 64);
+    if (!grid_fits(slots, H)) return KDA_ERR_UNSUPPORTED;
+    if (split_workspace_bytes(slots, H) > (int64_t)KDA_TRIL_NOALLOC_SCRATCH_BYTES ||
+        !split_within_budget(total_tokens, slots, H))
+        return KDA_ERR_WORKSPACE;
+    float *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+    return packed_call(A, a_dtype, X, x_dtype, cu_seqlens, num_seqs, total_tokens, H, 64,
+                       chunk_indices, num_chunks, ws, KDA_TRIL_NOALLOC_SCRATCH_BYTES,
+                       KDA_ALGO_SPLIT, stream);
+}
+
 kda_status kda_kkt_tril_inv_packed(const void *k, const float *g, const void *beta,
                                    kda_dtype k_dtype, void *X, kda_dtype x_dtype,
                                    const int32_t *cu_seqlens, int64_t num_seqs,

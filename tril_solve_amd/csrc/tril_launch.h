@@ -72,6 +72,9 @@ long walk_blocks(const void *fn, long waves, long min_waves);
 // Element-type codes of A and X: the kda_dtype values (0 f32, 1 bf16, 2 f16).
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
+// Device address, on the current device, of the library-held split workspace
+// of KDA_TRIL_NOALLOC_SCRATCH_BYTES (looked up once per device, then cached).
+hipError_t noalloc_scratch(float **ptr);
 hipError_t launch_fused_valu(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 // Chunks of 16 or 32 tokens (A and X rows of `chunk` elements).
 hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStream_t stream);

@@ -9,8 +9,20 @@
 // [slots * H, 4, 16, 16], each tile column-major; the merge kernel reads them
 // with the off-diagonal blocks of A and writes X. Per full chunk-head this
 // moves 8 KiB more than the fused kernel (tiles written once, read once).
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "kda_tril.h"
 #include "tril_device.h"
 #include "tril_launch.h"
+
+// Workspace of the allocation-free entry point (kda_tril_inv_packed_noalloc):
+// the split plan's tiles in device memory the library holds, one copy per GPU
+// for as long as the process runs. Host code never uses this name as an
+// address (on the host it is only a stand-in); it uses the device address
+// that noalloc_scratch looks up per device.
+static __device__ __align__(256) float scratch[KDA_TRIL_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace kda {
 
@@ -84,6 +96,30 @@ static hipError_t launch_split_t(const Problem &p, hipStream_t stream) {
     hipLaunchKernelGGL((tril_inv_split_merge<EI, EO>), dim3((unsigned)blocks),
                        dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, float *>> g_scratch;  // (device, address of `scratch` there)
+}  // namespace
+
+hipError_t noalloc_scratch(float **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    for (const auto &d : g_scratch)
+        if (d.first == dev) {
+            *ptr = d.second;
+            return hipSuccess;
+        }
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch.emplace_back(dev, static_cast<float *>(addr));
+    *ptr = static_cast<float *>(addr);
+    return hipSuccess;
 }
 
 hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
