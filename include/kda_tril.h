@@ -186,13 +186,18 @@ kda_status kda_tril_inv_packed_chunk(const void *A, kda_dtype a_dtype, void *X,
  * strengths instead of A:
  *   k      [rows, H, K] of k_dtype: key rows, K channels; K a multiple of 16,
  *          16 <= K <= 256 (other K: KDA_ERR_UNSUPPORTED).
- *   g      [rows, H, K] FP32: cumulative log-decay of each channel. Only
- *          differences within a chunk enter, evaluated in FP32 as
- *          exp(g_i - g_ri) exp(g_ri - g_rj) exp(g_rj - g_j) with r_i, r_j the
- *          first rows of the 16-row blocks of i and j. No factor overflows
- *          while g does not rise by more than ~88 anywhere in a chunk and does
- *          not fall by more than ~88 within 16 consecutive tokens (true of
- *          cumulative sums of log-gates <= 0 that stay above -5.5 per token).
+ *   g      [rows, H, K] FP32: cumulative log-decay of each channel,
+ *          non-increasing along a chunk (log-gates <= 0, as in KDA). Only
+ *          differences within a chunk enter, so g may restart at every chunk
+ *          or run over a whole request; each is taken in FP32 before it is
+ *          scaled, and evaluated as exp(g_i - g_ri) exp(g_ri - g_rj)
+ *          exp(g_rj - g_j) with r_i, r_j the first rows of the 16-row blocks of
+ *          i and j. Domain: a channel may fall by up to 5.4 per token for a
+ *          whole chunk (tested to the fp32 bounds, alone, mixed with slow
+ *          channels and in partial chunks). Past a fall of about 87 over 16
+ *          consecutive tokens (5.45 per token) the factor between adjacent
+ *          16-token blocks drops below 2^-126 and is flushed to 0, so entries
+ *          of A between those blocks lose that channel's term.
  *   beta   [rows, H] of k_dtype: write strengths.
  * rows = total_tokens (packed, with cu_seqlens and optional chunk_indices as
  * for kda_tril_inv_packed) or B * T (dense, [B, T, H, ...]). k, g and the

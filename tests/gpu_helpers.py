@@ -91,3 +91,15 @@ def host_chunk_map(lengths, C=64):
         for c in range((n + C - 1) // C):
             pairs.append((s, c))
     return np.asarray(pairs, np.int32).reshape(-1, 2)
+
+
+def residual_full_chunks(A, X):
+    """max |(I + A_c) X_c - I| over every chunk-head of packed [T, H, 64]
+    arrays whose chunks are all full and start at multiples of 64 (requests
+    of whole chunks); A's entries on and above the diagonal are ignored.
+    Batched in float64."""
+    T, H, C = A.shape
+    assert T % C == 0
+    M = np.tril(np.asarray(A, np.float64).reshape(T // C, C, H, C).transpose(0, 2, 1, 3), -1)
+    Xm = np.asarray(X, np.float64).reshape(T // C, C, H, C).transpose(0, 2, 1, 3)
+    return float(np.abs(M @ Xm + Xm - np.eye(C)).max())

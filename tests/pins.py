@@ -428,6 +428,46 @@ def check_dec_padding_and_slots(dec, d=8, W=4):
     return bool(ok)
 
 
+def check_dec_q_scale(dec, d=16, W=3):
+    """The scales of q and k, seen through an output that keeps them: zero
+    state, g = 0, beta = 1 and pass-through taps make the step store k v^T
+    and return o = (k . q) v; with eps_norm = 1, far above mean(o^2), the
+    gated RMSNorm no longer cancels a positive factor on q. Before the
+    normalisation q and k are one-hot in channel m of each head,
+    y_q = silu(xq) e_m and y_k = silu(xk) e_m, so by hand
+        q = e_m silu(xq) / sqrt(silu(xq)^2 + eps_l2) / sqrt(d),
+        k = e_m silu(xk) / sqrt(silu(xk)^2 + eps_l2),
+        out_j = (k_m q_m) v_j / sqrt((k_m q_m)^2 mean(v^2) + eps_norm) wn_j sigmoid(z_j),
+    for two values of eps_l2 (0 and 0.5) and a negative silu(xk), so the
+    sign of k . q enters too."""
+    rng = np.random.default_rng(16)
+    H = 2
+    cw = _onehot_conv(H, d, W)
+    ok = True
+    for eps_l2 in (0.0, 0.5):
+        x = np.zeros((1, 3, H, d))
+        xq, xk = np.array([1.5, 0.75]), np.array([-2.0, 3.0])
+        for h, m in enumerate((3, 10)):
+            x[0, 0, h, m] = xq[h]
+            x[0, 1, h, m] = xk[h]
+        x[0, 2] = rng.standard_normal((H, d))
+        z = rng.standard_normal((1, H, d))
+        wn = rng.random(d) + 0.5
+        out, _, _ = dec(x, np.zeros((1, H, d)), np.ones((1, H)), z, wn, cw,
+                        np.array([0], np.int32), np.zeros((1, H, d, d)),
+                        np.zeros((1, 3, H, W - 1, d)), eps_l2, 1.0)
+        for h in range(H):
+            a = xq[h] / (1.0 + np.exp(-xq[h]))
+            b = xk[h] / (1.0 + np.exp(-xk[h]))
+            qm = a / np.sqrt(a * a + eps_l2) / np.sqrt(d)
+            km = b / np.sqrt(b * b + eps_l2)
+            v = _silu(x[0, 2, h])
+            o = km * qm * v
+            want = o / np.sqrt(np.mean(o * o) + 1.0) * wn / (1.0 + np.exp(-z[0, h]))
+            ok &= np.abs(out[0, h] - want).max() <= 1e-13
+    return bool(ok)
+
+
 def dec_brute_force(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2, eps_norm):
     """The decode step with Python floats and loops, entry by entry."""
     import math
@@ -488,5 +528,5 @@ def check_dec_brute_force(dec, d=6, W=3):
 def dec_all(dec):
     checks = {"delta_rule": check_dec_delta_rule, "decay_only": check_dec_decay_only,
               "conv_taps": check_dec_conv_taps, "padding_and_slots": check_dec_padding_and_slots,
-              "brute_force": check_dec_brute_force}
+              "q_scale": check_dec_q_scale, "brute_force": check_dec_brute_force}
     return [n for n, f in checks.items() if not f(dec)]

@@ -126,6 +126,58 @@ def test_delta_rule_closed_form(kt):
         assert gh.excess(S[inp["slot"][b]], want_S, "f32") <= 0
 
 
+def _check_eps(kt, inp, d, out, eps_l2, eps_norm):
+    ref_out, ref_S, ref_cs = _ref(inp, eps_l2=eps_l2, eps_norm=eps_norm)
+    e = gh.excess(gh.to_numpy_f64(out), ref_out, "f32")
+    assert e <= 0, f"output exceeds tolerance by {e:.3g}"
+    e = gh.excess(d["state"].cpu().numpy().astype(np.float64), ref_S, "f32")
+    assert e <= 0, f"state exceeds tolerance by {e:.3g}"
+
+
+@pytest.mark.parametrize("eps_l2,eps_norm", [(0.5, 1.0), (0.0, 1.0), (2.0, 0.25)])
+def test_large_eps_keeps_q_scale(kt, eps_l2, eps_norm):
+    """eps_norm comparable to or above mean(o^2): the gated RMSNorm no longer
+    cancels the scale of q, so the 1/sqrt(d) and where eps_l2 enters both
+    reach the output (random inputs against the oracle)."""
+    inp = synth.decode_inputs(5, 3, seed=126)
+    d = _dev(inp)
+    out = _step(kt, d, eps_l2=eps_l2, eps_norm=eps_norm)
+    _check_eps(kt, inp, d, out, eps_l2, eps_norm)
+
+
+def test_q_scale_closed_form(kt):
+    """Zero state, g = 0, beta = 1, pass-through taps, q and k one-hot in one
+    channel before their normalisation, eps_l2 = 0.5, eps_norm = 1: the
+    output is (k_m q_m) v / sqrt((k_m q_m)^2 mean(v^2) + 1) * w * sigmoid(z)
+    with q_m = silu(xq) / sqrt(silu(xq)^2 + 0.5) / sqrt(128) and
+    k_m = silu(xk) / sqrt(silu(xk)^2 + 0.5), worked out here in float64."""
+    B, H, eps_l2 = 2, 3, 0.5
+    inp = synth.decode_inputs(B, H, seed=127)
+    inp["qkv"][:, :2] = 0.0
+    m = np.array([[5, 64, 127], [0, 33, 90]])
+    xq = np.array([[1.5, -0.5, 2.5], [0.25, 3.0, -1.0]], np.float32)
+    xk = np.array([[-2.0, 1.0, 0.5], [1.75, -0.75, 2.0]], np.float32)
+    for b in range(B):
+        for h in range(H):
+            inp["qkv"][b, 0, h, m[b, h]] = xq[b, h]
+            inp["qkv"][b, 1, h, m[b, h]] = xk[b, h]
+    inp["g"][:] = 0.0
+    inp["beta"][:] = 1.0
+    inp["state"][:] = 0.0
+    inp["conv_w"][:] = 0.0
+    inp["conv_w"][:, -1] = 1.0
+    d = _dev(inp)
+    out = gh.to_numpy_f64(_step(kt, d, eps_l2=eps_l2, eps_norm=1.0))
+    silu = lambda x: x / (1.0 + np.exp(-x))  # noqa: E731
+    a, bb = silu(xq.astype(np.float64)), silu(xk.astype(np.float64))
+    kq = (bb / np.sqrt(bb * bb + eps_l2)) * (a / np.sqrt(a * a + eps_l2) / np.sqrt(128.0))
+    v = silu(inp["qkv"][:, 2].astype(np.float64))
+    o = kq[:, :, None] * v
+    want = (o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1.0) * inp["norm_w"] /
+            (1.0 + np.exp(-inp["z"].astype(np.float64))))
+    assert gh.excess(out, want, "f32") <= 0
+
+
 def test_eight_steps_carry_state(kt):
     """Eight consecutive steps on the same slots, state kept on the device,
     against the oracle carrying its float64 state."""

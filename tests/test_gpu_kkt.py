@@ -191,11 +191,72 @@ def test_zero_keys_give_identity(kt):
         assert np.array_equal(X[s:s + L, h], want)
 
 
-def test_full_workload_sampled(kt):
-    """16 requests x 512 tokens, 64 heads, K = 128, bf16 keys: 16 sampled
-    chunks (all 64 heads each) against the oracle, every row's unit diagonal
-    and zero upper triangle checked on the device."""
-    name = "packed_16x512_h64_k128_kkt_bf16_f32"
+def _decay_inputs(lengths, H, K, mode, seed):
+    """Keys and write strengths from the generator, decays chosen per mode:
+      fast:    every channel falls by 5.4 per token (within 16 tokens, 86.4:
+               the edge of the documented domain), restarting at each chunk;
+      mixed:   half the channels fall by 5.4 per token, the others by the
+               generator's logsigmoid draws;
+      uniform: each (token, channel) falls by U(0, 5.4);
+      request: falls U(0, 0.5) summed over the whole request (no restart at
+               chunk boundaries) from -3000, so |g| runs into the thousands
+               and only the differences within a chunk are small."""
+    rng = np.random.default_rng(seed)
+    k, g, beta = synth.delta_rule_inputs(lengths, H, seed, K=K)
+    T = sum(lengths)
+    if mode == "fast":
+        fall = np.full((T, H, K), 5.4)
+    elif mode == "mixed":
+        fall = -np.diff(np.concatenate([np.zeros((1, H, K)), g.astype(np.float64)]), axis=0)
+        fall[:, :, ::2] = 5.4
+    elif mode in ("uniform", "request"):
+        fall = rng.uniform(0.0, 5.4 if mode == "uniform" else 0.5, (T, H, K))
+    g = np.zeros((T, H, K))
+    bos = 0
+    for n in lengths:
+        for p in range(0, n, 64):
+            hi = min(bos + n, bos + p + 64)
+            if mode == "request":
+                continue
+            g[bos + p:hi] = -np.cumsum(fall[bos + p:hi], axis=0)
+        if mode == "request":
+            g[bos:bos + n] = -3000.0 - np.cumsum(fall[bos:bos + n], axis=0)
+        bos += n
+    return k, g.astype(np.float32), beta
+
+
+@pytest.mark.parametrize("k_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["fast", "mixed", "uniform", "request"])
+def test_decay_domain(kt, mode, k_dtype):
+    """Parity across the documented decay domain (falls of up to 5.4 per
+    token), with full and partial chunks, against the oracle's float64 A."""
+    print(f"\n[kkt] decay domain {mode} k={k_dtype}", flush=True)
+    lengths = [64, 37, 150, 64]
+    H, K = 4, 128
+    k, g, beta = _decay_inputs(lengths, H, K, mode, seed=90)
+    if k_dtype == "bf16":
+        k, beta = synth.to_bf16_bits(k), synth.to_bf16_bits(beta)
+    cu = synth.cu_seqlens(lengths)
+    X = gh.to_numpy_f64(_solve(kt, *_dev(k, g, beta, k_dtype), cu))
+    A64 = oracle.kkt_packed(k, g, beta, cu, k_dtype)
+    ref = oracle.tril_inv_packed(A64, cu, "f64")
+    assert np.all(np.isfinite(X[~np.isnan(ref)]))
+    e = gh.excess(X, ref, "f32")
+    assert e <= 0, f"exceeds tolerance by {e:.3g}"
+    assert gh.residual_chunks(A64, X, gh.all_chunk_heads(lengths, H)) <= gh.RESIDUAL_TOL
+    # the matrix alone to the same bound
+    Ag = gh.to_numpy_f64(_solve(kt, *_dev(k, g, beta, k_dtype), cu, solve=False))
+    e = gh.excess(Ag, A64, "f32")
+    assert e <= 0, f"A exceeds tolerance by {e:.3g}"
+
+
+@pytest.mark.parametrize("name", ["packed_16x512_h64_k128_kkt_bf16_f32",
+                                  "packed_16x512_h64_k128_kkt_f32_f32"])
+def test_full_workload(kt, name):
+    """16 requests x 512 tokens, 64 heads, K = 128 (the benchmark's batch):
+    every one of the 8192 chunk-heads against the oracle, the residual of
+    every fp32 X against the oracle's float64 A, and every row's unit
+    diagonal and zero upper triangle bit for bit."""
     print(f"\n[kkt] workload {name}", flush=True)
     d = synth.make_kkt(name)
     dv = _dev(d["k"], d["g"], d["beta"], d["k_dtype"])
@@ -206,20 +267,39 @@ def test_full_workload_sampled(kt):
     upper = torch.triu(torch.ones(64, 64, device=DEV, dtype=torch.bool), 1)
     assert bool((t[:, :, upper] == 0).all())
     got = gh.to_numpy_f64(X)
-    rng = np.random.default_rng(4)
-    for c in rng.choice(T // 64, 16, replace=False):
-        s = 64 * int(c)
-        sl = slice(s, s + 64)
-        ref = oracle.kkt_tril_inv_packed(d["k"][sl], d["g"][sl], d["beta"][sl], [0, 64],
-                                         d["k_dtype"])
-        e = gh.excess(got[sl], ref, "f32")
-        assert e <= 0, f"chunk {c}: exceeds tolerance by {e:.3g}"
+    A64 = oracle.kkt_packed(d["k"], d["g"], d["beta"], d["cu_seqlens"], d["k_dtype"])
+    ref = oracle.tril_inv_packed(A64, d["cu_seqlens"], "f64")
+    e = gh.excess(got, ref, "f32")
+    assert e <= 0, f"exceeds tolerance by {e:.3g}"
+    assert gh.residual_full_chunks(A64, got) <= gh.RESIDUAL_TOL
+
+
+def test_deterministic_across_grids(kt, monkeypatch):
+    """The build-A path on the 16 x 512-token, 64-head batch (bf16 keys):
+    20 repeats on each of three grids (1, 2 and 3 workgroups per compute
+    unit, set per call) equal the default grid's result bit for bit."""
+    name = "packed_16x512_h64_k128_kkt_bf16_f32"
+    d = synth.make_kkt(name)
+    kd, gd, bd = _dev(d["k"], d["g"], d["beta"], d["k_dtype"])
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    monkeypatch.delenv("KDA_TRIL_BLOCKS_PER_CU", raising=False)
+    X0 = torch.empty((d["T_total"], d["H"], 64), device=DEV)
+    kt.kda_kkt_tril_inv(kd, gd, bd, X0, cu)
+    X = torch.empty_like(X0)
+    call = kt.prepare_kkt(kd, gd, bd, X, cu)
+    for per_cu in ("1", "2", "3"):
+        monkeypatch.setenv("KDA_TRIL_BLOCKS_PER_CU", per_cu)
+        for rep in range(20):
+            X.fill_(float("nan"))
+            call()
+            assert torch.equal(X, X0), f"{per_cu} per CU, repeat {rep}"
+    monkeypatch.delenv("KDA_TRIL_BLOCKS_PER_CU")
 
 
 def test_bench_launch_configuration(kt):
     """Prepared build-A calls over two rotating buffer sets, issued back to
     back with no synchronisation, as the benchmark times them; each set's X
-    checked on sampled chunks against the oracle."""
+    checked in full against the oracle."""
     name = "packed_16x512_h64_k128_kkt_bf16_f32"
     cfg = dict(synth.KKT_CONFIGS[name])
     sets = []
@@ -235,12 +315,8 @@ def test_bench_launch_configuration(kt):
     for i in range(6):
         calls[i % 2]()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
     for d, _, _, _, X in sets:
-        got = gh.to_numpy_f64(X)
-        for c in rng.choice(d["T_total"] // 64, 6, replace=False):
-            sl = slice(64 * int(c), 64 * int(c) + 64)
-            ref = oracle.kkt_tril_inv_packed(d["k"][sl], d["g"][sl], d["beta"][sl], [0, 64],
-                                             d["k_dtype"])
-            e = gh.excess(got[sl], ref, "f32")
-            assert e <= 0, f"seed {d['seed']} chunk {c}: exceeds tolerance by {e:.3g}"
+        ref = oracle.kkt_tril_inv_packed(d["k"], d["g"], d["beta"], d["cu_seqlens"],
+                                         d["k_dtype"])
+        e = gh.excess(gh.to_numpy_f64(X), ref, "f32")
+        assert e <= 0, f"seed {d['seed']}: exceeds tolerance by {e:.3g}"

@@ -187,6 +187,12 @@ _MUTANTS = {
     "dec_padding_output": ("for (int j = 0; j < d; ++j) o_out[j] = 0.0;",
                            "for (int j = 0; j < d; ++j) o_out[j] = 1.0;"),
     "dec_no_q_scale": ("/ sqrt(nq + eps_l2) / sqrt((double)d);", "/ sqrt(nq + eps_l2);"),
+    "dec_q_eps_outside": ("1.0 / sqrt(nq + eps_l2) / sqrt((double)d);",
+                          "1.0 / (sqrt(nq) + eps_l2) / sqrt((double)d);"),
+    "dec_k_no_eps": ("const double sk = 1.0 / sqrt(nk + eps_l2);",
+                     "const double sk = 1.0 / sqrt(nk);"),
+    "dec_q_scale_d_not_sqrt": ("/ sqrt(nq + eps_l2) / sqrt((double)d);",
+                               "/ sqrt(nq + eps_l2) / (double)d;"),
 }
 
 
@@ -292,7 +298,9 @@ def _pins_fail(lib):
                               H, d, a[5].shape[1], eps_l2, eps_norm)
         return out, S, cs
 
-    return bool(pins.dec_all(dec))
+    # the brute force restates the step's formulas, so it does not count as a
+    # pin here: every planted mistake must fail a closed-form check
+    return bool([n for n in pins.dec_all(dec) if n != "brute_force"])
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -403,7 +411,7 @@ def _oracle_dec(qkv, g, beta, z, wn, cw, slot, S, cs, eps_l2, eps_norm):
 
 @pytest.mark.parametrize("check", ["check_dec_delta_rule", "check_dec_decay_only",
                                    "check_dec_conv_taps", "check_dec_padding_and_slots",
-                                   "check_dec_brute_force"])
+                                   "check_dec_q_scale", "check_dec_brute_force"])
 def test_decode_step_pins(check):
     assert getattr(pins, check)(_oracle_dec)
 

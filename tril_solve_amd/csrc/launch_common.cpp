@@ -23,33 +23,43 @@ struct OccEntry {
     bool forced;  // per_cu set by KDA_TRIL_BLOCKS_PER_CU
 };
 std::mutex g_occ_mu;
-std::vector<OccEntry> g_occ;
+std::vector<OccEntry> g_occ;  // what the device reports, per kernel and device
 
 OccEntry residency(const void *fn, int threads) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return {fn, 0, 0, 0, false};
+    OccEntry r{fn, dev, 0, 0, false};
+    bool cached = false;
     {
         std::lock_guard<std::mutex> lk(g_occ_mu);
         for (const OccEntry &e : g_occ)
-            if (e.fn == fn && e.dev == dev) return e;
+            if (e.fn == fn && e.dev == dev) {
+                r = e;
+                cached = true;
+                break;
+            }
     }
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
-        per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
-    bool forced = false;
-    // Tuning override: workgroups per compute unit the grid is sized for.
+    if (!cached) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
+            per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        r.per_cu = per_cu;
+        r.cus = cus;
+        std::lock_guard<std::mutex> lk(g_occ_mu);
+        g_occ.push_back(r);
+    }
+    // Tuning and testing override, read on every call (so one process can
+    // launch the same problem on different grids): workgroups per compute
+    // unit the grid is sized for.
     if (const char *e = getenv("KDA_TRIL_BLOCKS_PER_CU")) {
         const int v = atoi(e);
         if (v > 0) {
-            per_cu = v;
-            forced = true;
+            r.per_cu = v;
+            r.forced = true;
         }
     }
-    const OccEntry r{fn, dev, per_cu, cus, forced};
-    std::lock_guard<std::mutex> lk(g_occ_mu);
-    g_occ.push_back(r);
     return r;
 }
 }  // namespace

@@ -26,8 +26,11 @@
 // gate; exponentials per lane and 16-channel slice drop from 56 (one per
 // block pair and row) to 36: 16 for Q, 16 for P and 4 for the six c_IJ, which
 // depend on the channel only and are spread over the lanes of a 16-lane row
-// and shared by DPP broadcasts. Decays are scaled by log2(e) once so every
-// exponential is a bare v_exp_f32.
+// and shared by DPP broadcasts. Each exponent (a decay difference) is scaled
+// by log2(e) so every exponential is a bare v_exp_f32. That instruction
+// returns no subnormal results: a factor below 2^-126 is 0, which bounds the
+// domain (c for adjacent blocks spans 16 tokens of decay, so falls up to
+// about 87 over 16 consecutive tokens, 5.45 per token, are represented).
 //
 // Each product is computed transposed, D = (P_J c_IJ) Q_I^T: the MFMA
 // accumulator then holds row i of A_IJ, columns 4g..4g+3, in lane (g, i),
@@ -183,13 +186,17 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
     f4 gl[4], gr[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        gl[b] = widen4<F32>(graw[b]) * kLog2e;
+        gl[b] = widen4<F32>(graw[b]);
         // decay of the block's reference row (its row 0) in every lane
 #pragma unroll
         for (int s = 0; s < 4; ++s) gr[b][s] = row_bcast<0>(gl[b][s]);
     }
+    // Every exponent is a difference of decays taken first and scaled by
+    // log2 e after: decays a few tokens apart subtract exactly, so a caller's
+    // cumulative decays may run far from zero (over a whole request rather
+    // than restarting at each chunk) without their rounding entering.
     // c for this lane's pair (I, J), every pair's c reaching the row by
-    // broadcast: the exponent gr[I] - gr[J] as sum_b wsel[b] gr[b] with
+    // broadcast: the difference gr[I] - gr[J] as sum_b wsel[b] gr[b] with
     // wsel[b] = [b == I] - [b == J], which for finite decays is that
     // difference bit for bit (the zero terms add exact zeros, the two others
     // round once); a select on the lane's pair compiled to divergent branches.
@@ -199,7 +206,7 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
         float a = wsel[0] * gr[0][s];
 #pragma unroll
         for (int b = 1; b < 4; ++b) a = __builtin_fmaf(wsel[b], gr[b][s], a);
-        cv[s] = __builtin_amdgcn_exp2f(a);
+        cv[s] = __builtin_amdgcn_exp2f(a * kLog2e);
     }
     f4 P[4];
     // all ten products, also for blocks past a partial chunk (their P and Q
@@ -209,7 +216,7 @@ __device__ __forceinline__ void accumulate_sub(const typename Raw4<EK>::T (&kr)[
         const f4 kb = widen4<EK>(kr[b]);
         // the two exponents are exact negations of each other: one
         // subtraction, the second exponential takes it negated
-        const f4 t = gr[b] - gl[b];
+        const f4 t = (gr[b] - gl[b]) * kLog2e;
         P[b] = scaled(kb, t);
         const f4 Q = scaled(kb, -t);
         acc[b][b] = mma_kq(P[b], Q, acc[b][b]);

@@ -55,7 +55,8 @@ constexpr int kFusedThreads = 64 * kFusedWaves;
 
 // Workgroups of `threads` threads of kernel `fn` that the current device
 // holds at once (occupancy x compute units; KDA_TRIL_BLOCKS_PER_CU, when set,
-// replaces the occupancy); 0 when unknown. Cached.
+// replaces the occupancy, read on every call); 0 when unknown. The device's
+// occupancy is cached per kernel and device.
 long resident_blocks(const void *fn, int threads);
 
 // Grid of a grid-stride kernel with kFusedWaves independent wavefronts per
