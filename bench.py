@@ -66,8 +66,9 @@ def kernel_of(workload: str):
         return r"kda_decode_step_kernel<", ["tril_device.h", "kda_decode.hip", "tril_launch.h"]
     import synth
     C = synth.CONFIGS[workload].get("chunk", 64)
-    if C == 64:
-        return r"tril_inv_fused_mfma<", ["tril_device.h", "tril_fused.hip", "tril_launch.h"]
+    if C == 64:  # one-round launches run the per-wavefront kernel, longer ones the 4-head one
+        return r"tril_inv_fused_(heads4|mfma)<", ["tril_device.h", "tril_fused.hip",
+                                                  "tril_launch.h", "launch_common.cpp"]
     return rf"tril_inv_c{C}<", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
 
 
@@ -99,7 +100,63 @@ def load_copy_probe():
     lib.kda_probe_copy_f32.restype = ctypes.c_int
     lib.kda_probe_copy_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]
+    lib.kda_probe_stream.restype = ctypes.c_int
+    lib.kda_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_void_p]
     return lib
+
+
+PROBE_KINDS = {"copy": 0, "read": 1, "fill": 2}
+PROBE_POLICIES = {"default": 0, "nontemporal": 1, "nt_stores": 2}
+
+
+def probe_bytes(kind: str, nbytes: int) -> int:
+    """HBM bytes one streaming probe moves over a buffer of nbytes: a copy
+    reads and writes it, a read or a fill touches it once."""
+    return 2 * nbytes if kind == "copy" else nbytes
+
+
+def probe_sweep(torch, stream, dev, tensors, reps=20):
+    """Streaming probes (copy, read-only, write-only) over the rotation of
+    `tensors` (each a source of the same size, with a destination of its
+    own), every unroll, cache policy and grid size; prints one JSON line per
+    setting to stdout and returns the fastest setting per kind."""
+    lib = load_copy_probe()
+    n = tensors[0].numel() * tensors[0].element_size() // 4
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    dsts = [torch.empty(n, dtype=torch.float32, device=dev) for _ in tensors]
+    best = {}
+    grids = [cus * k for k in (1, 2, 4, 8, 16, 32)] + [min(n // 4 // 256, 1 << 20)]
+    for kind, kc in PROBE_KINDS.items():
+        for pol, pc in PROBE_POLICIES.items():
+            if kind == "read" and pc == 2:
+                continue  # no stores to make nontemporal
+            for unroll in (1, 2, 4, 8):
+                for blocks in grids:
+                    args = [(kc, unroll, pc, ctypes.c_void_p(t.data_ptr()),
+                             ctypes.c_void_p(d.data_ptr()), n, d.numel(), blocks,
+                             ctypes.c_void_p(stream.cuda_stream))
+                            for t, d in zip(tensors, dsts)]
+                    for a in args[:2]:
+                        if lib.kda_probe_stream(*a) != 0:
+                            raise RuntimeError(f"probe {kind} failed")
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for i in range(reps):
+                        lib.kda_probe_stream(*args[i % len(args)])
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / reps
+                    gbs = probe_bytes(kind, 4 * n) / (us * 1e-6) / 1e9
+                    row = {"probe": kind, "policy": pol, "unroll": unroll, "blocks": blocks,
+                           "blocks_per_cu": round(blocks / cus, 2), "us": round(us, 2),
+                           "gbs": round(gbs, 1), "frac_of_8tbs": round(gbs / HBM_PEAK_GBS, 4)}
+                    print(json.dumps(row), flush=True)
+                    if kind not in best or gbs > best[kind]["gbs"]:
+                        best[kind] = row
+    return best
 
 
 def _code_only(text: str) -> str:
@@ -488,6 +545,11 @@ def run_solve(args, torch, np, dev, stream):
     copy = CopyProbe(torch, stream, dev)
     if args.probe == "copy":
         return copy.only([A for A, _ in sets], args)
+    if args.probe == "sweep":
+        best = probe_sweep(torch, stream, dev, [A for A, _ in sets])
+        print(json.dumps({"best": best, "buffer_bytes": A.numel() * A.element_size(),
+                          "rotation": len(sets)}), flush=True)
+        return 0
 
     cmap = None
     if args.chunk_map and not dense:  # built once on the host, reused by every call
@@ -684,8 +746,11 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0,
                     help="rotating input/output buffer sets (default: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", choices=["copy"], default=None,
-                    help="run only a plain copy of the input's byte count (counter calibration)")
+    ap.add_argument("--probe", choices=["copy", "sweep"], default=None,
+                    help="copy: run only a plain copy of the input's byte count (counter "
+                         "calibration); sweep: streaming copy / read / fill probes over the "
+                         "input rotation at every unroll, cache policy and grid size (one JSON "
+                         "line each, then the fastest per kind)")
     ap.add_argument("--record-traffic", nargs=5, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
                     help="write the HBM-traffic summary of --workload from rocprofv3 counter "

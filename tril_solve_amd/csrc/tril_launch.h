@@ -70,6 +70,11 @@ long resident_blocks(const void *fn, int threads);
 // memory system with fewer requests in flight while the others finish.
 long walk_blocks(const void *fn, long waves, long min_waves);
 
+// Grid of a grid-stride kernel whose workgroups (kFusedThreads threads) walk
+// `groups` work items together: what the device holds at once, one workgroup
+// per CU fewer for long problems (16 or more rounds), at most `groups`.
+long group_blocks(const void *fn, long groups);
+
 // Element-type codes of A and X: the kda_dtype values (0 f32, 1 bf16, 2 f16).
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
 hipError_t launch_split(const Problem &p, int a_dt, int x_dt, hipStream_t stream);
