@@ -142,6 +142,9 @@ typedef __attribute__((address_space(3))) void *LdsPtr;
 // This wavefront's share of a group's loads: pair slots wid, wid + 4, ... and
 // (FP32) the row slots of rows 32 + wid, 36 + wid, ... Lanes of heads past
 // the last head (nh < 4) use an out-of-range offset: their LDS bytes get 0.
+// Every line is read by exactly one instruction, so the loads carry the
+// nontemporal bit (same-box A/B: 16 x 512 tokens 42.9 -> 42.2 us, 48 ragged
+// requests 121.9 -> 117.9 us, 131,072 tokens 607 -> 583 us).
 template <class EI>
 __device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *lds, int wid,
                                            int lane) {
@@ -154,8 +157,7 @@ __device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *ld
         const int p = wid + 4 * q;
         const int row = 16 * (p >> 3) + (p & 7) + 8 * half;
         const uint32_t off = ((uint32_t)(row * rstride + ph * 64) * EI::kBytes + 16 * piece) | pmask;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(lds + p * kSlotBytes), 16, off, 0, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(lds + p * kSlotBytes), 16, off, 0, 0, kNontemporal);
     }
     const uint32_t rmask = (lane >> 4) < nh ? 0u : kOffMasked;
 #pragma unroll
@@ -163,7 +165,7 @@ __device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *ld
         const int row = 32 + wid + 4 * q;
         const uint32_t off = ((uint32_t)(row * rstride) * EI::kBytes + 16 * lane) | rmask;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (LdsPtr)(lds + (L::kPairSlots + row - 32) * kSlotBytes), 16, off, 0, 0, 0);
+            r, (LdsPtr)(lds + (L::kPairSlots + row - 32) * kSlotBytes), 16, off, 0, 0, kNontemporal);
     }
 }
 
