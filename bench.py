@@ -402,41 +402,58 @@ def graph_replay(torch, launch_all, n_calls, replays=50):
 
 
 class CopyProbe:
-    """A plain streaming copy (read N, write N bytes) of a tensor's bytes into
-    a destination of its own, marshalled once per source."""
+    """Streaming copies of a tensor's bytes into a destination of its own
+    (one per source): the plain copy (counter calibration) and the fastest
+    copy of the probe sweep (the measured ceiling)."""
 
     def __init__(self, torch, stream, dev):
         self.torch, self.stream, self.dev = torch, stream, dev
         self.lib = load_copy_probe()
-        self.calls = {}
+        self.dst = {}
 
-    def __call__(self, A):
-        fn = self.calls.get(A.data_ptr())
-        if fn is None:
+    def _dst(self, A):
+        D = self.dst.get(A.data_ptr())
+        if D is None:
             nbytes = A.numel() * A.element_size()
             D = self.torch.empty(nbytes // 4, dtype=self.torch.float32, device=self.dev)
             if nbytes % 16 or D.numel() * 4 != nbytes:
                 raise RuntimeError("copy probe: source and destination sizes differ")
-            cargs = (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()), nbytes // 4,
-                     ctypes.c_void_p(self.stream.cuda_stream))
-            f = self.lib.kda_probe_copy_f32
+            self.dst[A.data_ptr()] = D
+        return D
 
-            def fn(D=D):
-                if f(*cargs) != 0:
-                    raise RuntimeError("copy probe failed")
-            self.calls[A.data_ptr()] = fn
-        fn()
+    def __call__(self, A):
+        """The plain copy (one thread per 16 bytes, default cache policy)."""
+        D = self._dst(A)
+        if self.lib.kda_probe_copy_f32(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(D.data_ptr()),
+                                       D.numel(), ctypes.c_void_p(self.stream.cuda_stream)) != 0:
+            raise RuntimeError("copy probe failed")
 
-    def rate_gbs(self, tensors, ncopy=40):
-        """Read + write bytes per second of the copy over the rotation."""
+    def tuned(self, A):
+        """The fastest copy of the probe sweep: one nontemporal 16-byte load
+        and store per thread."""
+        D = self._dst(A)
+        n = D.numel()
+        st = self.lib.kda_probe_stream(PROBE_KINDS["copy"], 1, PROBE_POLICIES["nontemporal"],
+                                       ctypes.c_void_p(A.data_ptr()),
+                                       ctypes.c_void_p(D.data_ptr()), n, n,
+                                       max(1, min(n // 4 // 256, 1 << 20)),
+                                       ctypes.c_void_p(self.stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError("tuned copy probe failed")
+
+    def rate_gbs(self, tensors, ncopy=40, tuned=True):
+        """Read + write bytes per second of a copy over the rotation: the
+        fastest streaming copy of the probe sweep (one nontemporal 16-byte
+        load and store per thread) when `tuned`, else the plain copy."""
         torch = self.torch
+        fn = self.tuned if tuned else self
         for i in range(4):
-            self(tensors[i % len(tensors)])
+            fn(tensors[i % len(tensors)])
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c0.record(self.stream)
         for i in range(ncopy):
-            self(tensors[i % len(tensors)])
+            fn(tensors[i % len(tensors)])
         c1.record(self.stream)
         torch.cuda.synchronize()
         copy_s = c0.elapsed_time(c1) * 1e-3 / ncopy
@@ -565,6 +582,7 @@ def run_solve(args, torch, np, dev, stream):
     # measured copy roofline: a plain streaming copy of A's byte count, read
     # and written, same buffer rotation, events over the region
     copy_gbs = copy.rate_gbs([A for A, _ in sets]) if a_bytes == 4 else None
+    copy_plain = copy.rate_gbs([A for A, _ in sets], tuned=False) if a_bytes == 4 else None
 
     h200 = H200_INV_PER_S.get(args.workload)
     metric = METRIC if C == 64 else f"{C}x{C} tril inverses/sec + achieved HBM GB/s (% peak)"
@@ -580,6 +598,7 @@ def run_solve(args, torch, np, dev, stream):
     if args.algo in ("auto", "fused") and chosen == "fused":
         with_measured_hbm(out, load_traffic(args.workload))
     out["copy_roofline_gbs"] = copy_gbs
+    out["copy_plain_gbs"] = copy_plain
     if not args.no_cpu_baseline and args.workload == MAIN_WORKLOAD:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(d0)
