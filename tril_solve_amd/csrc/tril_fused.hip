@@ -364,9 +364,16 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
     return hipGetLastError();
 }
 
-static bool heads4_selected() {
+// KDA_TRIL_FUSED_LAYOUT (read on every call): "wave" runs the per-wavefront
+// kernel for every launch, "heads4" the 4-head kernel for every launch (one
+// round or not; the tests use it to reach its edge cases on small problems);
+// anything else, or unset, chooses by the number of rounds.
+enum class Layout { kAuto, kWave, kHeads4 };
+static Layout fused_layout() {
     const char *e = getenv("KDA_TRIL_FUSED_LAYOUT");
-    return !(e && strcmp(e, "wave") == 0);
+    if (e && strcmp(e, "wave") == 0) return Layout::kWave;
+    if (e && strcmp(e, "heads4") == 0) return Layout::kHeads4;
+    return Layout::kAuto;
 }
 
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
@@ -375,7 +382,8 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
         const long blocks = walk_blocks(
             reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves,
             min_chunks(p, kChunk) * p.heads);
-        if (blocks * kFusedWaves < waves && heads4_selected()) {
+        const Layout lay = fused_layout();
+        if (lay == Layout::kHeads4 || (lay == Layout::kAuto && blocks * kFusedWaves < waves)) {
             const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);
