@@ -67,8 +67,9 @@ def kernel_of(workload: str):
     import synth
     C = synth.CONFIGS[workload].get("chunk", 64)
     if C == 64:  # one-round launches run the per-wavefront kernel, longer ones the 4-head one
-        return r"tril_inv_fused_(heads4|mfma)<", ["tril_device.h", "tril_fused.hip",
-                                                  "tril_launch.h", "launch_common.cpp"]
+        return r"tril_inv_fused_(heads4|mfma)<", ["tril_device.h", "tril_group.h",
+                                                  "tril_fused.hip", "tril_launch.h",
+                                                  "launch_common.cpp"]
     return rf"tril_inv_c{C}<", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
 
 

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include "tril_device.h"
+#include "tril_group.h"
 #include "tril_launch.h"
 
 namespace kda {
@@ -96,152 +97,42 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 
 // ------------------------------------------------------------------------
 // Multi-head form of the same kernel, for launches in which wavefronts walk
-// several items. A workgroup of four wavefronts owns (chunk, four adjacent
-// heads): the lines of the four heads' tiles that the solve needs go from HBM
-// straight into LDS (buffer loads with the LDS bit, no VGPRs), each load
-// instruction covering one token's row of the four heads (1 KiB of adjacent
-// bytes) or two tokens' first lines of the four heads; then every wavefront
-// reads its own head's blocks from LDS in the layouts of the solve and runs
-// the same diagonal solve, merge and stores as the kernel above. Four heads'
-// rows are adjacent in HBM, so each load instruction covers long runs instead
-// of 64-byte pieces 16 KiB apart: measured with loads and stores alone on 16 x
-// 512 tokens, 64 heads, the pattern takes 40.0-40.4 us against 42.2 us.
+// several items. A workgroup of four wavefronts owns a group (chunk, four
+// adjacent heads): the lines of the four heads' tiles that the solve needs go
+// from HBM straight into LDS, each load instruction covering one token's row
+// of the four heads (1 KiB of adjacent bytes) or two tokens' first lines of
+// the four heads; then every wavefront reads its own head's blocks from LDS
+// in the layouts of the solve and runs the same diagonal solve, merge and
+// stores as the kernel above. Measured with loads and stores alone on 16 x
+// 512 tokens, 64 heads, this load pattern takes 40.0-40.4 us against 42.2 us
+// for the per-wavefront one.
 //
-// LDS tile layout (bytes), in slots of kSlotBytes (1 KiB plus 16 bytes, so
-// the 16 rows a block read touches fall on different banks):
-//   pair slots: two tokens r and r + 8 of one block row, each as the first
-//     128 bytes of heads 0..3 (512 bytes); the second token's heads are
-//     rotated by one position so that the two rows sit 128 bytes apart in
-//     bank order. FP32 input: the 32 rows of block rows 0 and 1 (they need
-//     columns 0..31, one line per head); 16-bit input: all 64 rows (a head's
-//     row is one 128-byte line).
-//   row slots (FP32 only): rows 32..63, all 256 bytes of heads 0..3.
-constexpr int kGroupHeads = 4;
-constexpr int kSlotBytes = 1040;
-
+// The solve needs columns 0..31 of block rows 0 and 1 (one line per FP32
+// row) and whole rows of block rows 2 and 3; a 16-bit row is one line.
 template <class EI>
-struct GroupTile {
-    static constexpr int kPairSlots = EI::kBytes == 4 ? 16 : 32;
-    static constexpr int kRowSlots = EI::kBytes == 4 ? 32 : 0;
-    static constexpr int kBytes = (kPairSlots + kRowSlots) * kSlotBytes;
-    static_assert(kBytes >= kGroupHeads * kLdsPerWave * 4,
-                  "the solve's LDS regions must fit in the tile's");
-
-    // byte address of row R, head position hh, byte column bc of that head
-    __device__ static __forceinline__ int addr(int R, int hh, int bc) {
-        if (EI::kBytes == 4 && R >= 32)
-            return (kPairSlots + R - 32) * kSlotBytes + hh * 256 + bc;
-        const int p = (R >> 4) * 8 + (R & 7), half = (R >> 3) & 1;
-        const int pos = half ? (hh + 3) & 3 : hh;
-        return p * kSlotBytes + half * 512 + pos * 128 + bc;
-    }
-};
-
-typedef __attribute__((address_space(3))) void *LdsPtr;
-
-// This wavefront's share of a group's loads: pair slots wid, wid + 4, ... and
-// (FP32) the row slots of rows 32 + wid, 36 + wid, ... Lanes of heads past
-// the last head (nh < 4) use an out-of-range offset: their LDS bytes get 0.
-// Every line is read by exactly one instruction, so the loads carry the
-// nontemporal bit (same-box A/B: 16 x 512 tokens 42.9 -> 42.2 us, 48 ragged
-// requests 121.9 -> 117.9 us, 131,072 tokens 607 -> 583 us).
-template <class EI>
-__device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *lds, int wid,
-                                           int lane) {
-    typedef GroupTile<EI> L;
-    const int half = lane >> 5, pos = (lane >> 3) & 3, piece = lane & 7;
-    const int ph = half ? (pos + 1) & 3 : pos;  // head whose bytes land at this position
-    const uint32_t pmask = ph < nh ? 0u : kOffMasked;
-#pragma unroll
-    for (int q = 0; q < L::kPairSlots / 4; ++q) {
-        const int p = wid + 4 * q;
-        const int row = 16 * (p >> 3) + (p & 7) + 8 * half;
-        const uint32_t off = ((uint32_t)(row * rstride + ph * 64) * EI::kBytes + 16 * piece) | pmask;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(lds + p * kSlotBytes), 16, off, 0, 0, kNontemporal);
-    }
-    const uint32_t rmask = (lane >> 4) < nh ? 0u : kOffMasked;
-#pragma unroll
-    for (int q = 0; q < L::kRowSlots / 4; ++q) {
-        const int row = 32 + wid + 4 * q;
-        const uint32_t off = ((uint32_t)(row * rstride) * EI::kBytes + 16 * lane) | rmask;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (LdsPtr)(lds + (L::kPairSlots + row - 32) * kSlotBytes), 16, off, 0, 0, kNontemporal);
-    }
-}
-
-// Columns c..c+3 of row R of head position hh, widened to FP32.
-template <class EI>
-__device__ __forceinline__ f4 lds_quad(const char *lds, int R, int hh, int c);
-template <>
-__device__ __forceinline__ f4 lds_quad<F32>(const char *lds, int R, int hh, int c) {
-    return *reinterpret_cast<const f4 *>(lds + GroupTile<F32>::addr(R, hh, 4 * c));
-}
-template <>
-__device__ __forceinline__ f4 lds_quad<BF16>(const char *lds, int R, int hh, int c) {
-    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-    const u2 v = *reinterpret_cast<const u2 *>(lds + GroupTile<BF16>::addr(R, hh, 2 * c));
-    f4 o;
-    o[0] = bf16_to_f32(v[0] & 0xFFFFu);
-    o[1] = bf16_to_f32(v[0] >> 16);
-    o[2] = bf16_to_f32(v[1] & 0xFFFFu);
-    o[3] = bf16_to_f32(v[1] >> 16);
-    return o;
-}
-// (A vector of binary16 values, as the global loads widen them: converting
-// single 16-bit lanes of an integer vector through bit casts lost three of
-// every four elements in this compiler's output.)
-template <>
-__device__ __forceinline__ f4 lds_quad<F16>(const char *lds, int R, int hh, int c) {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 v = *reinterpret_cast<const h4 *>(lds + GroupTile<F16>::addr(R, hh, 2 * c));
-    f4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (float)v[e];  // exact widening
-    return o;
-}
+using FusedPlan = GroupPlan<EI, kLine0, kLine0, kBoth, kBoth>;
 
 // Head position hh's tile from the group's LDS copy, in the registers of the
-// solve: diagonal blocks one row per lane (lane (b, i): row 16b + i, columns
-// 16b + 4q..+3 in dg[q]), blocks below the diagonal in OPND_A.
+// solve: diagonal blocks one row per lane, blocks below the diagonal in
+// OPND_A.
 template <class EI>
 __device__ __forceinline__ void read_tile(Tile &t, const char *lds, int hh, int lane) {
-    const int hi = lane >> 4, lo = lane & 15;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t.dg[q] = lds_quad<EI>(lds, 16 * hi + lo, hh, 16 * hi + 4 * q);
-#pragma unroll
-    for (int I = 1; I < 4; ++I)
-#pragma unroll
-        for (int K = 0; K < I; ++K) t.blk[I][K] = lds_quad<EI>(lds, 16 * I + lo, hh, 16 * K + 4 * hi);
+    read_diag_rows<EI, FusedPlan<EI>>(t.dg, lds, hh, lane);
+    read_offdiag_blocks<EI, FusedPlan<EI>>(t.blk, lds, hh, lane);
 }
 
-// A group of four heads of one chunk slot (len 0: nothing to do).
-struct Group {
-    Chunk ch;
-    int h0, nh;
-};
-
-template <class EI>
-__device__ __forceinline__ Group group_of(const Problem &p, int gi, int hg, int lane) {
-    Group gr;
-    const int slot = gi / hg;
-    gr.h0 = (gi - slot * hg) * kGroupHeads;
-    gr.nh = min(kGroupHeads, p.heads - gr.h0);
-    gr.ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
-    return gr;
-}
-
-template <class EI>
-__device__ __forceinline__ void load_group_of(const Problem &p, const Group &gr, char *lds,
-                                              int wid, int lane) {
-    const long row0 = (long)gr.ch.start * p.heads + gr.h0;
-    const TileView<EI> A{static_cast<const typename EI::T *>(p.A) + row0 * kChunk,
-                         p.heads * kChunk, gr.ch.len, gr.nh * kChunk};
-    load_group<EI>(A.rows_from(0), A.rstride, gr.nh, lds, wid, lane);
-}
-
+// (Issuing the next group's loads as soon as every wavefront has read the
+// current tile, with the inverses and staging in LDS of their own so that
+// the loads land while the tile is solved, was measured too: 70,400 bytes of
+// LDS per workgroup leave two workgroups per CU, and on the same box and
+// buffers 16 x 512 tokens took 42.3 against 42.0 us, 48 ragged requests
+// 117.9 against 117.2 us, 131,072 tokens 607 against 582 us.)
 template <class EI, class EO>
 __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_heads4(Problem p) {
-    __shared__ __attribute__((aligned(16))) char lds[GroupTile<EI>::kBytes];
+    typedef FusedPlan<EI> Plan;
+    static_assert(Plan::kBytes >= kGroupHeads * kLdsPerWave * 4,
+                  "the solve's LDS regions must fit in the tile's");
+    __shared__ __attribute__((aligned(16))) char lds[Plan::kBytes];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // once a group's tiles are in registers, the tile region holds each
@@ -252,13 +143,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_heads4(Problem p
     const int hg = (p.heads + kGroupHeads - 1) / kGroupHeads;
     const int groups = p.slots * hg;
     for (int gi = blockIdx.x; gi < groups; gi += gridDim.x) {
-        // the same chunk for the whole workgroup: every wavefront takes the
-        // same branches and meets the same barriers
-        const Group gr = group_of<EI>(p, gi, hg, lane);
+        const Group gr = group_of(p, gi, hg, lane);
         if (gr.ch.len <= 0) continue;
-        load_group_of<EI>(p, gr, lds, wid, opaque_lane(lane));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // every wavefront's share of the group has arrived
+        load_group_of<EI, Plan>(p, gr, lds, wid, opaque_lane(lane));
+        group_arrived();
         Tile t;
         read_tile<EI>(t, lds, wid, opaque_lane(lane));
         __syncthreads();  // every wavefront has its tile: the region is free
