@@ -1,15 +1,16 @@
-"""GPU tests of the fused solver's 4-head kernel on its edge cases.
+"""GPU tests of the solver's 4-head kernels on their edge cases.
 
-Launches that take more than one round of the GPU run the 4-head kernel (a
+Launches that take more than one round of the GPU run the 4-head kernels (a
 workgroup owns one chunk and four adjacent heads, their tiles loaded into
-LDS); the large workloads of the parity tests reach it with 64 heads.
-KDA_TRIL_FUSED_LAYOUT=heads4 makes every launch use it, so these tests reach
-its edge cases on small problems: head counts that are not a multiple of four
-(the last group masks the missing heads), partial chunks, every input and
-output type, a caller chunk map, garbage above the diagonal and malformed
-cu_seqlens. Every case is compared with the oracle and, bit for bit, with the
-per-wavefront kernel (KDA_TRIL_FUSED_LAYOUT=wave), which runs the same
-arithmetic.
+LDS): the fused kernel, and the split plan's diagonal and merge kernels. The
+large workloads of the parity tests reach them with 64 heads.
+KDA_TRIL_FUSED_LAYOUT=heads4 (fused) and KDA_TRIL_SPLIT_LAYOUT=heads4 (split)
+make every launch use them, so these tests reach their edge cases on small
+problems: head counts that are not a multiple of four (the last group masks
+the missing heads), partial chunks, every input and output type, a caller
+chunk map, garbage above the diagonal and malformed cu_seqlens. Every case is
+compared with the oracle and, bit for bit, with the per-wavefront kernels
+(layout "wave"), which run the same arithmetic.
 """
 import numpy as np
 import pytest
@@ -35,20 +36,29 @@ def kt():
     return tril_solve_amd
 
 
-def _both_layouts(kt, monkeypatch, call):
+LAYOUT_ENV = {"fused": "KDA_TRIL_FUSED_LAYOUT", "split": "KDA_TRIL_SPLIT_LAYOUT"}
+
+
+@pytest.fixture(params=sorted(LAYOUT_ENV))
+def algo(request):
+    return request.param
+
+
+def _both_layouts(kt, monkeypatch, call, algo):
     """call() under the 4-head layout and under the per-wavefront one."""
+    env = LAYOUT_ENV[algo]
     out = {}
     for lay in ("heads4", "wave"):
-        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
+        monkeypatch.setenv(env, lay)
         out[lay] = call()
         torch.cuda.synchronize()
-    monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT")
+    monkeypatch.delenv(env)
     return out["heads4"], out["wave"]
 
 
 @pytest.mark.parametrize("H", [1, 2, 3, 4, 5, 7])
-def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
-    print(f"\n[heads4] H={H}", flush=True)
+def test_head_counts_and_partial_chunks(kt, monkeypatch, algo, H):
+    print(f"\n[heads4] {algo} H={H}", flush=True)
     A = synth.delta_rule_A(LENGTHS, H, seed=300 + H, upper="nan")
     cu = synth.cu_seqlens(LENGTHS)
     T = A.shape[0]
@@ -57,10 +67,10 @@ def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
 
     def run():
         X = torch.full((T + PAD, H, 64), CANARY, device=DEV)
-        kt.kda_tril_inv_packed(Ad[:T], X[:T], cud, algo="fused")
+        kt.tril_inv(Ad[:T], cud, algo=algo, out=X[:T])  # allocates the split workspace
         return X
 
-    X4, Xw = _both_layouts(kt, monkeypatch, run)
+    X4, Xw = _both_layouts(kt, monkeypatch, run, algo)
     assert torch.equal(X4, Xw)
     X = X4.cpu().numpy().astype(np.float64)
     assert np.all(X[T:] == CANARY), "a row past the last request was written"
@@ -70,7 +80,7 @@ def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
 
 @pytest.mark.parametrize("a_dtype,x_dtype", [("f32", "bf16"), ("bf16", "f32"), ("f16", "f16"),
                                              ("bf16", "bf16")])
-def test_dtypes(kt, monkeypatch, a_dtype, x_dtype):
+def test_dtypes(kt, monkeypatch, algo, a_dtype, x_dtype):
     H = 6
     A32 = synth.delta_rule_A(LENGTHS, H, seed=310)
     A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
@@ -79,25 +89,25 @@ def test_dtypes(kt, monkeypatch, a_dtype, x_dtype):
     cud = torch.from_numpy(cu).to(DEV)
     xt = gh.out_torch_dtype(x_dtype)
     X4, Xw = _both_layouts(kt, monkeypatch,
-                           lambda: kt.tril_inv(Ad, cud, out_dtype=xt, algo="fused"))
+                           lambda: kt.tril_inv(Ad, cud, out_dtype=xt, algo=algo), algo)
     assert torch.equal(X4, Xw)
     ref = oracle.tril_inv_packed(A, cu, a_dtype)
     assert gh.excess(gh.to_numpy_f64(X4), ref, x_dtype) <= 0
 
 
-def test_dense_layout_and_chunk_map(kt, monkeypatch):
+def test_dense_layout_and_chunk_map(kt, monkeypatch, algo):
     H = 5
     B, T = 3, 150
     A = synth.delta_rule_A([T] * B, H, seed=320)
     Ad = torch.from_numpy(A).to(DEV)
     X4, Xw = _both_layouts(kt, monkeypatch,
-                           lambda: kt.tril_inv(Ad.view(B, T, H, 64), algo="fused"))
+                           lambda: kt.tril_inv(Ad.view(B, T, H, 64), algo=algo), algo)
     assert torch.equal(X4, Xw)
     cu = synth.cu_seqlens([T] * B)
     cud = torch.from_numpy(cu).to(DEV)
     cmap = torch.from_numpy(gh.host_chunk_map([T] * B)).to(DEV)
     Xm, _ = _both_layouts(kt, monkeypatch,
-                          lambda: kt.tril_inv(Ad, cud, chunk_indices=cmap, algo="fused"))
+                          lambda: kt.tril_inv(Ad, cud, chunk_indices=cmap, algo=algo), algo)
     assert torch.equal(Xm.view(B, T, H, 64), X4)
     ref = oracle.tril_inv_packed(A, cu)
     assert gh.excess(gh.to_numpy_f64(Xm), ref, "f32") <= 0
@@ -106,7 +116,7 @@ def test_dense_layout_and_chunk_map(kt, monkeypatch):
 @pytest.mark.parametrize("cu,clamped", [([0, 64, 200], [0, 64, 100]),
                                         ([-40, 64, 100], [24, 64, 100]),
                                         ([0, 64, 100, 300], [0, 64, 100, 100])])
-def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
+def test_malformed_cu_seqlens_clamped(kt, monkeypatch, algo, cu, clamped):
     """Chunks outside rows [0, T) are skipped or cut at T, as for the other
     kernels: nothing past T is read (NaN there) or written (canaries)."""
     H = 3
@@ -117,10 +127,10 @@ def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
 
     def run():
         X = torch.full((T + PAD, H, 64), CANARY, device=DEV)
-        kt.tril_inv(Ad[:T], cud, algo="fused", out=X[:T])
+        kt.tril_inv(Ad[:T], cud, algo=algo, out=X[:T])
         return X
 
-    X4, Xw = _both_layouts(kt, monkeypatch, run)
+    X4, Xw = _both_layouts(kt, monkeypatch, run, algo)
     assert torch.equal(X4, Xw)
     X = X4.cpu().numpy().astype(np.float64)
     assert np.all(X[T:] == CANARY)
@@ -132,7 +142,7 @@ def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
     assert gh.excess(X[:T][rows], ref[rows], "f32") <= 0
 
 
-def test_exact_subdiagonal_bitwise(kt, monkeypatch):
+def test_exact_subdiagonal_bitwise(kt, monkeypatch, algo):
     """A single subdiagonal c: X = (-c)^(i-j), every FP32 operation exact."""
     H, c = 7, -0.5
     lengths = [64, 40, 64]
@@ -146,7 +156,7 @@ def test_exact_subdiagonal_bitwise(kt, monkeypatch):
         bos += n
     cud = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
     Ad = torch.from_numpy(A).to(DEV)
-    X4, _ = _both_layouts(kt, monkeypatch, lambda: kt.tril_inv(Ad, cud, algo="fused"))
+    X4, _ = _both_layouts(kt, monkeypatch, lambda: kt.tril_inv(Ad, cud, algo=algo), algo)
     X = X4.cpu().numpy()
     bos = 0
     for n in lengths:

@@ -560,7 +560,7 @@ __device__ __forceinline__ void store_block_row(const TileView<E> &X, const f4 (
 
 // Merge products on the matrix cores: mm(P, Q, acc) = acc + P Q with P in
 // OPND_A and Q in OPND_O; negx(I, S) = -X_II S with X_II read (negated, in
-// OPND_A) from the column-major copy xs.
+// OPND_A) from the column-major copy xs; xkk(K) = X_KK in OPND_O.
 template <int BS, int CS>
 struct MfmaEngine {
     const float *xs;
@@ -570,38 +570,39 @@ struct MfmaEngine {
         const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
         return mma16(xs_opnd_a_neg<BS, CS>(xs, I, lane), S, z);
     }
+    __device__ __forceinline__ f4 xkk(int K) const { return xs_opnd_o<BS, CS>(xs, K, lane); }
 };
 
 // Block merge and stores, one block row at a time (the rows of block row I
 // are written as soon as X_I0..X_II are known):
 //   X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ,  I > J,
-// FP32 throughout. X_KK come from the column-major copy xs (LDS in the fused
-// kernel, the workspace in the split path); the products run in the same
-// order in both, so their results agree bit for bit. `stage` may alias xs
-// (the fused kernel): everything block row I needs from blocks 0..I of xs is
-// read before block row I is staged, and block row I's staging covers at most
-// the first 16 * stage_row(I) floats, which ends inside block I.
-template <class E, int BS, int CS, class Eng>
+// FP32 throughout. X_KK come from the engine (eng.xkk, eng.negx: a
+// column-major copy in LDS in the fused kernel, the workspace in the split
+// path); the products run in the same order in both, so their results agree
+// bit for bit. `stage` may alias the engine's LDS copy (the fused kernel):
+// everything block row I needs from blocks 0..I of it is read before block
+// row I is staged, and block row I's staging covers at most the first
+// 16 * stage_row(I) floats, which ends inside block I.
+template <class E, class Eng>
 __device__ __forceinline__ void merge_and_store(const Eng &eng, const f4 (&blk)[4][4],
-                                                const float *xs, float *stage,
-                                                const TileView<E> &X, int lane) {
+                                                float *stage, const TileView<E> &X, int lane) {
     const int len = X.len;
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     f4 xo[4] = {z, z, z, z};
     // block row 0
-    const f4 x00 = xs_opnd_o<BS, CS>(xs, 0, lane);
+    const f4 x00 = eng.xkk(0);
     xo[0] = x00;
     store_block_row<E, 0>(X, xo, stage, lane);
     if (len <= 16) return;
     // block row 1
-    const f4 x11 = xs_opnd_o<BS, CS>(xs, 1, lane);
+    const f4 x11 = eng.xkk(1);
     const f4 x10 = eng.negx(1, eng.mm(blk[1][0], x00, z));
     xo[0] = x10;
     xo[1] = x11;
     store_block_row<E, 1>(X, xo, stage, lane);
     if (len <= 32) return;
     // block row 2
-    const f4 x22 = xs_opnd_o<BS, CS>(xs, 2, lane);
+    const f4 x22 = eng.xkk(2);
     const f4 s21 = eng.mm(blk[2][1], x11, z);
     const f4 s20 = eng.mm(blk[2][1], x10, eng.mm(blk[2][0], x00, z));
     const f4 x21 = eng.negx(2, s21);
@@ -612,7 +613,7 @@ __device__ __forceinline__ void merge_and_store(const Eng &eng, const f4 (&blk)[
     store_block_row<E, 2>(X, xo, stage, lane);
     if (len <= 48) return;
     // block row 3
-    const f4 x33 = xs_opnd_o<BS, CS>(xs, 3, lane);
+    const f4 x33 = eng.xkk(3);
     const f4 s32 = eng.mm(blk[3][2], x22, z);
     const f4 s31 = eng.mm(blk[3][2], x21, eng.mm(blk[3][1], x11, z));
     const f4 s30 = eng.mm(blk[3][2], x20, eng.mm(blk[3][1], x10, eng.mm(blk[3][0], x00, z)));

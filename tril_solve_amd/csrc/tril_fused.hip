@@ -56,7 +56,7 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
     float arow[16];
     tile_diag_rows<ROWS>(t, arow);
     diag_inverses(xs, arow, lane);
-    merge_and_store<EO, kXsBlock, kXsCol>(eng, t.blk, xs, stage, X, lane);
+    merge_and_store<EO>(eng, t.blk, stage, X, lane);
 }
 
 // Wavefronts per workgroup: four independent ones for the launches that walk
@@ -107,10 +107,12 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 // 512 tokens, 64 heads, this load pattern takes 40.0-40.4 us against 42.2 us
 // for the per-wavefront one.
 //
-// The solve needs columns 0..31 of block rows 0 and 1 (one line per FP32
-// row) and whole rows of block rows 2 and 3; a 16-bit row is one line.
+// The solve needs columns 0..31 of block rows 0 and 1 and columns 0..63 of
+// block rows 2 and 3; rows of 16-bit elements are loaded whole, as one
+// 128-byte line each.
 template <class EI>
-using FusedPlan = GroupPlan<EI, kLine0, kLine0, kBoth, kBoth>;
+using FusedPlan = GroupPlan<EI, cols(0, EI::kBytes == 4 ? 32 : 64),
+                            cols(0, EI::kBytes == 4 ? 32 : 64), cols(0, 64), cols(0, 64)>;
 
 // Head position hh's tile from the group's LDS copy, in the registers of the
 // solve: diagonal blocks one row per lane, blocks below the diagonal in
@@ -214,6 +216,10 @@ struct ValuEngine {
         }
         wave_sync();
         return acc;
+    }
+
+    __device__ __forceinline__ f4 xkk(int K) const {
+        return xs_opnd_o<kXsBlock, kXsCol>(xs, K, lane);
     }
 };
 

@@ -3,30 +3,31 @@
 // *group* (one chunk, four heads) and each wavefront one head of it.
 //
 // The four heads' rows of a token are adjacent in HBM (4 x 256 bytes for
-// FP32, 4 x 128 for 16-bit elements), so a group's lines can be fetched with
+// FP32, 4 x 128 for 16-bit elements), so a group's rows can be fetched with
 // load instructions that each cover long runs of adjacent bytes, instead of
 // 64-byte pieces 16 KiB apart as when each wavefront loads its own head. The
 // loads are buffer loads with the LDS bit (gfx950's 16-byte direct-to-LDS
-// form): the data go to LDS without passing through VGPRs, and every line is
+// form): the data go to LDS without passing through VGPRs, and every byte is
 // read by exactly one instruction, so they carry the nontemporal bit (same
-// box, same buffers, the solver on 16 x 512 tokens: 42.9 -> 42.2 us; 48
-// ragged requests 121.9 -> 117.9 us; 131,072 tokens 607 -> 583 us).
+// box, same buffers, the fused solver on 16 x 512 tokens: 42.9 -> 42.2 us;
+// 48 ragged requests 121.9 -> 117.9 us; 131,072 tokens 607 -> 583 us).
 //
-// Which lines a tile holds is a per-kernel plan over the four block rows
-// (rows 16I..16I+15), per head: one 128-byte line of each row (columns 0..31
-// or 32..63 of an FP32 row; a 16-bit row is one line), both lines, or none.
+// Which columns a tile holds is a per-kernel plan over the four block rows
+// (rows 16I..16I+15): for each block row, columns c0..c0+nc-1 of every row of
+// every head, where nc x element size is 64, 128 or 256 bytes (a quarter,
+// half or whole FP32 row; a half or whole 16-bit row), or nothing.
 //
 // LDS layout (bytes), in slots of kSlotBytes (1 KiB plus 16 bytes, so the 16
-// rows one block read touches fall on different banks):
-//   pair slot: rows r and r + 8 of one block row, each as one line of heads
-//     0..3 (512 bytes); the second row's heads are rotated by one position,
-//     so that the two rows sit 128 bytes apart in bank order. A block row
-//     with one line per row takes 8 pair slots.
-//   row slot: one FP32 row, all 256 bytes of heads 0..3. A block row with
-//     both lines takes 16 row slots.
-// Slots follow block-row order; wavefront w issues the loads of slots w,
-// w + 4, w + 8, ... (every block row takes a multiple of four slots, so the
-// kind of slot the q-th load fills is the same for all four wavefronts).
+// rows one block read touches fall on different banks). A slot is what one
+// load instruction fills: n = 256 / piece rows of the four heads, where piece
+// is the bytes of a row the plan holds. Block row I takes 16 / n slots; its
+// slot j holds rows j, j + 16/n, j + 2*16/n, ... of the block row, the k-th
+// of them at byte k * 4 * piece with its heads rotated by k positions (head
+// hh at position (hh - k) mod 4), so that the rows a 16-lane read touches sit
+// on different banks. Slots follow block-row order; wavefront w issues the
+// loads of slots w, w + 4, w + 8, ... (every block row takes a multiple of
+// four slots, so what the q-th load of a wavefront fills is known at compile
+// time).
 #pragma once
 
 #include "tril_device.h"
@@ -36,30 +37,37 @@ namespace kda {
 constexpr int kGroupHeads = 4;
 constexpr int kSlotBytes = 1040;
 
-// Lines of a block row's rows that a group tile holds (per head).
-enum LineSel : int { kNone = 0, kLine0 = 1, kLine1 = 2, kBoth = 3 };
+// A block row's columns c0..c0+nc-1 (nc = 0: none), as a plan's argument.
+__host__ __device__ constexpr int cols(int c0, int nc) { return (c0 << 8) | nc; }
 
-template <class EI, int M0, int M1, int M2, int M3>
+template <class EI, int S0, int S1, int S2, int S3>
 struct GroupPlan {
-    // a 16-bit row is a single line: any selection holds all of it
-    __host__ __device__ static constexpr int mode(int I) {
-        const int m = I == 0 ? M0 : I == 1 ? M1 : I == 2 ? M2 : M3;
-        return (EI::kBytes == 2 && m != kNone) ? kLine0 : m;
+    __host__ __device__ static constexpr int sel(int I) {
+        return I == 0 ? S0 : I == 1 ? S1 : I == 2 ? S2 : S3;
     }
-    __host__ __device__ static constexpr bool paired(int I) {
-        return mode(I) == kLine0 || mode(I) == kLine1;
+    // bytes of a row held, and the byte column where they start
+    __host__ __device__ static constexpr int piece(int I) { return (sel(I) & 255) * EI::kBytes; }
+    __host__ __device__ static constexpr int lo(int I) { return (sel(I) >> 8) * EI::kBytes; }
+    // rows per slot, and slots of block row I
+    __host__ __device__ static constexpr int rows(int I) {
+        return piece(I) == 0 ? 1 : 256 / piece(I);
     }
     __host__ __device__ static constexpr int slots(int I) {
-        return mode(I) == kNone ? 0 : paired(I) ? 8 : 16;
+        return piece(I) == 0 ? 0 : 16 / rows(I);
     }
+    __host__ __device__ static constexpr bool valid(int I) {
+        return piece(I) == 0 ||
+               ((piece(I) == 64 || piece(I) == 128 || piece(I) == 256) &&
+                lo(I) % piece(I) == 0 && lo(I) + piece(I) <= kChunk * EI::kBytes);
+    }
+    static_assert(valid(0) && valid(1) && valid(2) && valid(3),
+                  "a block row holds an aligned quarter, half or whole FP32 row, or an "
+                  "aligned half or whole 16-bit row");
     // (closed forms, so that a block row known only at run time costs a few
     // selects rather than a loop)
     __host__ __device__ static constexpr int base(int I) {
         return (I > 0 ? slots(0) : 0) + (I > 1 ? slots(1) : 0) + (I > 2 ? slots(2) : 0) +
                (I > 3 ? slots(3) : 0);
-    }
-    __host__ __device__ static constexpr int line_bytes(int I) {
-        return mode(I) == kLine1 ? 128 : 0;
     }
     // the block row whose slots include slot s
     __host__ __device__ static constexpr int block_of(int s) {
@@ -71,46 +79,42 @@ struct GroupPlan {
     static constexpr int kBytes = kSlots * kSlotBytes;
 
     // LDS byte address of row R, head position hh, byte column bc of that
-    // head's row (bc inside the lines the plan holds for R's block row)
-    // (one address expression with selects, not two branches: R's block row
-    // is not always known at compile time)
+    // head's row (bc inside the columns the plan holds for R's block row);
+    // one expression with selects, not branches, as R's block row is not
+    // always known at compile time
     __device__ static __forceinline__ int addr(int R, int hh, int bc) {
-        const int I = R >> 4;
-        const bool pr = paired(I);
-        const int half = (R >> 3) & 1;
-        const int pos = half ? (hh + 3) & 3 : hh;
-        const int slot = base(I) + (pr ? (R & 7) : (R & 15));
-        const int inner = pr ? half * 512 + pos * 128 - line_bytes(I) : hh * 256;
-        return slot * kSlotBytes + inner + bc;
+        const int I = R >> 4, r = R & 15;
+        const int per = slots(I);  // a power of two
+        const int j = r & (per - 1), k = r / per;
+        const int pos = (hh - k) & 3;
+        return (base(I) + j) * kSlotBytes + (4 * k + pos) * piece(I) + bc - lo(I);
     }
 };
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
 
-// This wavefront's share of a group's loads (slots wid, wid + 4, ...). Lanes
-// of heads past the last head (nh < 4) use an out-of-range offset: their LDS
-// bytes get 0 and no memory is read for them.
+// This wavefront's share of a group's loads (slots wid, wid + 4, ...). Lane
+// l of a load that fills n rows takes row k = l / (64 / n) of the slot, and
+// a position and 16-byte piece in it; the position holds head (pos + k) mod
+// 4. Lanes of heads past the last head (nh < 4) use an out-of-range offset:
+// their LDS bytes get 0 and no memory is read for them.
 template <class EI, class Plan>
 __device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *lds, int wid,
                                            int lane) {
-    const int half = lane >> 5, pos = (lane >> 3) & 3, piece = lane & 7;
-    const int ph = half ? (pos + 1) & 3 : pos;  // head whose bytes land at this position
-    const uint32_t pmask = ph < nh ? 0u : kOffMasked;
-    const uint32_t rmask = (lane >> 4) < nh ? 0u : kOffMasked;
 #pragma unroll
     for (int q = 0; q < Plan::kSlots / 4; ++q) {
         const int I = Plan::block_of(4 * q);
+        const int n = Plan::rows(I), per = Plan::slots(I);
+        const int pieces = Plan::piece(I) / 16;  // lanes per (row, head)
+        const int k = lane / (64 / n);
+        const int w = lane % (64 / n);
+        const int pos = w / pieces, pc = w % pieces;
+        const int ph = (pos + k) & 3;
         const int s = wid + 4 * q;
-        const int j = s - Plan::base(I);  // slot within the block row
-        uint32_t off;
-        if (Plan::paired(I)) {
-            const int row = 16 * I + j + 8 * half;
-            off = ((uint32_t)(row * rstride + ph * 64) * EI::kBytes + Plan::line_bytes(I) +
-                   16 * piece) | pmask;
-        } else {
-            const int row = 16 * I + j;
-            off = ((uint32_t)(row * rstride) * EI::kBytes + 16 * lane) | rmask;
-        }
+        const int row = 16 * I + (s - Plan::base(I)) + k * per;
+        const uint32_t off =
+            ((uint32_t)(row * rstride + ph * kChunk) * EI::kBytes + Plan::lo(I) + 16 * pc) |
+            (ph < nh ? 0u : kOffMasked);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(lds + s * kSlotBytes), 16, off, 0,
                                                  0, kNontemporal);
     }
@@ -161,7 +165,8 @@ __device__ __forceinline__ void read_offdiag_blocks(f4 (&blk)[4][4], const char 
 #pragma unroll
     for (int I = 1; I < 4; ++I)
 #pragma unroll
-        for (int K = 0; K < I; ++K) blk[I][K] = lds_quad<EI, Plan>(lds, 16 * I + m, hh, 16 * K + 4 * g);
+        for (int K = 0; K < I; ++K)
+            blk[I][K] = lds_quad<EI, Plan>(lds, 16 * I + m, hh, 16 * K + 4 * g);
 }
 
 // A group of four heads of one chunk slot (len 0: nothing to do).

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_kkt(KktProblem q) {
             wave_sync();  // the previous item's last LDS reads are done
             const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
             diag_inverses(xs, arow, lane);
-            merge_and_store<EO, kXsBlock, kXsCol>(eng, acc, xs, xs, X, lane);
+            merge_and_store<EO>(eng, acc, xs, X, lane);
         } else {
             store_rows_a<EO, 0>(X, acc[0], xs, lane);
             if (ch.len <= 16) continue;
