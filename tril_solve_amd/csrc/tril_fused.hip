@@ -107,12 +107,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 // 512 tokens, 64 heads, this load pattern takes 40.0-40.4 us against 42.2 us
 // for the per-wavefront one.
 //
-// The solve needs columns 0..31 of block rows 0 and 1 and columns 0..63 of
-// block rows 2 and 3; rows of 16-bit elements are loaded whole, as one
-// 128-byte line each.
-template <class EI>
-using FusedPlan = GroupPlan<EI, cols(0, EI::kBytes == 4 ? 32 : 64),
-                            cols(0, EI::kBytes == 4 ? 32 : 64), cols(0, 64), cols(0, 64)>;
+// The tile is FusedPlan's (tril_group.h).
 
 // Head position hh's tile from the group's LDS copy, in the registers of the
 // solve: diagonal blocks one row per lane, blocks below the diagonal in

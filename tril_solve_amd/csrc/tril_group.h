@@ -82,39 +82,74 @@ struct GroupPlan {
     // head's row (bc inside the columns the plan holds for R's block row);
     // one expression with selects, not branches, as R's block row is not
     // always known at compile time
-    __device__ static __forceinline__ int addr(int R, int hh, int bc) {
+    __host__ __device__ static __forceinline__ int addr(int R, int hh, int bc) {
         const int I = R >> 4, r = R & 15;
         const int per = slots(I);  // a power of two
         const int j = r & (per - 1), k = r / per;
         const int pos = (hh - k) & 3;
         return (base(I) + j) * kSlotBytes + (4 * k + pos) * piece(I) + bc - lo(I);
     }
+
+    // What lane `lane` of the load that fills slot j of block row I (LDS
+    // slot base(I) + j) brings: 16 bytes of row `row` of the chunk, head
+    // position `head`, from byte column `byte` of that head's row, landing at
+    // byte 16 * lane of the slot. Lane l of a load that fills n rows takes
+    // row k = l / (64 / n) of the slot, and a position and 16-byte piece in
+    // it; the position holds head (pos + k) mod 4.
+    struct Src {
+        int row, head, byte;
+    };
+    __host__ __device__ static __forceinline__ Src load_src(int I, int j, int lane) {
+        const int n = rows(I), per = slots(I);
+        const int pieces = piece(I) / 16;  // lanes per (row, head)
+        const int k = lane / (64 / n);
+        const int w = lane % (64 / n);
+        const int pos = w / pieces, pc = w % pieces;
+        return Src{16 * I + j + k * per, (pos + k) & 3, lo(I) + 16 * pc};
+    }
 };
+
+// The plans of the solver kernels.
+// The fused kernel needs columns 0..31 of block rows 0 and 1 and columns
+// 0..63 of block rows 2 and 3; rows of 16-bit elements are loaded whole, as
+// one 128-byte line each.
+template <class EI>
+using FusedPlan = GroupPlan<EI, cols(0, EI::kBytes == 4 ? 32 : 64),
+                            cols(0, EI::kBytes == 4 ? 32 : 64), cols(0, 64), cols(0, 64)>;
+// The split plan's diagonal kernel reads the diagonal blocks alone: columns
+// 16I..16I+15 of block row I, a quarter FP32 row; 16-bit rows in halves
+// (columns 0..31 for block rows 0 and 1, 32..63 for 2 and 3), 64 bytes each.
+template <class EI>
+using DiagPlan = GroupPlan<EI, EI::kBytes == 4 ? cols(0, 16) : cols(0, 32),
+                           EI::kBytes == 4 ? cols(16, 16) : cols(0, 32),
+                           EI::kBytes == 4 ? cols(32, 16) : cols(32, 32),
+                           EI::kBytes == 4 ? cols(48, 16) : cols(32, 32)>;
+// The split plan's merge kernel reads the blocks below the diagonal: columns
+// 0..15 of block row 1 (16-bit: 0..31, 64 bytes), 0..31 of block row 2,
+// whole rows of block row 3.
+template <class EI>
+using MergePlan = GroupPlan<EI, cols(0, 0), cols(0, EI::kBytes == 4 ? 16 : 32), cols(0, 32),
+                            cols(0, 64)>;
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
 
-// This wavefront's share of a group's loads (slots wid, wid + 4, ...). Lane
-// l of a load that fills n rows takes row k = l / (64 / n) of the slot, and
-// a position and 16-byte piece in it; the position holds head (pos + k) mod
-// 4. Lanes of heads past the last head (nh < 4) use an out-of-range offset:
-// their LDS bytes get 0 and no memory is read for them.
+// This wavefront's share of a group's loads (slots wid, wid + 4, ...), each
+// lane's 16 bytes as Plan::load_src says. Lanes of heads past the last head
+// (nh < 4) use an out-of-range offset: their LDS bytes get 0 and no memory is
+// read for them.
 template <class EI, class Plan>
 __device__ __forceinline__ void load_group(Rsrc r, int rstride, int nh, char *lds, int wid,
                                            int lane) {
 #pragma unroll
     for (int q = 0; q < Plan::kSlots / 4; ++q) {
+        // the slot's block row depends on q alone (every block row takes a
+        // multiple of four slots), so it is known at compile time
         const int I = Plan::block_of(4 * q);
-        const int n = Plan::rows(I), per = Plan::slots(I);
-        const int pieces = Plan::piece(I) / 16;  // lanes per (row, head)
-        const int k = lane / (64 / n);
-        const int w = lane % (64 / n);
-        const int pos = w / pieces, pc = w % pieces;
-        const int ph = (pos + k) & 3;
         const int s = wid + 4 * q;
-        const int row = 16 * I + (s - Plan::base(I)) + k * per;
+        const typename Plan::Src src = Plan::load_src(I, s - Plan::base(I), lane);
         const uint32_t off =
-            ((uint32_t)(row * rstride + ph * kChunk) * EI::kBytes + Plan::lo(I) + 16 * pc) |
-            (ph < nh ? 0u : kOffMasked);
+            ((uint32_t)(src.row * rstride + src.head * kChunk) * EI::kBytes + src.byte) |
+            (src.head < nh ? 0u : kOffMasked);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(lds + s * kSlotBytes), 16, off, 0,
                                                  0, kNontemporal);
     }

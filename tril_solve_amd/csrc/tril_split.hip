@@ -118,20 +118,7 @@ struct WsEngine {
 // reads its head's blocks from LDS and computes what the kernels above
 // compute for it, with the same arithmetic (same results, bit for bit).
 
-// The diagonal kernel reads the diagonal blocks alone: columns 16I..16I+15 of
-// block row I, a quarter FP32 row; 16-bit rows in halves (columns 0..31 for
-// block rows 0 and 1, 32..63 for 2 and 3), 64 bytes each.
-template <class EI>
-using DiagPlan = GroupPlan<EI, EI::kBytes == 4 ? cols(0, 16) : cols(0, 32),
-                           EI::kBytes == 4 ? cols(16, 16) : cols(0, 32),
-                           EI::kBytes == 4 ? cols(32, 16) : cols(32, 32),
-                           EI::kBytes == 4 ? cols(48, 16) : cols(32, 32)>;
-// The merge kernel reads the blocks below the diagonal: columns 0..15 of
-// block row 1 (16-bit: 0..31, 64 bytes), 0..31 of block row 2, whole rows of
-// block row 3.
-template <class EI>
-using MergePlan = GroupPlan<EI, cols(0, 0), cols(0, EI::kBytes == 4 ? 16 : 32), cols(0, 32),
-                            cols(0, 64)>;
+// The tiles are DiagPlan's and MergePlan's (tril_group.h).
 
 // LDS of a 4-head split kernel: the group's tile, reused, once every
 // wavefront has read it, for each wavefront's region of kLdsPerWave floats
