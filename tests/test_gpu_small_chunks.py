@@ -279,3 +279,67 @@ def test_graph_capture_replay(kt, C):
         eager = kt.tril_inv(A, cu)
         torch.cuda.synchronize()
         assert torch.equal(X, eager), f"replay {rep}"
+
+
+def _both_small_layouts(monkeypatch, call):
+    """call() under the 32-token group kernel and under the per-wavefront one."""
+    out = {}
+    for lay in ("group", "wave"):
+        monkeypatch.setenv("KDA_TRIL_SMALL_LAYOUT", lay)
+        out[lay] = call()
+        torch.cuda.synchronize()
+    monkeypatch.delenv("KDA_TRIL_SMALL_LAYOUT")
+    return out["group"], out["wave"]
+
+
+@pytest.mark.parametrize("H", [1, 2, 3, 7, 8, 9, 13])
+def test_c32_group_kernel_edge_cases(kt, monkeypatch, H):
+    """The 8-head group kernel of the 32-token branch (which multi-round
+    launches run; KDA_TRIL_SMALL_LAYOUT=group makes every launch use it):
+    head counts that leave a group partly empty (a wavefront with one head
+    or none), partial chunks and NaN above the diagonal; X bit for bit that
+    of the per-wavefront kernel, within tolerance of the oracle, and rows past
+    the requests untouched."""
+    print(f"\n[small] c32 group H={H}", flush=True)
+    A = synth.delta_rule_A(LENGTHS, H, seed=40 + H, chunk=32, upper="nan")
+    cu = synth.cu_seqlens(LENGTHS)
+    T = A.shape[0]
+    pad = np.full((16, H, 32), np.nan, np.float32)
+    Ad = torch.from_numpy(np.concatenate([A, pad])).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+
+    def run():
+        X = torch.full((T + 16, H, 32), -777.0, device=DEV)
+        kt.tril_inv(Ad[:T], cud, out=X[:T])
+        return X
+
+    Xg, Xw = _both_small_layouts(monkeypatch, run)
+    assert torch.equal(Xg, Xw)
+    X = Xg.cpu().numpy().astype(np.float64)
+    assert np.all(X[T:] == -777.0), "a row past the last request was written"
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(X[:T], ref, "f32") <= 0
+
+
+@pytest.mark.parametrize("a_dtype,x_dtype", [("bf16", "f32"), ("f16", "f16"), ("f32", "bf16"),
+                                             ("bf16", "bf16")])
+def test_c32_group_kernel_dtypes_and_dense(kt, monkeypatch, a_dtype, x_dtype):
+    H = 10
+    A32 = synth.delta_rule_A(LENGTHS, H, seed=50, chunk=32)
+    A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
+    cu = synth.cu_seqlens(LENGTHS)
+    Ad = gh.to_torch_input(A, a_dtype, DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    xt = gh.out_torch_dtype(x_dtype)
+    Xg, Xw = _both_small_layouts(monkeypatch, lambda: kt.tril_inv(Ad, cud, out_dtype=xt))
+    assert torch.equal(Xg, Xw)
+    ref = oracle.tril_inv_packed(A, cu, a_dtype)
+    assert gh.excess(gh.to_numpy_f64(Xg), ref, x_dtype) <= 0
+    # dense [B, T, H, 32] through the group kernel equals the packed call
+    B, Tn = 3, 70
+    Adn = synth.delta_rule_A([Tn] * B, H, seed=51, chunk=32)
+    Add = torch.from_numpy(Adn).to(DEV)
+    Xd, _ = _both_small_layouts(monkeypatch, lambda: kt.tril_inv(Add.view(B, Tn, H, 32)))
+    Xp, _ = _both_small_layouts(
+        monkeypatch, lambda: kt.tril_inv(Add, torch.from_numpy(synth.cu_seqlens([Tn] * B)).to(DEV)))
+    assert torch.equal(Xd.view(B * Tn, H, 32), Xp)

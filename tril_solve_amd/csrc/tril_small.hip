@@ -23,10 +23,15 @@
 // on the same (zero-padded) rows.
 #include <utility>
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "tril_device.h"
 #include "tril_launch.h"
 
 namespace kda {
+
+typedef __attribute__((address_space(3))) void *LdsPtr32;
 
 // load1 with the nontemporal policy, for the 16-token kernel whose every
 // line is read by exactly one load instruction (a line read again by a later
@@ -256,7 +261,169 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
     }
 }
 
+// ------------------------------------------------------------------------
+// 32 tokens, group form (launches in which wavefronts walk several items): a
+// workgroup of four wavefronts owns one chunk and eight adjacent heads, whose
+// rows are 8 x 32 elements, 1 KiB (FP32) or 512 bytes (16-bit) of adjacent
+// bytes; they go from HBM straight into LDS (16-byte buffer loads with the
+// LDS bit, every byte read by one instruction, so nontemporal), and then each
+// wavefront takes its two heads from LDS in the layouts of the kernel above
+// (diagonal rows one per lane, A_10 in OPND_A) and runs the same arithmetic.
+//
+// LDS: slots of 1040 bytes (1 KiB + 16, so 16 consecutive rows fall on
+// different banks), each holding what one load instruction brings: one FP32
+// row of the eight heads, or two 16-bit rows 2j and 2j + 1, the second with
+// its heads rotated by two positions (128 bytes) for the same reason.
+
+constexpr int kHeadsGroup32 = 8;
+constexpr int kSlot32 = 1040;
+
+template <class EI>
+struct Tile32 {
+    static constexpr int kRowsPerSlot = 4 / EI::kBytes;      // 1 or 2
+    static constexpr int kHeadBytes = 32 * EI::kBytes;       // a head's row
+    static constexpr int kSlots = 32 / kRowsPerSlot;
+    static constexpr int kBytes = kSlots * kSlot32 > kFusedWaves * kLdsPerWave * 4
+                                      ? kSlots * kSlot32
+                                      : kFusedWaves * kLdsPerWave * 4;
+    // LDS byte of row R, head position hh (0..7), byte column bc of its row
+    __host__ __device__ static __forceinline__ int addr(int R, int hh, int bc) {
+        const int k = R % kRowsPerSlot;
+        const int pos = (hh - 2 * k) & 7;
+        return (R / kRowsPerSlot) * kSlot32 + k * 8 * kHeadBytes + pos * kHeadBytes + bc;
+    }
+};
+
+// Columns c..c+3 of row R of head position hh, widened to FP32.
+template <class EI>
+__device__ __forceinline__ f4 lds_quad32(const char *lds, int R, int hh, int c) {
+    typedef Tile32<EI> L;
+    if constexpr (EI::kBytes == 4) {
+        return *reinterpret_cast<const f4 *>(lds + L::addr(R, hh, 4 * c));
+    } else if constexpr (__is_same(EI, BF16)) {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 v = *reinterpret_cast<const u2 *>(lds + L::addr(R, hh, 2 * c));
+        f4 o;
+        o[0] = bf16_to_f32(v[0] & 0xFFFFu);
+        o[1] = bf16_to_f32(v[0] >> 16);
+        o[2] = bf16_to_f32(v[1] & 0xFFFFu);
+        o[3] = bf16_to_f32(v[1] >> 16);
+        return o;
+    } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 v = *reinterpret_cast<const h4 *>(lds + L::addr(R, hh, 2 * c));
+        f4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (float)v[e];  // exact widening
+        return o;
+    }
+}
+
+template <class EI, class EO>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_c32_group(Problem p) {
+    typedef Tile32<EI> L;
+    __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane0 = threadIdx.x & (kWave - 1);
+    // once the group's rows are read, the tile holds each wavefront's
+    // diagonal inverses and staging
+    float *xs = reinterpret_cast<float *>(lds) + wid * kLdsPerWave;
+    const int groups = (p.heads + kHeadsGroup32 - 1) / kHeadsGroup32;
+    const long total = (long)p.slots * groups;
+    for (long gi = blockIdx.x; gi < total; gi += gridDim.x) {
+        const int slot = (int)(gi / groups);
+        const int hg = (int)(gi - (long)slot * groups);
+        // the same chunk for the whole workgroup: every wavefront takes the
+        // same branches and meets the same barriers
+        const Chunk ch = uniform(resolve_chunk<32>(p, slot, lane0));
+        if (ch.len <= 0) continue;
+        const int lane = opaque_lane(lane0);
+        const int h0 = kHeadsGroup32 * hg;
+        const int nh = min(kHeadsGroup32, p.heads - h0);
+        const int rstride = p.heads * 32;
+        const long gbase = ((long)ch.start * p.heads + h0) * 32;
+        {
+            const TileView<EI> A{static_cast<const typename EI::T *>(p.A) + gbase, rstride,
+                                 ch.len, 32 * nh};
+            const Rsrc r = A.rows_from(0);
+            // lane l: row k = l / (64 / rows per slot) of the slot, position
+            // and 16-byte piece of that row; the position holds head
+            // (pos + 2k) mod 8
+            constexpr int lanes_row = 64 / L::kRowsPerSlot, pieces = L::kHeadBytes / 16;
+            const int k = lane / lanes_row, w = lane % lanes_row;
+            const int pos = w / pieces, pc = w % pieces;
+            const int ph = (pos + 2 * k) & 7;
+            const uint32_t hmask = ph < nh ? 0u : kOffMasked;
+#pragma unroll
+            for (int q = 0; q < L::kSlots / kFusedWaves; ++q) {
+                const int s = wid + kFusedWaves * q;
+                const int row = s * L::kRowsPerSlot + k;
+                const uint32_t off =
+                    ((uint32_t)(row * rstride + ph * 32) * EI::kBytes + 16 * pc) | hmask;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr32)(lds + s * kSlot32), 16,
+                                                         off, 0, 0, kNontemporal);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wavefront's share of the group has arrived
+        // this wavefront's heads: positions 2 wid (+1)
+        f4 dgb[4], a10[2];
+        {
+            const int b = lane >> 4, i = lane & 15, m = b >> 1, d = b & 1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dgb[q] = lds_quad32<EI>(lds, 16 * d + i, 2 * wid + m, 16 * d + 4 * q);
+            const int g = lane >> 4, mr = lane & 15;
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) a10[mm] = lds_quad32<EI>(lds, 16 + mr, 2 * wid + mm, 4 * g);
+        }
+        __syncthreads();  // every wavefront has its rows: the tile is free
+        const int hv = nh - 2 * wid;  // heads of this wavefront that exist
+        if (hv > 0) {
+            const uint32_t mask_hi = hv > 1 ? 0u : kOffMasked;
+            const long base = gbase + 2 * wid * 32;
+            const TileView<EO> X{static_cast<typename EO::T *>(p.X) + base, rstride, ch.len,
+                                 32 * min(hv, 2)};
+            float arow[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * q + e] = dgb[q][e];
+            diag_inverses(xs, arow, lane);
+            const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
+            const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            f4 x00[2], row1[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) x00[m] = xs_opnd_o<kXsBlock, kXsCol>(xs, 2 * m, lane);
+            const bool two_rows = ch.len > 16;
+            if (two_rows) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    row1[m][1] = xs_opnd_o<kXsBlock, kXsCol>(xs, 2 * m + 1, lane);
+                    row1[m][0] = eng.negx(2 * m + 1, eng.mm(a10[m], x00[m], z));
+                }
+            }
+            const f4 row0[2][2] = {{x00[0], z}, {x00[1], z}};
+            store_pair_rows<EO, 0>(X, row0, xs, mask_hi, lane);
+            if (two_rows) store_pair_rows<EO, 1>(X, row1, xs, mask_hi, lane);
+        }
+        __syncthreads();  // staging reads done before the next group's loads land
+    }
+}
+
 // ------------------------------------------------------------------ launch
+
+// KDA_TRIL_SMALL_LAYOUT (read on every call): "wave" runs the per-wavefront
+// 32-token kernel for every launch, "group" the 8-head group kernel for every
+// launch (the tests use it to reach its edge cases on small problems);
+// anything else, or unset, the group kernel when the per-wavefront launch
+// would take more than one round of the GPU.
+static int small_layout() {
+    const char *e = getenv("KDA_TRIL_SMALL_LAYOUT");
+    if (e && strcmp(e, "wave") == 0) return 1;
+    if (e && strcmp(e, "group") == 0) return 2;
+    return 0;
+}
 
 template <class K>
 static hipError_t launch_groups(K kernel, const Problem &p, int chunk, int heads_per_wave,
@@ -273,15 +440,24 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
         if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, 16, kHeads16, stream);
         if (chunk == 32) {
             // the ROWS = false variant sizes the grid; one-round launches run
-            // the row-per-lane variant
+            // the row-per-lane variant, longer ones the group kernel
             const long groups = (p.heads + kHeads32 - 1) / kHeads32;
             const long items = (long)p.slots * groups;
             const long blocks =
                 walk_blocks(reinterpret_cast<const void *>(tril_inv_c32<EI, EO, false>), items,
                             min_chunks(p, 32) * groups);
-            if (blocks * kFusedWaves >= items)
-                return launch_groups(tril_inv_c32<EI, EO, true>, p, 32, kHeads32, stream);
-            return launch_groups(tril_inv_c32<EI, EO, false>, p, 32, kHeads32, stream);
+            const int lay = small_layout();
+            if (lay == 2 || (lay == 0 && blocks * kFusedWaves < items)) {
+                const long g8 = (long)p.slots * ((p.heads + kHeadsGroup32 - 1) / kHeadsGroup32);
+                const long gb = group_blocks(
+                    reinterpret_cast<const void *>(tril_inv_c32_group<EI, EO>), g8);
+                hipLaunchKernelGGL((tril_inv_c32_group<EI, EO>), dim3((unsigned)gb),
+                                   dim3(kFusedThreads), 0, stream, p);
+                return hipGetLastError();
+            }
+            if (lay == 1 && blocks * kFusedWaves < items)
+                return launch_groups(tril_inv_c32<EI, EO, false>, p, 32, kHeads32, stream);
+            return launch_groups(tril_inv_c32<EI, EO, true>, p, 32, kHeads32, stream);
         }
         return hipErrorInvalidValue;
     });
