@@ -70,6 +70,9 @@ def kernel_of(workload: str):
         return r"tril_inv_fused_(heads4|mfma)<", ["tril_device.h", "tril_group.h",
                                                   "tril_fused.hip", "tril_launch.h",
                                                   "launch_common.cpp"]
+    if C == 32:  # one-round launches run the per-wavefront kernel, longer ones the group one
+        return r"tril_inv_c32(_group)?<", ["tril_device.h", "tril_small.hip", "tril_launch.h",
+                                           "launch_common.cpp"]
     return rf"tril_inv_c{C}<", ["tril_device.h", "tril_small.hip", "tril_launch.h"]
 
 

@@ -180,3 +180,25 @@ def test_line_labels_algorithmic_and_measured_rates():
     m = out["hbm_measured"]
     assert m["achieved"] == pytest.approx(235368201 / 45e-6 / 1e9)
     assert m["frac"] == pytest.approx(m["achieved"] / 8000.0)
+
+
+def test_kernel_patterns_match_the_kernels_each_workload_runs():
+    """The counter summaries are matched to rocprofv3's demangled names: a
+    workload's pattern must cover every kernel its launches can run (one-round
+    and multi-round forms) and none of the other paths'."""
+    import re
+    names = {
+        "packed_16x512_h64_f32": ["void kda::tril_inv_fused_heads4<kda::F32, kda::F32>(kda::Problem)",
+                                  "void kda::tril_inv_fused_mfma<kda::F32, kda::F32, true>(kda::Problem)"],
+        "packed_16x512_h64_c32_f32": ["void kda::tril_inv_c32_group<kda::F32, kda::F32>(kda::Problem)",
+                                      "void kda::tril_inv_c32<kda::F32, kda::F32, true>(kda::Problem)"],
+        "packed_16x512_h64_c16_f32": ["void kda::tril_inv_c16<kda::F32, kda::F32>(kda::Problem)"],
+    }
+    others = ["kda_probe_copy_kernel(float __vector(4) const*, float __vector(4)*, long)",
+              "void kda::tril_inv_split_merge_heads4<kda::F32, kda::F32>(kda::Problem)"]
+    for w, ks in names.items():
+        pat = re.compile(bench.kernel_of(w)[0])
+        for k in ks:
+            assert pat.search(k), (w, k)
+        for k in others + [n for v, l in names.items() if v != w for n in l]:
+            assert not pat.search(k), (w, k)
