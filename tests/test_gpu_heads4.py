@@ -167,3 +167,38 @@ def test_exact_subdiagonal_bitwise(kt, monkeypatch, algo):
         for h in range(H):
             assert np.array_equal(X[bos:bos + L, h], want), (bos, h)
         bos += n
+
+
+@pytest.mark.parametrize("algo_", ["fused", "split"])
+def test_graph_capture_replay_heads4(kt, monkeypatch, algo_):
+    """The 4-head kernels captured in a HIP graph (launch configuration fixed
+    at capture) and replayed on new inputs, with eager work and
+    synchronisation between replays: every replay equals the eager result."""
+    monkeypatch.setenv(LAYOUT_ENV[algo_], "heads4")
+    lengths = [512, 300, 64, 9]
+    H = 7
+    T = sum(lengths)
+    inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (111, 112, 113)]
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    A = torch.from_numpy(inputs[0]).to(DEV)
+    X = torch.empty_like(A)
+    nbytes, _ = kt.kda_tril_inv_workspace_size(T, len(lengths), 0, H, algo_)
+    ws = torch.empty(max(nbytes // 4, 1), device=DEV) if nbytes else None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kt.kda_tril_inv_packed(A, X, cu, workspace=ws, algo=algo_)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kt.kda_tril_inv_packed(A, X, cu, workspace=ws, algo=algo_)
+    for i in range(6):
+        A.copy_(torch.from_numpy(inputs[i % 3]))
+        X.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = kt.tril_inv(A, cu, algo=algo_)
+        torch.cuda.synchronize()
+        assert torch.equal(X, ref), i

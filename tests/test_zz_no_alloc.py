@@ -68,3 +68,39 @@ def test_noalloc_refuses_oversize(kt):
     with pytest.raises(kt.KdaError) as e:
         kt.kda_tril_inv_packed_noalloc(A, X, cu, chunk_indices=cmap)
     assert e.value.status == kt.KDA_ERR_WORKSPACE
+
+
+def test_noalloc_under_graph_capture(kt, monkeypatch):
+    """What the entry point is for: a call captured into a HIP graph (no
+    allocation inside the capture), replayed on new inputs with eager work and
+    synchronisation between replays; every replay equals the workspace-taking
+    split call bit for bit. Run once on the per-wavefront split kernels and
+    once on the 4-head ones."""
+    lengths = [512, 300, 64, 9]
+    H = 6
+    T = sum(lengths)
+    inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (121, 122, 123)]
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    for layout in ("wave", "heads4"):
+        monkeypatch.setenv("KDA_TRIL_SPLIT_LAYOUT", layout)
+        A = torch.from_numpy(inputs[0]).to(DEV)
+        X = torch.empty_like(A)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            kt.kda_tril_inv_packed_noalloc(A, X, cu, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            kt.kda_tril_inv_packed_noalloc(A, X, cu)
+        for i in range(6):
+            A.copy_(torch.from_numpy(inputs[i % 3]))
+            X.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ref = _with_workspace(kt, A, cu, torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(X, ref), (layout, i)
+    monkeypatch.delenv("KDA_TRIL_SPLIT_LAYOUT")
