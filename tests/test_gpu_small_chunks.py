@@ -343,3 +343,25 @@ def test_c32_group_kernel_dtypes_and_dense(kt, monkeypatch, a_dtype, x_dtype):
     Xp, _ = _both_small_layouts(
         monkeypatch, lambda: kt.tril_inv(Add, torch.from_numpy(synth.cu_seqlens([Tn] * B)).to(DEV)))
     assert torch.equal(Xd.view(B * Tn, H, 32), Xp)
+
+
+@pytest.mark.parametrize("C", SIZES)
+def test_deterministic_across_grids(kt, monkeypatch, C):
+    """The 16 x 512-token, 64-head batch (multi-round: the 32-token group
+    kernel, the 16-token walking kernel) on grids of 1, 2, 3 and 5
+    workgroups per CU (KDA_TRIL_BLOCKS_PER_CU, read on every call), 10 calls
+    each: X is the same bit for bit as on the default grid."""
+    print(f"\n[small] grids C={C}", flush=True)
+    name = f"packed_16x512_h64_c{C}_f32"
+    d = synth.make(name)
+    A = _dev(d["A"])
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    X0 = kt.tril_inv(A, cu)
+    torch.cuda.synchronize()
+    for bpc in ("1", "2", "3", "5"):
+        monkeypatch.setenv("KDA_TRIL_BLOCKS_PER_CU", bpc)
+        for _ in range(10):
+            X = kt.tril_inv(A, cu)
+            torch.cuda.synchronize()
+            assert torch.equal(X, X0), bpc
+    monkeypatch.delenv("KDA_TRIL_BLOCKS_PER_CU")
