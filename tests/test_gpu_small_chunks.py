@@ -295,7 +295,8 @@ def _both_small_layouts(monkeypatch, call):
 @pytest.mark.parametrize("H", [1, 2, 3, 7, 8, 9, 13])
 def test_c32_group_kernel_edge_cases(kt, monkeypatch, H):
     """The 8-head group kernel of the 32-token branch (which multi-round
-    launches run; KDA_TRIL_SMALL_LAYOUT=group makes every launch use it):
+    launches with 32 heads or more run; KDA_TRIL_SMALL_LAYOUT=group makes
+    every launch use it):
     head counts that leave a group partly empty (a wavefront with one head
     or none), partial chunks and NaN above the diagonal; X bit for bit that
     of the per-wavefront kernel, within tolerance of the oracle, and rows past

@@ -256,8 +256,19 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
 // KDA_TRIL_FUSED_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernel for every launch, "heads4" the 4-head kernel for every launch (one
 // round or not; the tests use it to reach its edge cases on small problems);
-// anything else, or unset, chooses by the number of rounds.
+// anything else, or unset, chooses by the number of rounds and of heads.
 enum class Layout { kAuto, kWave, kHeads4 };
+
+// Heads from which multi-round launches take the 4-head kernel. With few
+// heads the rows of a chunk's heads are close together anyway, so the
+// per-wavefront loads cover nearly adjacent bytes, and groups of four run
+// partly empty when H is not a multiple of four. Measured on single long
+// requests (same box, six rotating buffer sets; µs, per-wavefront / 4-head):
+// 8,192 chunk-heads at H = 2 44.5 / 45.1, 4 45.4 / 46.5, 5 45.8 / 52.3,
+// 8 45.6 / 46.5, 9 45.7 / 44.1, 10 46.0 / 44.5, 12 46.7 / 45.7, 13 45.4 / 46.3,
+// 16 52.5 / 46.9, 32 47.6 / 44.5, 64 44.6 / 42.6; 4,096 at H = 1 22.8 / 32.9;
+// 6,144 at H = 6 34.2 / 38.7.
+constexpr int kHeads4MinHeads = 9;
 static Layout fused_layout() {
     const char *e = getenv("KDA_TRIL_FUSED_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return Layout::kWave;
@@ -272,7 +283,8 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
             reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves,
             min_chunks(p, kChunk) * p.heads);
         const Layout lay = fused_layout();
-        if (lay == Layout::kHeads4 || (lay == Layout::kAuto && blocks * kFusedWaves < waves)) {
+        if (lay == Layout::kHeads4 ||
+            (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads)) {
             const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);

@@ -276,6 +276,13 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
 // its heads rotated by two positions (128 bytes) for the same reason.
 
 constexpr int kHeadsGroup32 = 8;
+// Heads from which multi-round launches take the group kernel: with fewer the
+// per-wavefront kernel reads nearly adjacent rows anyway and groups of eight
+// run partly empty. Single long requests of 16,384 chunk-heads, same box (µs,
+// per-wavefront / group): H = 1 27.0 / 77.7, 2 26.0 / 37.6, 4 26.2 / 26.3,
+// 8 25.6 / 25.4, 12 26.0 / 28.6, 16 26.0 / 25.8, 32 26.0 / 25.8, 64 26.0 / 25.1:
+// below 32 heads the two are within noise of each other or the group loses.
+constexpr int kGroup32MinHeads = 32;
 constexpr int kSlot32 = 1040;
 
 template <class EI>
@@ -440,14 +447,16 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
         if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, 16, kHeads16, stream);
         if (chunk == 32) {
             // the ROWS = false variant sizes the grid; one-round launches run
-            // the row-per-lane variant, longer ones the group kernel
+            // the row-per-lane variant, longer ones the group kernel when
+            // there are enough heads, else the ROWS = false variant
             const long groups = (p.heads + kHeads32 - 1) / kHeads32;
             const long items = (long)p.slots * groups;
             const long blocks =
                 walk_blocks(reinterpret_cast<const void *>(tril_inv_c32<EI, EO, false>), items,
                             min_chunks(p, 32) * groups);
             const int lay = small_layout();
-            if (lay == 2 || (lay == 0 && blocks * kFusedWaves < items)) {
+            if (lay == 2 ||
+                (lay == 0 && blocks * kFusedWaves < items && p.heads >= kGroup32MinHeads)) {
                 const long g8 = (long)p.slots * ((p.heads + kHeadsGroup32 - 1) / kHeadsGroup32);
                 const long gb = group_blocks(
                     reinterpret_cast<const void *>(tril_inv_c32_group<EI, EO>), g8);

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge_heads4(Pro
 // KDA_TRIL_SPLIT_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernels for every launch, "heads4" the 4-head ones for every launch;
 // anything else, or unset, the 4-head ones when the per-wavefront launch
-// would not fit on the device at once.
+// would not fit on the device at once and there are two heads or more.
 static int split_layout() {
     const char *e = getenv("KDA_TRIL_SPLIT_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return 1;
@@ -216,11 +216,14 @@ static hipError_t launch_split_t(const Problem &p, hipStream_t stream) {
     const long waves = (long)p.slots * p.heads;
     const long blocks = (waves + kFusedWaves - 1) / kFusedWaves;
     const int lay = split_layout();
+    // (A single head leaves three of a group's four wavefronts idle: on a
+    // 524,288-token request the per-wavefront kernels took 63-65 µs against
+    // 75-76; from two heads on the 4-head ones win, 60 against 63 at H = 2.)
     const bool heads4 =
         lay == 2 ||
-        (lay == 0 && blocks > resident_blocks(reinterpret_cast<const void *>(
-                                                  tril_inv_split_merge<EI, EO>),
-                                              kFusedThreads));
+        (lay == 0 && p.heads >= 2 &&
+         blocks > resident_blocks(reinterpret_cast<const void *>(tril_inv_split_merge<EI, EO>),
+                                  kFusedThreads));
     if (heads4) {
         const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
         const long gd = group_blocks(
