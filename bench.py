@@ -66,8 +66,9 @@ def kernel_of(workload: str):
         return r"kda_decode_step_kernel<", ["tril_device.h", "kda_decode.hip", "tril_launch.h"]
     import synth
     C = synth.CONFIGS[workload].get("chunk", 64)
-    if C == 64:  # the per-wavefront kernel or, for long launches with 9+ heads, the 4-head one
-        return r"tril_inv_fused_(heads4|mfma)<", ["tril_device.h", "tril_group.h",
+    if C == 64:  # the column kernel (few chunk-heads), the per-wavefront kernel or, for
+        # long launches with 9+ heads, the 4-head one
+        return r"tril_inv_fused_(heads4|mfma|cols)<", ["tril_device.h", "tril_group.h",
                                                   "tril_fused.hip", "tril_launch.h",
                                                   "launch_common.cpp"]
     if C == 32:  # the per-wavefront kernel or, for long launches with 32+ heads, the group one

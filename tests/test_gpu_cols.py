@@ -1,0 +1,186 @@
+"""GPU tests of the fused solver's four-wavefronts-per-chunk-head kernel.
+
+Launches whose chunk-heads fit on the GPU several times over (a 64-token
+request over 64 heads, a few short requests) run tril_inv_fused_cols: one
+workgroup per chunk-head, wavefront J computes block column J of X, and after
+one barrier wavefront I stores block row I. KDA_TRIL_FUSED_LAYOUT=cols makes
+every launch use it, so these tests also reach it on problems that take
+several rounds. Every case is compared with the oracle and, bit for bit,
+with the one-wavefront kernel (layout "wave"), whose products it runs in the
+same order.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_helpers as gh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LENGTHS = [1, 17, 64, 100, 130, 5, 48]  # partial chunks of every block count
+PAD = 16
+CANARY = -777.0
+
+
+@pytest.fixture(scope="module")
+def kt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tril_solve_amd
+    return tril_solve_amd
+
+
+def _cols_and_wave(monkeypatch, call):
+    """call() under the column kernel and under the one-wavefront one."""
+    out = {}
+    for lay in ("cols", "wave"):
+        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
+        out[lay] = call()
+        torch.cuda.synchronize()
+    monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT")
+    return out["cols"], out["wave"]
+
+
+@pytest.mark.parametrize("H", [1, 3, 4, 7, 64])
+def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
+    print(f"\n[cols] H={H}", flush=True)
+    A = synth.delta_rule_A(LENGTHS, H, seed=600 + H, upper="nan")
+    cu = synth.cu_seqlens(LENGTHS)
+    T = A.shape[0]
+    Ad = torch.from_numpy(np.concatenate([A, np.full((PAD, H, 64), np.nan, np.float32)])).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+
+    def run():
+        X = torch.full((T + PAD, H, 64), CANARY, device=DEV)
+        kt.tril_inv(Ad[:T], cud, algo="fused", out=X[:T])
+        return X
+
+    Xc, Xw = _cols_and_wave(monkeypatch, run)
+    assert torch.equal(Xc, Xw)
+    X = Xc.cpu().numpy().astype(np.float64)
+    assert np.all(X[T:] == CANARY), "a row past the last request was written"
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(X[:T], ref, "f32") <= 0
+
+
+@pytest.mark.parametrize("a_dtype,x_dtype", [("f32", "bf16"), ("bf16", "f32"), ("f16", "f16"),
+                                             ("bf16", "bf16"), ("f16", "f32")])
+def test_dtypes(kt, monkeypatch, a_dtype, x_dtype):
+    H = 6
+    A32 = synth.delta_rule_A(LENGTHS, H, seed=610)
+    A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
+    cu = synth.cu_seqlens(LENGTHS)
+    Ad = gh.to_torch_input(A, a_dtype, DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    xt = gh.out_torch_dtype(x_dtype)
+    Xc, Xw = _cols_and_wave(monkeypatch,
+                            lambda: kt.tril_inv(Ad, cud, out_dtype=xt, algo="fused"))
+    assert torch.equal(Xc, Xw)
+    ref = oracle.tril_inv_packed(A, cu, a_dtype)
+    assert gh.excess(gh.to_numpy_f64(Xc), ref, x_dtype) <= 0
+
+
+def test_dense_layout_and_chunk_map(kt, monkeypatch):
+    H = 5
+    B, T = 3, 150
+    A = synth.delta_rule_A([T] * B, H, seed=620)
+    Ad = torch.from_numpy(A).to(DEV)
+    Xc, Xw = _cols_and_wave(monkeypatch,
+                            lambda: kt.tril_inv(Ad.view(B, T, H, 64), algo="fused"))
+    assert torch.equal(Xc, Xw)
+    cu = synth.cu_seqlens([T] * B)
+    cud = torch.from_numpy(cu).to(DEV)
+    cmap = torch.from_numpy(gh.host_chunk_map([T] * B)).to(DEV)
+    Xm, _ = _cols_and_wave(monkeypatch,
+                           lambda: kt.tril_inv(Ad, cud, chunk_indices=cmap, algo="fused"))
+    assert torch.equal(Xm.view(B, T, H, 64), Xc)
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(gh.to_numpy_f64(Xm), ref, "f32") <= 0
+
+
+@pytest.mark.parametrize("cu,clamped", [([0, 64, 200], [0, 64, 100]),
+                                        ([-40, 64, 100], [24, 64, 100]),
+                                        ([0, 64, 100, 300], [0, 64, 100, 100])])
+def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
+    """Chunks outside rows [0, T) are skipped or cut at T: nothing past T is
+    read (NaN there) or written (canaries)."""
+    H = 3
+    A = synth.delta_rule_A([64, 36], H, seed=630)
+    T = A.shape[0]
+    Ad = torch.from_numpy(np.concatenate([A, np.full((PAD, H, 64), np.nan, np.float32)])).to(DEV)
+    cud = torch.tensor(cu, dtype=torch.int32, device=DEV)
+
+    def run():
+        X = torch.full((T + PAD, H, 64), CANARY, device=DEV)
+        kt.tril_inv(Ad[:T], cud, algo="fused", out=X[:T])
+        return X
+
+    Xc, Xw = _cols_and_wave(monkeypatch, run)
+    assert torch.equal(Xc, Xw)
+    X = Xc.cpu().numpy().astype(np.float64)
+    assert np.all(X[T:] == CANARY)
+    ref = np.full(A.shape, np.nan)
+    for s, e in zip(clamped[:-1], clamped[1:]):
+        if s < e:
+            ref[s:e] = oracle.tril_inv_packed(A[s:e], [0, e - s])
+    rows = ~np.isnan(ref[:, 0, 0])
+    assert gh.excess(X[:T][rows], ref[rows], "f32") <= 0
+
+
+def test_multi_round_problem(kt, monkeypatch):
+    """Forced on a problem of many rounds (one workgroup per chunk-head, the
+    GPU schedules them in turn): the same X as the 4-head kernel the launch
+    would otherwise run."""
+    d = synth.make("packed_16x512_h64_f32")
+    A = torch.from_numpy(d["A"]).to(DEV)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    out = {}
+    for lay in ("cols", "heads4"):
+        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
+        out[lay] = kt.tril_inv(A, cu, algo="fused")
+        torch.cuda.synchronize()
+    assert torch.equal(out["cols"], out["heads4"])
+
+
+def test_auto_choice_on_small_workloads(kt):
+    """Without the variable, a 64-token request over 64 heads (64 chunk-heads)
+    runs the column kernel: the same X as the forced layouts."""
+    d = synth.make("packed_1x64_h64_f32")
+    A = torch.from_numpy(d["A"]).to(DEV)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+    X = kt.tril_inv(A, cu)
+    ref = oracle.tril_inv_packed(d["A"], d["cu_seqlens"])
+    assert gh.excess(X.cpu().numpy().astype(np.float64), ref, "f32") <= 0
+
+
+def test_graph_capture_replay(kt, monkeypatch):
+    """Captured in a HIP graph and replayed on new inputs, with eager work and
+    synchronisation between replays: every replay equals the eager result."""
+    monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", "cols")
+    lengths = [64, 100, 9]
+    H = 8
+    inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (641, 642, 643)]
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(DEV)
+    A = torch.from_numpy(inputs[0]).to(DEV)
+    X = torch.empty_like(A)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kt.kda_tril_inv_packed(A, X, cu, algo="fused")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kt.kda_tril_inv_packed(A, X, cu, algo="fused")
+    for i in range(6):
+        A.copy_(torch.from_numpy(inputs[i % 3]))
+        X.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = kt.tril_inv(A, cu, algo="fused")
+        torch.cuda.synchronize()
+        assert torch.equal(X, eager), f"replay {i}"

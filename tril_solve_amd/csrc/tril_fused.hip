@@ -96,6 +96,125 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 }
 
 // ------------------------------------------------------------------------
+// Latency form for launches that leave compute units idle (every chunk-head
+// fits on the GPU four times over, e.g. one 64-token request over 64
+// heads): a workgroup of four wavefronts per chunk-head, wavefront J for
+// block column J. The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
+// only blocks of column J above row I and the diagonal inverses, so the
+// columns need nothing from each other: each wavefront inverts the four
+// diagonal blocks itself (the same lanes and steps as the one-wavefront
+// kernel, at the same cost as one block), runs its column's products in
+// the one-wavefront kernel's order, and writes X_JJ..X_3J into the staging
+// rows of their block rows; after one barrier wavefront I stores block row
+// I. The longest chain of products is column 0's 36 instead of all 64 in
+// one wavefront, the stores of the four block rows run at once, and X is
+// the same bit for bit.
+
+template <class EI, int J>
+__device__ __forceinline__ void load_column_tile(Tile &t, const TileView<EI> &A, int lane) {
+    load_diag_row_quads<EI>(t.dg, A, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the diagonal solve waits for these only
+    const int g = lane >> 4, m = lane & 15;
+    const uint32_t off = (uint32_t)(m * A.rstride + 4 * g) * EI::kBytes;
+#pragma unroll
+    for (int I = J + 1; I < 4; ++I) {
+        const Rsrc r = A.rows_from(16 * I);
+#pragma unroll
+        for (int K = J; K < I; ++K) t.blk[I][K] = load4<EI>(r, off + 16 * K * EI::kBytes);
+    }
+}
+
+// Floats of block row I's staging (16 rows of stage_row(I)) and where it
+// starts in the workgroup's staging region.
+__host__ __device__ constexpr int col_stage_floats(int I) { return 16 * stage_row(I); }
+__host__ __device__ constexpr int col_stage_base(int I) {
+    return I == 0 ? 0 : col_stage_base(I - 1) + col_stage_floats(I - 1);
+}
+constexpr int kColStageFloats = col_stage_base(4);
+
+template <class EI, int J>
+__device__ __forceinline__ void column_merge(const Problem &p, const Chunk &ch, int h, float *xs,
+                                             float *stage, int lane) {
+    const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
+                             ((long)ch.start * p.heads + h) * kChunk,
+                         p.heads * kChunk, ch.len, kChunk};
+    Tile t;
+    load_column_tile<EI, J>(t, A, opaque_lane(lane));
+    float arow[16];
+    tile_diag_rows<true>(t, arow);
+    diag_inverses(xs, arow, opaque_lane(lane));
+    const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
+    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4 x[4];
+    x[J] = eng.xkk(J);
+#pragma unroll
+    for (int I = J + 1; I < 4; ++I) {
+        f4 acc = z;
+#pragma unroll
+        for (int K = J; K < I; ++K) acc = eng.mm(t.blk[I][K], x[K], acc);
+        x[I] = eng.negx(I, acc);
+    }
+    // X_IJ into block row I's staging, columns 16J.. (store_block_row's layout)
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int I = J; I < 4; ++I) {
+        float *st = stage + col_stage_base(I);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(4 * g + r) * stage_row(I) + 16 * J + n] = x[I][r];
+    }
+}
+
+// Rows 16I..16I+15 of X from block row I's staging: four whole rows per store
+// instruction, zeros right of the block row (as in store_block_row).
+template <class EO, int I>
+__device__ __forceinline__ void store_staged_row(const TileView<EO> &X, const float *stage,
+                                                 int lane) {
+    constexpr int S = stage_row(I);
+    const float *st = stage + col_stage_base(I);
+    const int r4 = lane >> 4, c4 = (lane & 15) * 4;
+    const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t off = (uint32_t)(r4 * X.rstride + c4) * EO::kBytes;
+    const bool in_row = c4 < 16 * (I + 1);
+    const int cs = in_row ? c4 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f4 sv = *reinterpret_cast<const f4 *>(&st[(4 * i + r4) * S + cs]);
+        store4<EO>(X.rows_from(16 * I + 4 * i), off, in_row ? sv : z);
+    }
+}
+
+template <class EI, class EO>
+__global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_cols(Problem p) {
+    __shared__ __attribute__((aligned(16))) float xs_all[kFusedWaves * kLdsPerWave];
+    __shared__ __attribute__((aligned(16))) float stage[kColStageFloats];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float *xs = xs_all + wid * kLdsPerWave;
+    const long w = blockIdx.x;  // one chunk-head per workgroup
+    const int slot = (int)(w / p.heads);
+    const int h = (int)(w - (long)slot * p.heads);
+    const Chunk ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
+    if (ch.len <= 0) return;  // the same for the whole workgroup
+    switch (wid) {
+        case 0: column_merge<EI, 0>(p, ch, h, xs, stage, lane); break;
+        case 1: column_merge<EI, 1>(p, ch, h, xs, stage, lane); break;
+        case 2: column_merge<EI, 2>(p, ch, h, xs, stage, lane); break;
+        default: column_merge<EI, 3>(p, ch, h, xs, stage, lane); break;
+    }
+    __syncthreads();
+    if (ch.len <= 16 * wid) return;  // block row past the chunk
+    const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
+                             ((long)ch.start * p.heads + h) * kChunk,
+                         p.heads * kChunk, ch.len, kChunk};
+    switch (wid) {
+        case 0: store_staged_row<EO, 0>(X, stage, lane); break;
+        case 1: store_staged_row<EO, 1>(X, stage, lane); break;
+        case 2: store_staged_row<EO, 2>(X, stage, lane); break;
+        default: store_staged_row<EO, 3>(X, stage, lane); break;
+    }
+}
+
+// ------------------------------------------------------------------------
 // Multi-head form of the same kernel, for launches in which wavefronts walk
 // several items. A workgroup of four wavefronts owns a group (chunk, four
 // adjacent heads): the lines of the four heads' tiles that the solve needs go
@@ -255,9 +374,10 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
 
 // KDA_TRIL_FUSED_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernel for every launch, "heads4" the 4-head kernel for every launch (one
-// round or not; the tests use it to reach its edge cases on small problems);
+// round or not; the tests use it to reach its edge cases on small problems),
+// "cols" the four-wavefronts-per-chunk-head kernel for every launch;
 // anything else, or unset, chooses by the number of rounds and of heads.
-enum class Layout { kAuto, kWave, kHeads4 };
+enum class Layout { kAuto, kWave, kHeads4, kCols };
 
 // Heads from which multi-round launches take the 4-head kernel. With few
 // heads the rows of a chunk's heads are close together anyway, so the
@@ -269,10 +389,26 @@ enum class Layout { kAuto, kWave, kHeads4 };
 // 16 52.5 / 46.9, 32 47.6 / 44.5, 64 44.6 / 42.6; 4,096 at H = 1 22.8 / 32.9;
 // 6,144 at H = 6 34.2 / 38.7.
 constexpr int kHeads4MinHeads = 9;
+
+// Chunk-heads per compute unit up to which launches take the
+// four-wavefronts-per-chunk-head kernel. Requests of 64 tokens over 64 heads
+// (µs per call, back to back, same box; one-wavefront / column kernel):
+// 64 chunk-heads 4.96 / 4.08, 128 5.02 / 4.12, 256 5.05 / 4.25, 512 5.80 /
+// 5.69 (16 heads, bf16 A: 5.65 / 5.66), 1024 6.70 / 7.55, 2048 11.4 / 13.4.
+constexpr long kColsPerCu = 2;
+
+static long device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
 static Layout fused_layout() {
     const char *e = getenv("KDA_TRIL_FUSED_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return Layout::kWave;
     if (e && strcmp(e, "heads4") == 0) return Layout::kHeads4;
+    if (e && strcmp(e, "cols") == 0) return Layout::kCols;
     return Layout::kAuto;
 }
 
@@ -289,6 +425,11 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);
             hipLaunchKernelGGL((tril_inv_fused_heads4<EI, EO>), dim3((unsigned)g),
+                               dim3(kFusedThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+        if (lay == Layout::kCols || (lay == Layout::kAuto && waves <= kColsPerCu * device_cus())) {
+            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO>), dim3((unsigned)waves),
                                dim3(kFusedThreads), 0, stream, p);
             return hipGetLastError();
         }
