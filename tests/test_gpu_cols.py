@@ -1,13 +1,14 @@
-"""GPU tests of the fused solver's four-wavefronts-per-chunk-head kernel.
+"""GPU tests of the fused solver's column kernel.
 
-Launches whose chunk-heads fit on the GPU several times over (a 64-token
-request over 64 heads, a few short requests) run tril_inv_fused_cols: one
-workgroup per chunk-head, wavefront J computes block column J of X, and after
-one barrier wavefront I stores block row I. KDA_TRIL_FUSED_LAYOUT=cols makes
-every launch use it, so these tests also reach it on problems that take
-several rounds. Every case is compared with the oracle and, bit for bit,
-with the one-wavefront kernel (layout "wave"), whose products it runs in the
-same order.
+Launches of few chunk-heads per compute unit (a 64-token request over 64
+heads, a few short requests) run tril_inv_fused_cols: one workgroup per
+chunk-head, its four (or two) wavefronts compute one (or two) block columns
+of X each, and after one barrier they store the block rows.
+KDA_TRIL_FUSED_LAYOUT=cols (four wavefronts) and =cols2 (two) make every
+launch use it, so these tests also reach it on problems that take several
+rounds. Every case is compared with the oracle and, bit for bit, with the
+one-wavefront kernel (layout "wave"), whose products it runs in the same
+order.
 """
 import numpy as np
 import pytest
@@ -33,20 +34,26 @@ def kt():
     return tril_solve_amd
 
 
-def _cols_and_wave(monkeypatch, call):
-    """call() under the column kernel and under the one-wavefront one."""
+@pytest.fixture(params=["cols", "cols2"])
+def lay(request):
+    return request.param
+
+
+def _cols_and_wave(monkeypatch, call, lay):
+    """call() under the column kernel (layout `lay`) and under the
+    one-wavefront one."""
     out = {}
-    for lay in ("cols", "wave"):
-        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
-        out[lay] = call()
+    for name in (lay, "wave"):
+        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", name)
+        out[name] = call()
         torch.cuda.synchronize()
     monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT")
-    return out["cols"], out["wave"]
+    return out[lay], out["wave"]
 
 
 @pytest.mark.parametrize("H", [1, 3, 4, 7, 64])
-def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
-    print(f"\n[cols] H={H}", flush=True)
+def test_head_counts_and_partial_chunks(kt, monkeypatch, lay, H):
+    print(f"\n[cols] {lay} H={H}", flush=True)
     A = synth.delta_rule_A(LENGTHS, H, seed=600 + H, upper="nan")
     cu = synth.cu_seqlens(LENGTHS)
     T = A.shape[0]
@@ -58,7 +65,7 @@ def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
         kt.tril_inv(Ad[:T], cud, algo="fused", out=X[:T])
         return X
 
-    Xc, Xw = _cols_and_wave(monkeypatch, run)
+    Xc, Xw = _cols_and_wave(monkeypatch, run, lay)
     assert torch.equal(Xc, Xw)
     X = Xc.cpu().numpy().astype(np.float64)
     assert np.all(X[T:] == CANARY), "a row past the last request was written"
@@ -68,7 +75,7 @@ def test_head_counts_and_partial_chunks(kt, monkeypatch, H):
 
 @pytest.mark.parametrize("a_dtype,x_dtype", [("f32", "bf16"), ("bf16", "f32"), ("f16", "f16"),
                                              ("bf16", "bf16"), ("f16", "f32")])
-def test_dtypes(kt, monkeypatch, a_dtype, x_dtype):
+def test_dtypes(kt, monkeypatch, lay, a_dtype, x_dtype):
     H = 6
     A32 = synth.delta_rule_A(LENGTHS, H, seed=610)
     A = {"f32": A32, "bf16": synth.to_bf16_bits(A32), "f16": synth.to_f16_bits(A32)}[a_dtype]
@@ -77,25 +84,25 @@ def test_dtypes(kt, monkeypatch, a_dtype, x_dtype):
     cud = torch.from_numpy(cu).to(DEV)
     xt = gh.out_torch_dtype(x_dtype)
     Xc, Xw = _cols_and_wave(monkeypatch,
-                            lambda: kt.tril_inv(Ad, cud, out_dtype=xt, algo="fused"))
+                            lambda: kt.tril_inv(Ad, cud, out_dtype=xt, algo="fused"), lay)
     assert torch.equal(Xc, Xw)
     ref = oracle.tril_inv_packed(A, cu, a_dtype)
     assert gh.excess(gh.to_numpy_f64(Xc), ref, x_dtype) <= 0
 
 
-def test_dense_layout_and_chunk_map(kt, monkeypatch):
+def test_dense_layout_and_chunk_map(kt, monkeypatch, lay):
     H = 5
     B, T = 3, 150
     A = synth.delta_rule_A([T] * B, H, seed=620)
     Ad = torch.from_numpy(A).to(DEV)
     Xc, Xw = _cols_and_wave(monkeypatch,
-                            lambda: kt.tril_inv(Ad.view(B, T, H, 64), algo="fused"))
+                            lambda: kt.tril_inv(Ad.view(B, T, H, 64), algo="fused"), lay)
     assert torch.equal(Xc, Xw)
     cu = synth.cu_seqlens([T] * B)
     cud = torch.from_numpy(cu).to(DEV)
     cmap = torch.from_numpy(gh.host_chunk_map([T] * B)).to(DEV)
     Xm, _ = _cols_and_wave(monkeypatch,
-                           lambda: kt.tril_inv(Ad, cud, chunk_indices=cmap, algo="fused"))
+                           lambda: kt.tril_inv(Ad, cud, chunk_indices=cmap, algo="fused"), lay)
     assert torch.equal(Xm.view(B, T, H, 64), Xc)
     ref = oracle.tril_inv_packed(A, cu)
     assert gh.excess(gh.to_numpy_f64(Xm), ref, "f32") <= 0
@@ -104,7 +111,7 @@ def test_dense_layout_and_chunk_map(kt, monkeypatch):
 @pytest.mark.parametrize("cu,clamped", [([0, 64, 200], [0, 64, 100]),
                                         ([-40, 64, 100], [24, 64, 100]),
                                         ([0, 64, 100, 300], [0, 64, 100, 100])])
-def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
+def test_malformed_cu_seqlens_clamped(kt, monkeypatch, lay, cu, clamped):
     """Chunks outside rows [0, T) are skipped or cut at T: nothing past T is
     read (NaN there) or written (canaries)."""
     H = 3
@@ -118,7 +125,7 @@ def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
         kt.tril_inv(Ad[:T], cud, algo="fused", out=X[:T])
         return X
 
-    Xc, Xw = _cols_and_wave(monkeypatch, run)
+    Xc, Xw = _cols_and_wave(monkeypatch, run, lay)
     assert torch.equal(Xc, Xw)
     X = Xc.cpu().numpy().astype(np.float64)
     assert np.all(X[T:] == CANARY)
@@ -130,7 +137,7 @@ def test_malformed_cu_seqlens_clamped(kt, monkeypatch, cu, clamped):
     assert gh.excess(X[:T][rows], ref[rows], "f32") <= 0
 
 
-def test_multi_round_problem(kt, monkeypatch):
+def test_multi_round_problem(kt, monkeypatch, lay):
     """Forced on a problem of many rounds (one workgroup per chunk-head, the
     GPU schedules them in turn): the same X as the 4-head kernel the launch
     would otherwise run."""
@@ -138,16 +145,16 @@ def test_multi_round_problem(kt, monkeypatch):
     A = torch.from_numpy(d["A"]).to(DEV)
     cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
     out = {}
-    for lay in ("cols", "heads4"):
-        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
-        out[lay] = kt.tril_inv(A, cu, algo="fused")
+    for name in (lay, "heads4"):
+        monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", name)
+        out[name] = kt.tril_inv(A, cu, algo="fused")
         torch.cuda.synchronize()
-    assert torch.equal(out["cols"], out["heads4"])
+    assert torch.equal(out[lay], out["heads4"])
 
 
 def test_auto_choice_on_small_workloads(kt):
-    """Without the variable, a 64-token request over 64 heads (64 chunk-heads)
-    runs the column kernel: the same X as the forced layouts."""
+    """Without the variable, a 64-token request over 64 heads (64 chunk-heads,
+    the column kernel's size) is solved within tolerance of the oracle."""
     d = synth.make("packed_1x64_h64_f32")
     A = torch.from_numpy(d["A"]).to(DEV)
     cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
@@ -156,10 +163,10 @@ def test_auto_choice_on_small_workloads(kt):
     assert gh.excess(X.cpu().numpy().astype(np.float64), ref, "f32") <= 0
 
 
-def test_graph_capture_replay(kt, monkeypatch):
+def test_graph_capture_replay(kt, monkeypatch, lay):
     """Captured in a HIP graph and replayed on new inputs, with eager work and
     synchronisation between replays: every replay equals the eager result."""
-    monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", "cols")
+    monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", lay)
     lengths = [64, 100, 9]
     H = 8
     inputs = [synth.delta_rule_A(lengths, H, seed=s) for s in (641, 642, 643)]

@@ -96,31 +96,42 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 }
 
 // ------------------------------------------------------------------------
-// Latency form for launches that leave compute units idle (every chunk-head
-// fits on the GPU four times over, e.g. one 64-token request over 64
-// heads): a workgroup of four wavefronts per chunk-head, wavefront J for
-// block column J. The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
+// Latency form for launches that leave compute units idle (at most one
+// chunk-head per compute unit, e.g. one 64-token request over 64 heads): a
+// workgroup of W = 2 (or 4) wavefronts per chunk-head, each for two (or one)
+// block columns. The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
 // only blocks of column J above row I and the diagonal inverses, so the
 // columns need nothing from each other: each wavefront inverts the four
 // diagonal blocks itself (the same lanes and steps as the one-wavefront
-// kernel, at the same cost as one block), runs its column's products in
-// the one-wavefront kernel's order, and writes X_JJ..X_3J into the staging
-// rows of their block rows; after one barrier wavefront I stores block row
-// I. The longest chain of products is column 0's 36 instead of all 64 in
-// one wavefront, the stores of the four block rows run at once, and X is
-// the same bit for bit.
+// kernel, at the same cost as one block), runs its columns' products in the
+// one-wavefront kernel's order, and writes X_JJ..X_3J into the staging rows
+// of their block rows; after one barrier the wavefronts store the block
+// rows. The longest chain of products is 36 instead of all 64 in one
+// wavefront (two wavefronts: columns 0 and 3, beside columns 1 and 2's 28;
+// four: column 0, beside 20, 8 and none), the block rows are stored at once,
+// and X is the same bit for bit.
 
-template <class EI, int J>
+// Columns of wavefront w out of W: one each for W = 4; for W = 2, columns 0
+// and 3 (36 products) and columns 1 and 2 (28).
+__host__ __device__ constexpr int column_mask(int W, int w) {
+    return W == 4 ? 1 << w : (w == 0 ? 0x9 : 0x6);
+}
+__host__ __device__ constexpr int lowest_column(int mask) {
+    return (mask & 1) ? 0 : (mask & 2) ? 1 : (mask & 4) ? 2 : 3;
+}
+
+// The diagonal rows and the blocks below the diagonal from column J0 on.
+template <class EI, int J0>
 __device__ __forceinline__ void load_column_tile(Tile &t, const TileView<EI> &A, int lane) {
     load_diag_row_quads<EI>(t.dg, A, lane);
     __builtin_amdgcn_sched_barrier(0);  // the diagonal solve waits for these only
     const int g = lane >> 4, m = lane & 15;
     const uint32_t off = (uint32_t)(m * A.rstride + 4 * g) * EI::kBytes;
 #pragma unroll
-    for (int I = J + 1; I < 4; ++I) {
+    for (int I = J0 + 1; I < 4; ++I) {
         const Rsrc r = A.rows_from(16 * I);
 #pragma unroll
-        for (int K = J; K < I; ++K) t.blk[I][K] = load4<EI>(r, off + 16 * K * EI::kBytes);
+        for (int K = J0; K < I; ++K) t.blk[I][K] = load4<EI>(r, off + 16 * K * EI::kBytes);
     }
 }
 
@@ -132,18 +143,11 @@ __host__ __device__ constexpr int col_stage_base(int I) {
 }
 constexpr int kColStageFloats = col_stage_base(4);
 
-template <class EI, int J>
-__device__ __forceinline__ void column_merge(const Problem &p, const Chunk &ch, int h, float *xs,
-                                             float *stage, int lane) {
-    const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
-                             ((long)ch.start * p.heads + h) * kChunk,
-                         p.heads * kChunk, ch.len, kChunk};
-    Tile t;
-    load_column_tile<EI, J>(t, A, opaque_lane(lane));
-    float arow[16];
-    tile_diag_rows<true>(t, arow);
-    diag_inverses(xs, arow, opaque_lane(lane));
-    const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
+// Block column J of X, staged into the rows of its block rows
+// (store_block_row's layout).
+template <int J, class Eng>
+__device__ __forceinline__ void merge_column(const Eng &eng, const Tile &t, float *stage,
+                                             int lane) {
     const f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     f4 x[4];
     x[J] = eng.xkk(J);
@@ -154,7 +158,6 @@ __device__ __forceinline__ void column_merge(const Problem &p, const Chunk &ch, 
         for (int K = J; K < I; ++K) acc = eng.mm(t.blk[I][K], x[K], acc);
         x[I] = eng.negx(I, acc);
     }
-    // X_IJ into block row I's staging, columns 16J.. (store_block_row's layout)
     const int g = lane >> 4, n = lane & 15;
 #pragma unroll
     for (int I = J; I < 4; ++I) {
@@ -162,6 +165,24 @@ __device__ __forceinline__ void column_merge(const Problem &p, const Chunk &ch, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[(4 * g + r) * stage_row(I) + 16 * J + n] = x[I][r];
     }
+}
+
+template <class EI, int MASK>
+__device__ __forceinline__ void merge_columns(const Problem &p, const Chunk &ch, int h,
+                                              float *xs, float *stage, int lane) {
+    const TileView<EI> A{static_cast<const typename EI::T *>(p.A) +
+                             ((long)ch.start * p.heads + h) * kChunk,
+                         p.heads * kChunk, ch.len, kChunk};
+    Tile t;
+    load_column_tile<EI, lowest_column(MASK)>(t, A, opaque_lane(lane));
+    float arow[16];
+    tile_diag_rows<true>(t, arow);
+    diag_inverses(xs, arow, opaque_lane(lane));
+    const MfmaEngine<kXsBlock, kXsCol> eng{xs, lane};
+    if constexpr ((MASK & 1) != 0) merge_column<0>(eng, t, stage, lane);
+    if constexpr ((MASK & 2) != 0) merge_column<1>(eng, t, stage, lane);
+    if constexpr ((MASK & 4) != 0) merge_column<2>(eng, t, stage, lane);
+    if constexpr ((MASK & 8) != 0) merge_column<3>(eng, t, stage, lane);
 }
 
 // Rows 16I..16I+15 of X from block row I's staging: four whole rows per store
@@ -183,9 +204,10 @@ __device__ __forceinline__ void store_staged_row(const TileView<EO> &X, const fl
     }
 }
 
-template <class EI, class EO>
-__global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_cols(Problem p) {
-    __shared__ __attribute__((aligned(16))) float xs_all[kFusedWaves * kLdsPerWave];
+template <class EI, class EO, int W>
+__global__ __launch_bounds__(kWave * W) void tril_inv_fused_cols(Problem p) {
+    static_assert(W == 2 || W == 4, "two or four wavefronts per chunk-head");
+    __shared__ __attribute__((aligned(16))) float xs_all[W * kLdsPerWave];
     __shared__ __attribute__((aligned(16))) float stage[kColStageFloats];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -195,23 +217,27 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_cols(Problem p) 
     const int h = (int)(w - (long)slot * p.heads);
     const Chunk ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
     if (ch.len <= 0) return;  // the same for the whole workgroup
-    switch (wid) {
-        case 0: column_merge<EI, 0>(p, ch, h, xs, stage, lane); break;
-        case 1: column_merge<EI, 1>(p, ch, h, xs, stage, lane); break;
-        case 2: column_merge<EI, 2>(p, ch, h, xs, stage, lane); break;
-        default: column_merge<EI, 3>(p, ch, h, xs, stage, lane); break;
+    if constexpr (W == 4) {
+        switch (wid) {
+            case 0: merge_columns<EI, column_mask(4, 0)>(p, ch, h, xs, stage, lane); break;
+            case 1: merge_columns<EI, column_mask(4, 1)>(p, ch, h, xs, stage, lane); break;
+            case 2: merge_columns<EI, column_mask(4, 2)>(p, ch, h, xs, stage, lane); break;
+            default: merge_columns<EI, column_mask(4, 3)>(p, ch, h, xs, stage, lane); break;
+        }
+    } else if (wid == 0) {
+        merge_columns<EI, column_mask(2, 0)>(p, ch, h, xs, stage, lane);
+    } else {
+        merge_columns<EI, column_mask(2, 1)>(p, ch, h, xs, stage, lane);
     }
     __syncthreads();
-    if (ch.len <= 16 * wid) return;  // block row past the chunk
+    // block row I is stored by wavefront I mod W (rows past the chunk: none)
     const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
                              ((long)ch.start * p.heads + h) * kChunk,
                          p.heads * kChunk, ch.len, kChunk};
-    switch (wid) {
-        case 0: store_staged_row<EO, 0>(X, stage, lane); break;
-        case 1: store_staged_row<EO, 1>(X, stage, lane); break;
-        case 2: store_staged_row<EO, 2>(X, stage, lane); break;
-        default: store_staged_row<EO, 3>(X, stage, lane); break;
-    }
+    if (wid == 0) store_staged_row<EO, 0>(X, stage, lane);
+    if (wid == 1 % W && ch.len > 16) store_staged_row<EO, 1>(X, stage, lane);
+    if (wid == 2 % W && ch.len > 32) store_staged_row<EO, 2>(X, stage, lane);
+    if (wid == 3 % W && ch.len > 48) store_staged_row<EO, 3>(X, stage, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -375,9 +401,11 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
 // KDA_TRIL_FUSED_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernel for every launch, "heads4" the 4-head kernel for every launch (one
 // round or not; the tests use it to reach its edge cases on small problems),
-// "cols" the four-wavefronts-per-chunk-head kernel for every launch;
+// "cols" and "cols2" the column kernel with four and two wavefronts per
+// chunk-head for every launch (the four-wavefront form is kept as the
+// comparison point: at every size measured it was at most level with two);
 // anything else, or unset, chooses by the number of rounds and of heads.
-enum class Layout { kAuto, kWave, kHeads4, kCols };
+enum class Layout { kAuto, kWave, kHeads4, kCols, kCols2 };
 
 // Heads from which multi-round launches take the 4-head kernel. With few
 // heads the rows of a chunk's heads are close together anyway, so the
@@ -390,12 +418,15 @@ enum class Layout { kAuto, kWave, kHeads4, kCols };
 // 6,144 at H = 6 34.2 / 38.7.
 constexpr int kHeads4MinHeads = 9;
 
-// Chunk-heads per compute unit up to which launches take the
-// four-wavefronts-per-chunk-head kernel. Requests of 64 tokens over 64 heads
-// (µs per call, back to back, same box; one-wavefront / column kernel):
-// 64 chunk-heads 4.96 / 4.08, 128 5.02 / 4.12, 256 5.05 / 4.25, 512 5.80 /
-// 5.69 (16 heads, bf16 A: 5.65 / 5.66), 1024 6.70 / 7.55, 2048 11.4 / 13.4.
-constexpr long kColsPerCu = 2;
+// Launches of at most one chunk-head per compute unit take the column kernel
+// with two wavefronts per chunk-head. Requests of 64 tokens over 64 heads
+// (µs per call, back to back, same box; one-wavefront / four-wavefront
+// column / two-wavefront column kernel): 64 chunk-heads 4.90 / 4.04 / 4.02,
+// 128 4.96 / 4.13 / 4.06, 256 5.06 / 4.26 / 4.19, 320 5.31 / 5.30 / 5.37,
+// 384 5.43 / 5.42 / 5.51, 512 5.71 / 5.61 / 5.81, 640 5.96 / 6.31 / 6.05,
+// 1024 6.59 / 7.35 / 7.39. Past one chunk-head per CU the column kernels gain
+// nothing, and from about two per CU they lose.
+constexpr long kColsPerCu = 1;
 
 static long device_cus() {
     int dev = 0, cus = 0;
@@ -409,6 +440,7 @@ static Layout fused_layout() {
     if (e && strcmp(e, "wave") == 0) return Layout::kWave;
     if (e && strcmp(e, "heads4") == 0) return Layout::kHeads4;
     if (e && strcmp(e, "cols") == 0) return Layout::kCols;
+    if (e && strcmp(e, "cols2") == 0) return Layout::kCols2;
     return Layout::kAuto;
 }
 
@@ -428,9 +460,18 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
                                dim3(kFusedThreads), 0, stream, p);
             return hipGetLastError();
         }
-        if (lay == Layout::kCols || (lay == Layout::kAuto && waves <= kColsPerCu * device_cus())) {
-            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO>), dim3((unsigned)waves),
-                               dim3(kFusedThreads), 0, stream, p);
+        // (one workgroup per chunk-head: forced launches keep the grid below
+        // 2^24 workgroups, larger ones take the walking kernel)
+        const bool small = waves < (1L << 24);
+        if (lay == Layout::kCols && small) {
+            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO, 4>), dim3((unsigned)waves),
+                               dim3(kWave * 4), 0, stream, p);
+            return hipGetLastError();
+        }
+        if ((lay == Layout::kCols2 && small) ||
+            (lay == Layout::kAuto && waves <= kColsPerCu * device_cus())) {
+            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO, 2>), dim3((unsigned)waves),
+                               dim3(kWave * 2), 0, stream, p);
             return hipGetLastError();
         }
         return launch_walk(tril_inv_fused_mfma<EI, EO, false>, tril_inv_fused_mfma<EI, EO, true>,
