@@ -190,7 +190,7 @@ def test_kernel_patterns_match_the_kernels_each_workload_runs():
     names = {
         "packed_16x512_h64_f32": ["void kda::tril_inv_fused_heads4<kda::F32, kda::F32>(kda::Problem)",
                                   "void kda::tril_inv_fused_mfma<kda::F32, kda::F32, true>(kda::Problem)",
-                                  "void kda::tril_inv_fused_cols<kda::F32, kda::F32>(kda::Problem)"],
+                                  "void kda::tril_inv_fused_cols<kda::F32, kda::F32, 2, 1>(kda::Problem)"],
         "packed_16x512_h64_c32_f32": ["void kda::tril_inv_c32_group<kda::F32, kda::F32>(kda::Problem)",
                                       "void kda::tril_inv_c32<kda::F32, kda::F32, true>(kda::Problem)"],
         "packed_16x512_h64_c16_f32": ["void kda::tril_inv_c16<kda::F32, kda::F32>(kda::Problem)"],

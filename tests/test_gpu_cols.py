@@ -1,14 +1,16 @@
 """GPU tests of the fused solver's column kernel.
 
-Launches of few chunk-heads per compute unit (a 64-token request over 64
-heads, a few short requests) run tril_inv_fused_cols: one workgroup per
-chunk-head, its four (or two) wavefronts compute one (or two) block columns
-of X each, and after one barrier they store the block rows.
-KDA_TRIL_FUSED_LAYOUT=cols (four wavefronts) and =cols2 (two) make every
-launch use it, so these tests also reach it on problems that take several
-rounds. Every case is compared with the oracle and, bit for bit, with the
-one-wavefront kernel (layout "wave"), whose products it runs in the same
-order.
+Launches of at most two chunk-heads per compute unit (a 64-token request over
+64 heads, a few short requests) run tril_inv_fused_cols: two wavefronts per
+chunk-head (or four) compute two block columns of X each (or one), and after
+one barrier they store the block rows; a workgroup holds one chunk-head or
+two. KDA_TRIL_FUSED_LAYOUT=cols2, cols2p (two chunk-heads per workgroup) and
+cols4 make every launch use one form, so these tests also reach them on
+problems that take several rounds. Every case is compared with the oracle
+and, bit for bit, with the one-wavefront kernel (layout "wave"), whose
+products it runs in the same order. The one-wavefront kernel's one-round
+launches (workgroups of one wavefront, or of four past two chunk-heads per
+CU) are compared with the 4-head kernel.
 """
 import numpy as np
 import pytest
@@ -34,7 +36,7 @@ def kt():
     return tril_solve_amd
 
 
-@pytest.fixture(params=["cols", "cols2"])
+@pytest.fixture(params=["cols2", "cols2p", "cols4"])
 def lay(request):
     return request.param
 
@@ -51,7 +53,7 @@ def _cols_and_wave(monkeypatch, call, lay):
     return out[lay], out["wave"]
 
 
-@pytest.mark.parametrize("H", [1, 3, 4, 7, 64])
+@pytest.mark.parametrize("H", [1, 3, 4, 7, 64])  # odd item counts leave a half-empty workgroup
 def test_head_counts_and_partial_chunks(kt, monkeypatch, lay, H):
     print(f"\n[cols] {lay} H={H}", flush=True)
     A = synth.delta_rule_A(LENGTHS, H, seed=600 + H, upper="nan")
@@ -191,3 +193,29 @@ def test_graph_capture_replay(kt, monkeypatch, lay):
         eager = kt.tril_inv(A, cu, algo="fused")
         torch.cuda.synchronize()
         assert torch.equal(X, eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("requests", [1, 4, 9, 16, 40])
+def test_one_round_workgroup_shapes(kt, monkeypatch, requests):
+    """One-round launches of the one-wavefront kernel (64 to 2,560
+    chunk-heads: workgroups of one wavefront up to two chunk-heads per CU, of
+    four beyond) and the automatic choice: X bit for bit that of the 4-head
+    kernel, and within tolerance of the oracle."""
+    lengths = [64] * requests
+    H = 64
+    A = synth.delta_rule_A(lengths, H, seed=650 + requests)
+    cu = synth.cu_seqlens(lengths)
+    Ad = torch.from_numpy(A).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    out = {}
+    for name in ("wave", "heads4", None):
+        if name is None:
+            monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT", raising=False)
+        else:
+            monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", name)
+        out[name] = kt.tril_inv(Ad, cud, algo="fused")
+        torch.cuda.synchronize()
+    assert torch.equal(out["wave"], out["heads4"])
+    assert torch.equal(out[None], out["heads4"])
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(out[None].cpu().numpy().astype(np.float64), ref, "f32") <= 0

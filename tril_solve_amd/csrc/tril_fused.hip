@@ -62,7 +62,10 @@ __device__ __forceinline__ void solve(const Problem &p, const Item &it, const Ti
 // Wavefronts per workgroup: four independent ones for the launches that walk
 // several items each; one for the launches in which every item has its own
 // wavefront (ROWS), so that those items spread over as many compute units as
-// possible (64 matrices: 64 CUs instead of 16).
+// possible (64 matrices: 64 CUs instead of 16). (Workgroups of four for
+// one-round launches past two chunk-heads per CU measured level: 1,024
+// chunk-heads 6.70-6.90 against 6.58-6.74 us, 2,048 10.88-11.14 against
+// 11.08-11.43.)
 template <bool ROWS>
 __host__ __device__ constexpr int waves_per_block() {
     return ROWS ? 1 : kFusedWaves;
@@ -96,10 +99,11 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 }
 
 // ------------------------------------------------------------------------
-// Latency form for launches that leave compute units idle (at most one
-// chunk-head per compute unit, e.g. one 64-token request over 64 heads): a
-// workgroup of W = 2 (or 4) wavefronts per chunk-head, each for two (or one)
-// block columns. The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
+// Latency form for launches that leave compute units idle (at most two
+// chunk-heads per compute unit, e.g. one 64-token request over 64 heads): W =
+// 2 (or 4) wavefronts per chunk-head, each for two (or one) block columns, in
+// workgroups of one chunk-head (two when there are more chunk-heads than
+// CUs, so that no CU runs a second workgroup). The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
 // only blocks of column J above row I and the diagonal inverses, so the
 // columns need nothing from each other: each wavefront inverts the four
 // diagonal blocks itself (the same lanes and steps as the one-wavefront
@@ -204,33 +208,45 @@ __device__ __forceinline__ void store_staged_row(const TileView<EO> &X, const fl
     }
 }
 
-template <class EI, class EO, int W>
-__global__ __launch_bounds__(kWave * W) void tril_inv_fused_cols(Problem p) {
-    static_assert(W == 2 || W == 4, "two or four wavefronts per chunk-head");
-    __shared__ __attribute__((aligned(16))) float xs_all[W * kLdsPerWave];
-    __shared__ __attribute__((aligned(16))) float stage[kColStageFloats];
+// W wavefronts per chunk-head, P chunk-heads per workgroup (consecutive work
+// items); wavefront W * q + j works on the workgroup's q-th chunk-head.
+template <class EI, class EO, int W, int P>
+__global__ __launch_bounds__(kWave * W * P) void tril_inv_fused_cols(Problem p) {
+    static_assert((W == 2 && (P == 1 || P == 2)) || (W == 4 && P == 1),
+                  "two wavefronts per chunk-head, one or two chunk-heads per workgroup, or four");
+    __shared__ __attribute__((aligned(16))) float xs_all[W * P * kLdsPerWave];
+    __shared__ __attribute__((aligned(16))) float stage_all[P * kColStageFloats];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    float *xs = xs_all + wid * kLdsPerWave;
-    const long w = blockIdx.x;  // one chunk-head per workgroup
-    const int slot = (int)(w / p.heads);
-    const int h = (int)(w - (long)slot * p.heads);
-    const Chunk ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
-    if (ch.len <= 0) return;  // the same for the whole workgroup
-    if constexpr (W == 4) {
-        switch (wid) {
-            case 0: merge_columns<EI, column_mask(4, 0)>(p, ch, h, xs, stage, lane); break;
-            case 1: merge_columns<EI, column_mask(4, 1)>(p, ch, h, xs, stage, lane); break;
-            case 2: merge_columns<EI, column_mask(4, 2)>(p, ch, h, xs, stage, lane); break;
-            default: merge_columns<EI, column_mask(4, 3)>(p, ch, h, xs, stage, lane); break;
-        }
-    } else if (wid == 0) {
-        merge_columns<EI, column_mask(2, 0)>(p, ch, h, xs, stage, lane);
-    } else {
-        merge_columns<EI, column_mask(2, 1)>(p, ch, h, xs, stage, lane);
+    const int wall = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int q = wall / W, wid = wall - q * W;
+    float *xs = xs_all + wall * kLdsPerWave;
+    float *stage = stage_all + q * kColStageFloats;
+    const long w = (long)blockIdx.x * P + q;
+    Chunk ch{0, 0};
+    int h = 0;
+    if (w < (long)p.slots * p.heads) {
+        const int slot = (int)(w / p.heads);
+        h = (int)(w - (long)slot * p.heads);
+        ch = uniform(resolve_chunk<kChunk>(p, slot, lane));
     }
-    __syncthreads();
-    // block row I is stored by wavefront I mod W (rows past the chunk: none)
+    if (ch.len > 0) {
+        if constexpr (W == 4) {
+            switch (wid) {
+                case 0: merge_columns<EI, column_mask(4, 0)>(p, ch, h, xs, stage, lane); break;
+                case 1: merge_columns<EI, column_mask(4, 1)>(p, ch, h, xs, stage, lane); break;
+                case 2: merge_columns<EI, column_mask(4, 2)>(p, ch, h, xs, stage, lane); break;
+                default: merge_columns<EI, column_mask(4, 3)>(p, ch, h, xs, stage, lane); break;
+            }
+        } else if (wid == 0) {
+            merge_columns<EI, column_mask(2, 0)>(p, ch, h, xs, stage, lane);
+        } else {
+            merge_columns<EI, column_mask(2, 1)>(p, ch, h, xs, stage, lane);
+        }
+    }
+    __syncthreads();  // every wavefront of the workgroup, with work or not
+    if (ch.len <= 0) return;
+    // block row I is stored by wavefront I mod W of its chunk-head (rows past
+    // the chunk: none)
     const TileView<EO> X{static_cast<typename EO::T *>(p.X) +
                              ((long)ch.start * p.heads + h) * kChunk,
                          p.heads * kChunk, ch.len, kChunk};
@@ -377,6 +393,14 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 
 // ------------------------------------------------------------------ launch
 
+static long device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 // The layout of the diagonal-block loads (ROWS, see Tile) is chosen per
 // launch. When every item has its own wavefront (one round), latency decides
 // and the row-per-lane loads win (64 matrices: 5.7 against 6.3 us on
@@ -401,11 +425,12 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
 // KDA_TRIL_FUSED_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernel for every launch, "heads4" the 4-head kernel for every launch (one
 // round or not; the tests use it to reach its edge cases on small problems),
-// "cols" and "cols2" the column kernel with four and two wavefronts per
-// chunk-head for every launch (the four-wavefront form is kept as the
-// comparison point: at every size measured it was at most level with two);
-// anything else, or unset, chooses by the number of rounds and of heads.
-enum class Layout { kAuto, kWave, kHeads4, kCols, kCols2 };
+// "cols2", "cols2p" and "cols4" the column kernel for every launch, with two
+// wavefronts per chunk-head and one or two chunk-heads per workgroup, or with
+// four wavefronts per chunk-head (kept as the comparison point: at every
+// size measured it was at most level with two); anything else, or unset,
+// chooses by the number of rounds, of chunk-heads per CU and of heads.
+enum class Layout { kAuto, kWave, kHeads4, kCols2, kCols2P, kCols4 };
 
 // Heads from which multi-round launches take the 4-head kernel. With few
 // heads the rows of a chunk's heads are close together anyway, so the
@@ -419,37 +444,50 @@ enum class Layout { kAuto, kWave, kHeads4, kCols, kCols2 };
 constexpr int kHeads4MinHeads = 9;
 
 // Launches of at most one chunk-head per compute unit take the column kernel
-// with two wavefronts per chunk-head. Requests of 64 tokens over 64 heads
-// (µs per call, back to back, same box; one-wavefront / four-wavefront
-// column / two-wavefront column kernel): 64 chunk-heads 4.90 / 4.04 / 4.02,
-// 128 4.96 / 4.13 / 4.06, 256 5.06 / 4.26 / 4.19, 320 5.31 / 5.30 / 5.37,
-// 384 5.43 / 5.42 / 5.51, 512 5.71 / 5.61 / 5.81, 640 5.96 / 6.31 / 6.05,
-// 1024 6.59 / 7.35 / 7.39. Past one chunk-head per CU the column kernels gain
-// nothing, and from about two per CU they lose.
+// with two wavefronts per chunk-head, and launches of at most two per CU the
+// same kernel with two chunk-heads per workgroup (four wavefronts): a second
+// workgroup on a CU costs about as much as the shorter chains save. Requests
+// of 64 tokens over 64 heads, one box, µs per call back to back (one-wavefront
+// kernel / column kernel with two wavefronts per chunk-head, one chunk-head
+// per workgroup / two per workgroup / four wavefronts per chunk-head):
+//   64 chunk-heads   4.92-4.98 / 4.03-4.05 / 4.31-4.33 / 4.04-4.07
+//   256              4.96-5.08 / 4.18-4.25 / 4.66-4.69 / 4.31-4.40
+//   320              5.27-5.39 / 5.42-5.50 / 4.76-4.80 / 5.27-5.29
+//   512              5.64-5.75 / 5.73-5.84 / 5.31-5.35 / 5.59-5.65
+//   640              5.88-6.02 / 6.06-6.16 / 6.18-6.26 / 6.15-6.24
+//   1,024            6.47-6.83 / 7.24-8.31 / 6.79-7.02 / 7.27-7.57
+// and dense 4 x 512 tokens, 16 heads, bf16 A (512 chunk-heads): 5.56-5.70 /
+// 5.69-5.79 / 5.30-5.37 / 5.67-5.72.
 constexpr long kColsPerCu = 1;
+constexpr long kCols2PPerCu = 2;
 
-static long device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    return cus;
-}
 static Layout fused_layout() {
     const char *e = getenv("KDA_TRIL_FUSED_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return Layout::kWave;
     if (e && strcmp(e, "heads4") == 0) return Layout::kHeads4;
-    if (e && strcmp(e, "cols") == 0) return Layout::kCols;
     if (e && strcmp(e, "cols2") == 0) return Layout::kCols2;
+    if (e && strcmp(e, "cols2p") == 0) return Layout::kCols2P;
+    if (e && strcmp(e, "cols4") == 0) return Layout::kCols4;
     return Layout::kAuto;
+}
+
+template <class K>
+static hipError_t launch_cols(K kernel, long chunk_heads, int per_block, int threads,
+                              hipStream_t stream, const Problem &p) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)((chunk_heads + per_block - 1) / per_block)),
+                       dim3(threads), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t stream) {
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
+        // chunk slots x heads (for packed inputs without a chunk map the slots
+        // are an upper bound on the chunks), and chunk-heads that have rows
+        // (a lower bound: exact for dense inputs and chunk maps)
         const long waves = (long)p.slots * p.heads;
+        const long items = min_chunks(p, kChunk) * p.heads;
         const long blocks = walk_blocks(
-            reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves,
-            min_chunks(p, kChunk) * p.heads);
+            reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves, items);
         const Layout lay = fused_layout();
         if (lay == Layout::kHeads4 ||
             (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads)) {
@@ -460,20 +498,17 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
                                dim3(kFusedThreads), 0, stream, p);
             return hipGetLastError();
         }
-        // (one workgroup per chunk-head: forced launches keep the grid below
-        // 2^24 workgroups, larger ones take the walking kernel)
+        // (one workgroup per one or two chunk-heads: forced launches keep the
+        // grid below 2^24 workgroups, larger ones take the walking kernel)
         const bool small = waves < (1L << 24);
-        if (lay == Layout::kCols && small) {
-            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO, 4>), dim3((unsigned)waves),
-                               dim3(kWave * 4), 0, stream, p);
-            return hipGetLastError();
-        }
-        if ((lay == Layout::kCols2 && small) ||
-            (lay == Layout::kAuto && waves <= kColsPerCu * device_cus())) {
-            hipLaunchKernelGGL((tril_inv_fused_cols<EI, EO, 2>), dim3((unsigned)waves),
-                               dim3(kWave * 2), 0, stream, p);
-            return hipGetLastError();
-        }
+        const long cus = lay == Layout::kAuto ? device_cus() : 0;
+        if ((lay == Layout::kCols2 && small) || (lay == Layout::kAuto && items <= kColsPerCu * cus))
+            return launch_cols(tril_inv_fused_cols<EI, EO, 2, 1>, waves, 1, 2 * kWave, stream, p);
+        if ((lay == Layout::kCols2P && small) ||
+            (lay == Layout::kAuto && items <= kCols2PPerCu * cus))
+            return launch_cols(tril_inv_fused_cols<EI, EO, 2, 2>, waves, 2, 4 * kWave, stream, p);
+        if (lay == Layout::kCols4 && small)
+            return launch_cols(tril_inv_fused_cols<EI, EO, 4, 1>, waves, 1, 4 * kWave, stream, p);
         return launch_walk(tril_inv_fused_mfma<EI, EO, false>, tril_inv_fused_mfma<EI, EO, true>,
                            p, stream);
     });
