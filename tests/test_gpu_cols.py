@@ -219,3 +219,37 @@ def test_one_round_workgroup_shapes(kt, monkeypatch, requests):
     assert torch.equal(out[None], out["heads4"])
     ref = oracle.tril_inv_packed(A, cu)
     assert gh.excess(out[None].cpu().numpy().astype(np.float64), ref, "f32") <= 0
+
+
+# (seed, requests, longest request, heads): from a few chunk-heads to several
+# rounds of the GPU, so that the automatic choice lands on each form: the column
+# kernel with one and with two chunk-heads per workgroup, the one-wavefront
+# kernel in one round, walking with few heads, and the 4-head kernel
+SHAPES = [(0, 12, 400, 5), (1, 9, 130, 32), (2, 30, 250, 16), (3, 150, 800, 5),
+          (4, 70, 600, 16), (5, 3, 300, 1)]
+
+
+@pytest.mark.parametrize("seed,requests,longest,H", SHAPES)
+def test_random_shapes_every_form_agrees(kt, monkeypatch, seed, requests, longest, H):
+    """Random request lengths: X bit for bit the same under the automatic
+    choice and under every forced form, and within tolerance of the oracle."""
+    rng = np.random.default_rng(700 + seed)
+    lengths = [int(x) for x in rng.integers(1, longest + 1, requests)]
+    print(f"\n[cols] random seed={seed} requests={requests} tokens={sum(lengths)} H={H}", flush=True)
+    A = synth.delta_rule_A(lengths, H, seed=710 + seed, upper="nan")
+    cu = synth.cu_seqlens(lengths)
+    Ad = torch.from_numpy(A).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    out = {}
+    for name in (None, "wave", "heads4", "cols2", "cols2p", "cols4"):
+        if name is None:
+            monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT", raising=False)
+        else:
+            monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", name)
+        out[name] = kt.tril_inv(Ad, cud, algo="fused")
+        torch.cuda.synchronize()
+    monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT", raising=False)
+    for name, X in out.items():
+        assert torch.equal(X, out["heads4"]), name
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(out[None].cpu().numpy().astype(np.float64), ref, "f32") <= 0
