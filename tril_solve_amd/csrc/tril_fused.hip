@@ -1,16 +1,19 @@
-// Fused KDA chunk solver kernels for gfx950: one wavefront per chunk-head at
-// a time.
+// Fused KDA chunk solver kernels for gfx950, in three forms: one wavefront
+// per chunk-head at a time (the basis of the others), four adjacent heads of a
+// chunk per workgroup with their tiles loaded into LDS (launches of several
+// rounds), and two or four wavefronts per chunk-head, one per pair of block
+// columns or per column (launches that leave compute units idle).
 //
 // LightLLM PR #1703 ("perf(kda): parallelize diagonal solves in Prefill",
 // PR description): invert the four 16x16 diagonal blocks of every 64x64
 // chunk matrix independently, then merge into the 64x64 inverse with FP32
-// tiles. Everything for one chunk-head happens inside one wavefront: the
-// tile goes HBM -> VGPRs, the diagonal inverses go through a small LDS copy,
-// the inverse goes VGPRs -> LDS staging -> HBM as whole rows.
-//
-// The grid is sized to what the GPU holds at once and every wavefront walks
-// chunk-heads with a stride of the grid size, so consecutive wavefronts work
-// on neighbouring heads of the same chunk (adjacent 256-byte rows in HBM).
+// tiles. In the one-wavefront form everything for one chunk-head happens
+// inside one wavefront: the tile goes HBM -> VGPRs, the diagonal inverses go
+// through a small LDS copy, the inverse goes VGPRs -> LDS staging -> HBM as
+// whole rows. Its grid is sized to what the GPU holds at once and every
+// wavefront walks chunk-heads with a stride of the grid size, so consecutive
+// wavefronts work on neighbouring heads of the same chunk (adjacent 256-byte
+// rows in HBM).
 //
 // Traffic per full chunk-head: the ten blocks on or below the diagonal of A
 // are read (the six upper blocks are never needed, so never loaded) and all
@@ -103,9 +106,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_mfma(Problem p) 
 // chunk-heads per compute unit, e.g. one 64-token request over 64 heads): W =
 // 2 (or 4) wavefronts per chunk-head, each for two (or one) block columns, in
 // workgroups of one chunk-head (two when there are more chunk-heads than
-// CUs, so that no CU runs a second workgroup). The merge X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads
-// only blocks of column J above row I and the diagonal inverses, so the
-// columns need nothing from each other: each wavefront inverts the four
+// CUs, so that no CU runs a second workgroup). The merge
+// X_IJ = -X_II * sum_{K=J}^{I-1} A_IK X_KJ reads only blocks of column J
+// above row I and the diagonal inverses, so the columns need nothing from
+// each other: each wavefront inverts the four
 // diagonal blocks itself (the same lanes and steps as the one-wavefront
 // kernel, at the same cost as one block), runs its columns' products in the
 // one-wavefront kernel's order, and writes X_JJ..X_3J into the staging rows
