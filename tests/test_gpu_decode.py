@@ -65,10 +65,15 @@ def _check(kt, inp, d, out, x_dtype="f32"):
     assert e <= 0, f"conv windows exceed tolerance by {e:.3g}"
 
 
+@pytest.mark.parametrize("layout", [None, "pairs", "cols"])
 @pytest.mark.parametrize("W", [2, 3, 4])
 @pytest.mark.parametrize("B,H", [(1, 1), (3, 4), (8, 2), (96, 3)])
-def test_step_parity(kt, B, H, W):
-    print(f"\n[decode] B={B} H={H} W={W}", flush=True)
+def test_step_parity(kt, monkeypatch, B, H, W, layout):
+    """One step against the oracle, under the automatic split of the state
+    over the wavefronts and under each forced one (KDA_TRIL_DECODE_LAYOUT)."""
+    if layout is not None:
+        monkeypatch.setenv("KDA_TRIL_DECODE_LAYOUT", layout)
+    print(f"\n[decode] B={B} H={H} W={W} layout={layout}", flush=True)
     inp = synth.decode_inputs(B, H, W=W, seed=100 + B * 10 + H + W)
     d = _dev(inp)
     _check(kt, inp, d, _step(kt, d))

@@ -20,17 +20,30 @@
 // One workgroup of 256 threads per (sequence, head). The state dominates the
 // traffic (64 KiB read and 64 KiB written per step), so every other input is
 // loaded first and the state tile right after, before any wait; the
-// convolution and the norms then run while the tile is in flight. The state
-// is split by value columns: wavefront w owns columns 32w..32w+31 of all 128
-// key rows (lane l: columns 32w + 4(l % 8) .. +3 of rows 16(l / 8) .. +15), so the
-// reductions over key rows (S^T k and S^T q of the decayed state) stay inside
-// the wavefront (per-lane sums over 16 rows, then lanes xor 8, 16, 32) and
-// each wavefront updates and writes back its columns as soon as its own
-// tile has arrived, with no barrier in between. Since
-// S_new^T q = (decayed S)^T q + (k . q) u, the state is read and written
-// exactly once.
+// convolution and the norms then run while the tile is in flight. Two ways
+// to split the state over the four wavefronts (S_new^T q = (decayed S)^T q +
+// (k . q) u, so either way the state is read and written exactly once):
+//   - by value columns (larger batches): wavefront w owns columns
+//     32w..32w+31 of all 128 key rows (lane l: columns 32w + 4(l % 8) .. +3
+//     of rows 16(l / 8) .. +15), so the reductions over key rows (S^T k and
+//     S^T q of the decayed state) stay inside the wavefront (per-lane sums
+//     over 16 rows, then lanes xor 8, 16, 32) and each wavefront updates and
+//     writes back its columns as soon as its own tile has arrived, with no
+//     barrier in between;
+//   - by pairs of key rows (up to one (sequence, head) pair per compute
+//     unit, where latency rules): wavefront w owns row pairs 4i + w (lanes
+//     0..31 the even row, 32..63 the odd one; lane l: columns 4(l % 32) .. +3),
+//     so every load and store instruction covers two whole rows, 1 KiB of
+//     adjacent bytes instead of eight 128-byte pieces; the row sums of the
+//     four wavefronts meet in LDS after one barrier.
+// Same box, same state pools, B sequences x 32 heads (µs per step, columns /
+// row pairs): B = 2 6.44 / 6.24-6.25, 4 7.31-7.35 / 7.10-7.17, 8 8.98-8.99 /
+// 8.45-8.49, 16 14.98-14.99 / 15.14-15.19 (another box: 14.94-14.96 /
+// 14.52-14.60), 32 27.59-27.60 / 28.41-28.50.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "tril_device.h"
 #include "tril_launch.h"
@@ -111,14 +124,17 @@ __device__ __forceinline__ float wave_sum(float v) {
     return rows_half_add(v);
 }
 
-// One step for one (sequence, head); layouts as in the C ABI.
-template <class EI, class EO>
+// One step for one (sequence, head); layouts as in the C ABI. PAIRS: the
+// state split by pairs of key rows, else by value columns.
+template <class EI, class EO, bool PAIRS>
 __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProblem p) {
     // per key row: padded (row r at r + r / 16), so the 8 rows a wavefront
     // reads at once (16 apart) fall in distinct banks
     __shared__ float yq[kDecPad], yk[kDecPad], gq[kDecPad];
     __shared__ __align__(16) float yv[kDecD], zs[kDecD], nws[kDecD];  // per value column
-    __shared__ float red[kDecThreads / kWave];
+    // row sums of each wavefront (PAIRS), or each wavefront's sum of o^2
+    __shared__ __align__(16) float red_k[kDecThreads / kWave][kDecD];
+    __shared__ __align__(16) float red_q[kDecThreads / kWave][kDecD];
 
     const int t = threadIdx.x;
     const int b = blockIdx.x / p.H, h = blockIdx.x - b * p.H;
@@ -161,16 +177,18 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     // z (threads 0..127) and norm_w (threads 128..255), kept in LDS until the end
     const float zraw = ld_elem<EI>(static_cast<const typename EI::T *>(p.z), bh * kDecD + c);
     const float nwraw = p.norm_w[c];
-    // this lane's 4 value columns and its 16 consecutive key rows
+    // this lane's 4 value columns and its 16 key rows
     const int l = t & (kWave - 1);
-    const int col = 32 * wv + 4 * (l & 7), row0 = 16 * (l >> 3);
+    const int col = PAIRS ? 4 * (l & 31) : 32 * wv + 4 * (l & 7);
+    const int half = l >> 5;  // PAIRS: the row of the pair
+    auto key_row = [&](int i) { return PAIRS ? 2 * (4 * i + wv) + half : 16 * (l >> 3) + i; };
 
     // 2. then the state tile of this lane
     float *S = p.state + ((long)slot * p.H + h) * kDecD * kDecD + col;
     f4 s[kDecRows];
 #pragma unroll
     for (int i = 0; i < kDecRows; ++i)
-        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(long)(row0 + i) * kDecD]));
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(long)key_row(i) * kDecD]));
     __builtin_amdgcn_sched_barrier(0);  // keep every use of the loads below this point
 
     // 3. causal convolution over the window of the W - 1 previous inputs and
@@ -220,16 +238,38 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     f4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = pa;
 #pragma unroll
     for (int i = 0; i < kDecRows; ++i) {
-        const int r = pad_row(row0 + i);
+        const int r = pad_row(key_row(i));
         s[i] *= gq[r];
         pa += s[i] * yk[r];
         pb += s[i] * yq[r];
     }
-    // sums over the eight lanes with the same l % 8 (l, l ^ 8, l ^ 16, ...)
+    if constexpr (PAIRS) {
+        // the two rows of each pair (lanes l and l ^ 32), then the four
+        // wavefronts in order, so every lane of a column gets the same bits
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        pa[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pa[j])));
-        pb[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pb[j])));
+        for (int j = 0; j < 4; ++j) {
+            pa[j] = rows_half_add(pa[j]);
+            pb[j] = rows_half_add(pb[j]);
+        }
+        if (half == 0) {
+            *reinterpret_cast<f4 *>(&red_k[wv][col]) = pa;
+            *reinterpret_cast<f4 *>(&red_q[wv][col]) = pb;
+        }
+        __syncthreads();
+        pa = *reinterpret_cast<const f4 *>(&red_k[0][col]);
+        pb = *reinterpret_cast<const f4 *>(&red_q[0][col]);
+#pragma unroll
+        for (int w = 1; w < kDecThreads / kWave; ++w) {
+            pa += *reinterpret_cast<const f4 *>(&red_k[w][col]);
+            pb += *reinterpret_cast<const f4 *>(&red_q[w][col]);
+        }
+    } else {
+        // sums over the eight lanes with the same l % 8 (l, l ^ 8, l ^ 16, ...)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pa[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pa[j])));
+            pb[j] = rows_half_add(rows_pair_add(dpp_add<kRowRor8>(pb[j])));
+        }
     }
 
     // 6. u = beta (v - S^T k), state update S += k u^T written back in place,
@@ -238,18 +278,27 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     const f4 u = beta * (v4 - pa * sk);
 #pragma unroll
     for (int i = 0; i < kDecRows; ++i) {
-        const float ki = yk[pad_row(row0 + i)] * sk;
-        __builtin_nontemporal_store(s[i] + ki * u, reinterpret_cast<f4 *>(&S[(long)(row0 + i) * kDecD]));
+        const float ki = yk[pad_row(key_row(i))] * sk;
+        __builtin_nontemporal_store(s[i] + ki * u, reinterpret_cast<f4 *>(&S[(long)key_row(i) * kDecD]));
     }
     const f4 o = pb * sq + (dqk * sq * sk) * u;
 
-    // 7. gated RMSNorm of o over the 128 value columns
+    // 7. gated RMSNorm of o over the 128 value columns: PAIRS, lanes 0..31 of
+    //    every wavefront hold all of them and wavefront 0 writes the output;
+    //    else lanes 0..7 of each wavefront hold its 32, and each writes those
     float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
     ss = dpp_add<kHalfMirror>(dpp_add<kQuadXor2>(dpp_add<kQuadXor1>(ss)));  // over 8 lanes
-    if (l == 0) red[wv] = ss;
-    __syncthreads();
-    if (l < 8) {
-        const float ms = (red[0] + red[1] + red[2] + red[3]) / kDecD;
+    float ms;
+    if constexpr (PAIRS) {
+        if (wv != 0 || half != 0) return;
+        ms = rows_pair_add(dpp_add<kRowMirror>(ss)) / kDecD;  // lanes 0..31
+    } else {
+        if (l == 0) red_k[0][wv] = ss;
+        __syncthreads();
+        if (l >= 8) return;
+        ms = (red_k[0][0] + red_k[0][1] + red_k[0][2] + red_k[0][3]) / kDecD;
+    }
+    {
         const float rn = 1.0f / __builtin_sqrtf(ms + p.eps_norm);
         const f4 z4 = *reinterpret_cast<const f4 *>(&zs[col]);
         const f4 w4 = *reinterpret_cast<const f4 *>(&nws[col]);
@@ -261,10 +310,25 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_step_kernel(DecodeProb
     }
 }
 
+// The state split by row pairs up to one (sequence, head) pair per compute
+// unit. (At two per CU the two splits measured level: 14.5-15.2 µs either
+// way, by box.) KDA_TRIL_DECODE_LAYOUT (read on every call) = "pairs" or
+// "cols" forces one split for every launch (the tests reach both on small
+// problems).
+constexpr long kDecPairsPerCu = 1;
+
 hipError_t launch_decode(const DecodeProblem &p, int in_dt, int out_dt, hipStream_t stream) {
+    const char *e = getenv("KDA_TRIL_DECODE_LAYOUT");
+    const bool pairs = e && strcmp(e, "pairs") == 0   ? true
+                       : e && strcmp(e, "cols") == 0 ? false
+                                                     : (long)p.B * p.H <= kDecPairsPerCu * device_cus();
     return dispatch_dtypes<F32, BF16, F16>(in_dt, out_dt, [&]<class EI, class EO>() {
-        auto kernel = kda_decode_step_kernel<EI, EO>;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)(p.B * p.H)), dim3(kDecThreads), 0, stream, p);
+        if (pairs)
+            hipLaunchKernelGGL((kda_decode_step_kernel<EI, EO, true>), dim3((unsigned)(p.B * p.H)),
+                               dim3(kDecThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((kda_decode_step_kernel<EI, EO, false>), dim3((unsigned)(p.B * p.H)),
+                               dim3(kDecThreads), 0, stream, p);
         return hipGetLastError();
     });
 }

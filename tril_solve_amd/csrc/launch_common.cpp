@@ -67,6 +67,14 @@ OccEntry residency(const void *fn, int threads) {
 }
 }  // namespace
 
+long device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 long resident_blocks(const void *fn, int threads) {
     const OccEntry r = residency(fn, threads);
     return r.per_cu * r.cus;

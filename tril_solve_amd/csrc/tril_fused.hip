@@ -397,14 +397,6 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 
 // ------------------------------------------------------------------ launch
 
-static long device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    return cus;
-}
-
 // The layout of the diagonal-block loads (ROWS, see Tile) is chosen per
 // launch. When every item has its own wavefront (one round), latency decides
 // and the row-per-lane loads win (64 matrices: 5.7 against 6.3 us on

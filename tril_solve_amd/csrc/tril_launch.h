@@ -59,6 +59,9 @@ constexpr int kFusedThreads = 64 * kFusedWaves;
 // occupancy is cached per kernel and device.
 long resident_blocks(const void *fn, int threads);
 
+// Compute units of the current device (0 when unknown).
+long device_cus();
+
 // Grid of a grid-stride kernel with kFusedWaves independent wavefronts per
 // workgroup and at most `waves` wavefront work items (at least `min_waves` of
 // them real; the rest are chunk slots past the last chunk, which end after
