@@ -14,7 +14,10 @@
 //     X_10 = -X_11 (A_10 X_00), on the matrix cores. A wavefront takes two
 //     heads of one chunk: its four 16-lane rows run the four diagonal
 //     substitutions of both heads at once, then both merges follow, and the
-//     rows are written through LDS staging as whole 2-head rows.
+//     rows are written through LDS staging as whole 2-head rows. Launches of
+//     several rounds with 32 heads or more give a workgroup one chunk and
+//     eight heads instead, their rows loaded straight into LDS (the group
+//     kernel below), with the same arithmetic.
 //
 // Both kernels walk their work items (chunk, group of heads) with a grid
 // stride like the 64-token kernel, and compute in FP32 with the same

@@ -9,6 +9,9 @@
 // [slots * H, 4, 16, 16], each tile column-major; the merge kernel reads them
 // with the off-diagonal blocks of A and writes X. Per full chunk-head this
 // moves 8 KiB more than the fused kernel (tiles written once, read once).
+// Both kernels come in two forms with the same arithmetic: one wavefront per
+// chunk-head, and four adjacent heads of a chunk per workgroup with their
+// tiles loaded into LDS (launches of several rounds with two heads or more).
 #include <stdlib.h>
 #include <string.h>
 
