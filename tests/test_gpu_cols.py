@@ -253,3 +253,25 @@ def test_random_shapes_every_form_agrees(kt, monkeypatch, seed, requests, longes
         assert torch.equal(X, out["heads4"]), name
     ref = oracle.tril_inv_packed(A, cu)
     assert gh.excess(out[None].cpu().numpy().astype(np.float64), ref, "f32") <= 0
+
+
+@pytest.mark.parametrize("name", ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32"])
+def test_repeats_bitwise(kt, name):
+    """100 back-to-back calls of the small workloads (column kernel with one
+    and with two chunk-heads per workgroup under the automatic choice): every
+    result equals the first bit for bit."""
+    d = synth.make(name)
+    A = gh.to_torch_input(d["A"], d["a_dtype"], DEV)
+    xt = gh.out_torch_dtype(d["x_dtype"])
+    if d["layout"] == "dense":
+        A = A.view(d["B"], d["T"], d["H"], 64)
+        X0 = kt.tril_inv(A, out_dtype=xt)
+        run = lambda: kt.tril_inv(A, out_dtype=xt)  # noqa: E731
+    else:
+        cu = torch.from_numpy(d["cu_seqlens"]).to(DEV)
+        X0 = kt.tril_inv(A, cu, out_dtype=xt)
+        run = lambda: kt.tril_inv(A, cu, out_dtype=xt)  # noqa: E731
+    outs = [run() for _ in range(100)]
+    torch.cuda.synchronize()
+    for i, X in enumerate(outs):
+        assert torch.equal(X, X0), f"repeat {i}"

@@ -280,3 +280,27 @@ def test_slots_past_4gib_of_state(kt):
     e = gh.excess(cs[idx].cpu().numpy().astype(np.float64), ref_cs, "f32")
     assert e <= 0, f"conv windows exceed tolerance by {e:.3g}"
     assert bool((S[2000] == 7.0).all())
+
+
+@pytest.mark.parametrize("layout", ["pairs", "cols"])
+def test_repeats_bitwise(kt, monkeypatch, layout):
+    """50 steps from the same state pools and inputs, under each split of the
+    state over the wavefronts: every output, state and conv window equals the
+    first run's bit for bit (the row sums of the row-pair split meet in a
+    fixed order)."""
+    monkeypatch.setenv("KDA_TRIL_DECODE_LAYOUT", layout)
+    inp = synth.decode_inputs(8, 32, seed=131)
+    d = _dev(inp)
+    S0, C0 = d["state"].clone(), d["conv_state"].clone()
+    first = None
+    for rep in range(50):
+        d["state"].copy_(S0)
+        d["conv_state"].copy_(C0)
+        out = _step(kt, d)
+        got = (out.clone(), d["state"].clone(), d["conv_state"].clone())
+        if first is None:
+            first = got
+            _check(kt, inp, d, out)
+        else:
+            for a, b in zip(got, first):
+                assert torch.equal(a, b), f"repeat {rep}"
