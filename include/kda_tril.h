@@ -74,7 +74,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_F16 = 2 } kda_dtype;
  *            summary: by chunk occupancy, to bound scratch). An ineligible
  *            SPLIT silently falls back to FUSED.
  *   FUSED  - one kernel: diagonal inverses and merges of a chunk-head in one
- *            wavefront, merge products on the FP32 matrix cores (MFMA).
+ *            wavefront (small launches: two wavefronts, each merging two
+ *            block columns), merge products on the FP32 matrix cores
+ *            (MFMA); every form gives the same bits.
  *   SPLIT  - two kernels: the diagonal kernel writes the four FP32 16 x 16
  *            inverse tiles of every chunk-head to the workspace, the merge
  *            kernel reads them back with A and writes X. Needs workspace of
