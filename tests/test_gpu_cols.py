@@ -224,9 +224,11 @@ def test_one_round_workgroup_shapes(kt, monkeypatch, requests):
 # (seed, requests, longest request, heads): from a few chunk-heads to several
 # rounds of the GPU, so that the automatic choice lands on each form: the column
 # kernel with one and with two chunk-heads per workgroup, the one-wavefront
-# kernel in one round, walking with few heads, and the 4-head kernel
+# kernel in one round, walking with few heads, and the 4-head kernel; many
+# tiny requests, whose chunks ceil(T / 64) undercounts, stay off the column
+# kernel
 SHAPES = [(0, 12, 400, 5), (1, 9, 130, 32), (2, 30, 250, 16), (3, 150, 800, 5),
-          (4, 70, 600, 16), (5, 3, 300, 1)]
+          (4, 70, 600, 16), (5, 3, 300, 1), (6, 200, 3, 64)]  # the last: many tiny requests
 
 
 @pytest.mark.parametrize("seed,requests,longest,H", SHAPES)

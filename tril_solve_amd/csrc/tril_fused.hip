@@ -438,6 +438,12 @@ enum class Layout { kAuto, kWave, kHeads4, kCols2, kCols2P, kCols4 };
 // 16 52.5 / 46.9, 32 47.6 / 44.5, 64 44.6 / 42.6; 4,096 at H = 1 22.8 / 32.9;
 // 6,144 at H = 6 34.2 / 38.7.
 constexpr int kHeads4MinHeads = 9;
+// ... and only while the chunks are mostly full: when the chunk-heads that
+// have rows (ceil(T / 64) per head) are fewer than half the chunk slots, as
+// for many requests of a few tokens, the tile loads and barriers of the
+// 4-head kernel cost more than they save (200 requests of 1-3 tokens over 64
+// heads: 18.6 us against 14.6-15.2; 100 requests of 1-20 tokens: 12.1
+// against 9.0-9.4).
 
 // Launches of at most one chunk-head per compute unit take the column kernel
 // with two wavefronts per chunk-head, and launches of at most two per CU the
@@ -454,8 +460,13 @@ constexpr int kHeads4MinHeads = 9;
 //   1,024            6.47-6.83 / 7.24-8.31 / 6.79-7.02 / 7.27-7.57
 // and dense 4 x 512 tokens, 16 heads, bf16 A (512 chunk-heads): 5.56-5.70 /
 // 5.69-5.79 / 5.30-5.37 / 5.67-5.72.
+// The rules count the chunk-heads that have rows (a lower bound for packed
+// inputs without a chunk map: ceil(T / 64) chunks per head) and also bound
+// the chunk slots (an upper bound), so that many short requests, whose
+// chunks the lower bound undercounts, keep the per-wavefront kernel.
 constexpr long kColsPerCu = 1;
 constexpr long kCols2PPerCu = 2;
+constexpr long kColsSlotsPerCu = 2;  // chunk slots x heads per CU (x 2 with two per workgroup)
 
 static Layout fused_layout() {
     const char *e = getenv("KDA_TRIL_FUSED_LAYOUT");
@@ -486,7 +497,8 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
             reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves, items);
         const Layout lay = fused_layout();
         if (lay == Layout::kHeads4 ||
-            (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads)) {
+            (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads &&
+             2 * items >= waves)) {
             const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);
@@ -498,10 +510,12 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
         // grid below 2^24 workgroups, larger ones take the walking kernel)
         const bool small = waves < (1L << 24);
         const long cus = lay == Layout::kAuto ? device_cus() : 0;
-        if ((lay == Layout::kCols2 && small) || (lay == Layout::kAuto && items <= kColsPerCu * cus))
+        if ((lay == Layout::kCols2 && small) ||
+            (lay == Layout::kAuto && items <= kColsPerCu * cus && waves <= kColsSlotsPerCu * cus))
             return launch_cols(tril_inv_fused_cols<EI, EO, 2, 1>, waves, 1, 2 * kWave, stream, p);
         if ((lay == Layout::kCols2P && small) ||
-            (lay == Layout::kAuto && items <= kCols2PPerCu * cus))
+            (lay == Layout::kAuto && items <= kCols2PPerCu * cus &&
+             waves <= 2 * kColsSlotsPerCu * cus))
             return launch_cols(tril_inv_fused_cols<EI, EO, 2, 2>, waves, 2, 4 * kWave, stream, p);
         if (lay == Layout::kCols4 && small)
             return launch_cols(tril_inv_fused_cols<EI, EO, 4, 1>, waves, 1, 4 * kWave, stream, p);
