@@ -285,6 +285,11 @@ constexpr int kHeadsGroup32 = 8;
 // per-wavefront / group): H = 1 27.0 / 77.7, 2 26.0 / 37.6, 4 26.2 / 26.3,
 // 8 25.6 / 25.4, 12 26.0 / 28.6, 16 26.0 / 25.8, 32 26.0 / 25.8, 64 26.0 / 25.1:
 // below 32 heads the two are within noise of each other or the group loses.
+// It also needs mostly full chunks (chunks with rows, ceil(T / 32), at least
+// half the chunk slots): for many requests of a few tokens its tile loads and
+// barriers cost more than they save (64 heads, 200 requests of 1-3 tokens
+// 9.4-9.6 us against 8.1-8.4; 400 requests of 1-10 tokens 19.8-20.1 against
+// 16.1-16.7).
 constexpr int kGroup32MinHeads = 32;
 constexpr int kSlot32 = 1040;
 
@@ -451,15 +456,20 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
         if (chunk == 32) {
             // the ROWS = false variant sizes the grid; one-round launches run
             // the row-per-lane variant, longer ones the group kernel when
-            // there are enough heads, else the ROWS = false variant
+            // there are enough heads and the chunks are mostly full, else the
+            // ROWS = false variant (the row-per-lane one when the chunks are
+            // mostly empty: 200 requests of 1-3 tokens over 64 heads 7.7-7.9
+            // against 8.0-8.3 us; single long requests at 4 and 16 heads
+            // 25.7-26.1 against 26.3-26.5 the other way)
             const long groups = (p.heads + kHeads32 - 1) / kHeads32;
             const long items = (long)p.slots * groups;
             const long blocks =
                 walk_blocks(reinterpret_cast<const void *>(tril_inv_c32<EI, EO, false>), items,
                             min_chunks(p, 32) * groups);
+            const bool multi = blocks * kFusedWaves < items;
+            const bool full = 2 * min_chunks(p, 32) >= p.slots;
             const int lay = small_layout();
-            if (lay == 2 ||
-                (lay == 0 && blocks * kFusedWaves < items && p.heads >= kGroup32MinHeads)) {
+            if (lay == 2 || (lay == 0 && multi && full && p.heads >= kGroup32MinHeads)) {
                 const long g8 = (long)p.slots * ((p.heads + kHeadsGroup32 - 1) / kHeadsGroup32);
                 const long gb = group_blocks(
                     reinterpret_cast<const void *>(tril_inv_c32_group<EI, EO>), g8);
@@ -467,7 +477,7 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
                                    dim3(kFusedThreads), 0, stream, p);
                 return hipGetLastError();
             }
-            if (lay == 1 && blocks * kFusedWaves < items)
+            if (multi && (lay == 1 || full))
                 return launch_groups(tril_inv_c32<EI, EO, false>, p, 32, kHeads32, stream);
             return launch_groups(tril_inv_c32<EI, EO, true>, p, 32, kHeads32, stream);
         }
