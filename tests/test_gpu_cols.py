@@ -255,6 +255,9 @@ def test_random_shapes_every_form_agrees(kt, monkeypatch, seed, requests, longes
         assert torch.equal(X, out["heads4"]), name
     ref = oracle.tril_inv_packed(A, cu)
     assert gh.excess(out[None].cpu().numpy().astype(np.float64), ref, "f32") <= 0
+    # the VALU merge on the same launch rules (its own products' order)
+    Xv = kt.tril_inv(Ad, cud, algo="fused_valu")
+    assert gh.excess(Xv.cpu().numpy().astype(np.float64), ref, "f32") <= 0
 
 
 @pytest.mark.parametrize("name", ["packed_1x64_h64_f32", "dense_b4_t512_h16_bf16_f32"])

@@ -403,8 +403,13 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 // MI355X). When wavefronts walk several items, the 16-row loads with lane
 // swaps were faster on 16 x 512 tokens (0.9%) and on the 48 ragged requests
 // (1.3-3.5%); on long single requests the two measured within 2% of each
-// other, in either order depending on the machine. The ROWS = false variant
-// sizes the grid (its registers allow fewer wavefronts).
+// other, in either order depending on the machine. Walks over mostly empty
+// chunks (fewer chunks with rows, ceil(T / 64), than half the chunk slots:
+// many requests of a few tokens) run the row-per-lane variant as well, in
+// workgroups of one wavefront: 64 heads, 200 requests of 1-3 tokens 12.6-13.1
+// against 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7 against 9.0-9.8, 400 of
+// 1-10 tokens 27.7-27.9 against 30.2-31.4 (same bits). The ROWS = false
+// variant sizes the grid (its registers allow fewer wavefronts).
 template <class KT, class KR>
 static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t stream) {
     const long waves = (long)p.slots * p.heads;
@@ -413,6 +418,9 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
     const bool one_round = blocks * kFusedWaves >= waves;
     if (one_round)  // one item per workgroup of one wavefront
         hipLaunchKernelGGL(krows, dim3((unsigned)waves), dim3(kWave), 0, stream, p);
+    else if (2 * min_chunks(p, kChunk) < p.slots)  // the same wavefronts, walking
+        hipLaunchKernelGGL(krows, dim3((unsigned)(blocks * kFusedWaves)), dim3(kWave), 0, stream,
+                           p);
     else
         hipLaunchKernelGGL(ktput, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
