@@ -280,3 +280,37 @@ def test_repeats_bitwise(kt, name):
     torch.cuda.synchronize()
     for i, X in enumerate(outs):
         assert torch.equal(X, X0), f"repeat {i}"
+
+
+def test_short_chunks_dense_and_chunk_map(kt, monkeypatch):
+    """Short chunks that the chunk count cannot reveal: a caller chunk map of
+    many short requests, and a dense batch of 100 rows of 10 tokens (the
+    automatic choice walks them with the row-per-lane kernel): X bit for bit
+    that of the 4-head kernel, and within tolerance of the oracle."""
+    H = 64
+    rng = np.random.default_rng(660)
+    lengths = [int(x) for x in rng.integers(1, 12, 150)]
+    A = synth.delta_rule_A(lengths, H, seed=661)
+    cu = synth.cu_seqlens(lengths)
+    Ad = torch.from_numpy(A).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    cmap = torch.from_numpy(gh.host_chunk_map(lengths)).to(DEV)
+    B, T = 100, 10
+    Adn = torch.from_numpy(synth.delta_rule_A([T] * B, H, seed=662)).to(DEV)
+    out = {}
+    for name in (None, "heads4"):
+        if name is None:
+            monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT", raising=False)
+        else:
+            monkeypatch.setenv("KDA_TRIL_FUSED_LAYOUT", name)
+        out[name] = (kt.tril_inv(Ad, cud, chunk_indices=cmap, algo="fused"),
+                     kt.tril_inv(Adn.view(B, T, H, 64), algo="fused"))
+        torch.cuda.synchronize()
+    monkeypatch.delenv("KDA_TRIL_FUSED_LAYOUT", raising=False)
+    assert torch.equal(out[None][0], out["heads4"][0])
+    assert torch.equal(out[None][1], out["heads4"][1])
+    ref = oracle.tril_inv_packed(A, cu)
+    assert gh.excess(out[None][0].cpu().numpy().astype(np.float64), ref, "f32") <= 0
+    refn = oracle.tril_inv_packed(Adn.cpu().numpy(), synth.cu_seqlens([T] * B))
+    assert gh.excess(out[None][1].view(B * T, H, 64).cpu().numpy().astype(np.float64), refn,
+                     "f32") <= 0

@@ -404,8 +404,8 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 // swaps were faster on 16 x 512 tokens (0.9%) and on the 48 ragged requests
 // (1.3-3.5%); on long single requests the two measured within 2% of each
 // other, in either order depending on the machine. Walks over mostly empty
-// chunks (fewer chunks with rows, ceil(T / 64), than half the chunk slots:
-// many requests of a few tokens) run the row-per-lane variant as well, in
+// chunks (many requests, or dense rows, of a few tokens) run the
+// row-per-lane variant as well, in
 // workgroups of one wavefront: 64 heads, 200 requests of 1-3 tokens 12.6-13.1
 // against 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7 against 9.0-9.8, 400 of
 // 1-10 tokens 27.7-27.9 against 30.2-31.4 (same bits). The ROWS = false
@@ -418,7 +418,7 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
     const bool one_round = blocks * kFusedWaves >= waves;
     if (one_round)  // one item per workgroup of one wavefront
         hipLaunchKernelGGL(krows, dim3((unsigned)waves), dim3(kWave), 0, stream, p);
-    else if (2 * min_chunks(p, kChunk) < p.slots)  // the same wavefronts, walking
+    else if (!chunks_mostly_full(p, kChunk))  // the same wavefronts, walking
         hipLaunchKernelGGL(krows, dim3((unsigned)(blocks * kFusedWaves)), dim3(kWave), 0, stream,
                            p);
     else
@@ -446,9 +446,9 @@ enum class Layout { kAuto, kWave, kHeads4, kCols2, kCols2P, kCols4 };
 // 16 52.5 / 46.9, 32 47.6 / 44.5, 64 44.6 / 42.6; 4,096 at H = 1 22.8 / 32.9;
 // 6,144 at H = 6 34.2 / 38.7.
 constexpr int kHeads4MinHeads = 9;
-// ... and only while the chunks are mostly full: when the chunk-heads that
-// have rows (ceil(T / 64) per head) are fewer than half the chunk slots, as
-// for many requests of a few tokens, the tile loads and barriers of the
+// ... and only while the chunks are mostly full: when the tokens would fill
+// fewer than half the chunk slots, as for many requests of a few tokens,
+// the tile loads and barriers of the
 // 4-head kernel cost more than they save (200 requests of 1-3 tokens over 64
 // heads: 18.6 us against 14.6-15.2; 100 requests of 1-20 tokens: 12.1
 // against 9.0-9.4).
@@ -506,7 +506,7 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
         const Layout lay = fused_layout();
         if (lay == Layout::kHeads4 ||
             (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads &&
-             2 * items >= waves)) {
+             chunks_mostly_full(p, kChunk))) {
             const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);

@@ -100,6 +100,13 @@ inline long min_chunks(const Problem &p, int C) {
     return p.slots;
 }
 
+// Whether the chunks of a call are mostly full: its tokens would fill at
+// least half of its chunk slots (many requests, or dense rows, of a few
+// tokens are not).
+inline bool chunks_mostly_full(const Problem &p, int C) {
+    return 2 * (((long)p.total_tokens + C - 1) / C) >= p.slots;
+}
+
 // Calls f.template operator()<EI, EO>() for the element types of the codes.
 template <class EF32, class EBF16, class EF16, class F>
 hipError_t dispatch_dtypes(int a_dt, int x_dt, F &&f) {

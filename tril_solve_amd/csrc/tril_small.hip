@@ -285,8 +285,8 @@ constexpr int kHeadsGroup32 = 8;
 // per-wavefront / group): H = 1 27.0 / 77.7, 2 26.0 / 37.6, 4 26.2 / 26.3,
 // 8 25.6 / 25.4, 12 26.0 / 28.6, 16 26.0 / 25.8, 32 26.0 / 25.8, 64 26.0 / 25.1:
 // below 32 heads the two are within noise of each other or the group loses.
-// It also needs mostly full chunks (chunks with rows, ceil(T / 32), at least
-// half the chunk slots): for many requests of a few tokens its tile loads and
+// It also needs mostly full chunks (the tokens would fill at least half the
+// chunk slots): for many requests of a few tokens its tile loads and
 // barriers cost more than they save (64 heads, 200 requests of 1-3 tokens
 // 9.4-9.6 us against 8.1-8.4; 400 requests of 1-10 tokens 19.8-20.1 against
 // 16.1-16.7).
@@ -467,7 +467,7 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
                 walk_blocks(reinterpret_cast<const void *>(tril_inv_c32<EI, EO, false>), items,
                             min_chunks(p, 32) * groups);
             const bool multi = blocks * kFusedWaves < items;
-            const bool full = 2 * min_chunks(p, 32) >= p.slots;
+            const bool full = chunks_mostly_full(p, 32);
             const int lay = small_layout();
             if (lay == 2 || (lay == 0 && multi && full && p.heads >= kGroup32MinHeads)) {
                 const long g8 = (long)p.slots * ((p.heads + kHeadsGroup32 - 1) / kHeadsGroup32);
