@@ -14,9 +14,9 @@ namespace {
 // memory pattern reaches the same rate with 16 and with 32 wavefronts per CU,
 // and fewer leave too few bytes in flight.
 constexpr long kMinWavesPerCu = 16;
-// Rounds of a multi-head launch (groups per resident workgroup) from which
-// the grid takes one workgroup per CU fewer.
-constexpr long kLongRounds = 16;
+// Largest grid of a multi-head launch: its 256-thread workgroups stay far
+// below the 2^32 work-items of one dispatch; larger problems walk.
+constexpr long kMaxGroupGrid = 1L << 22;
 
 struct OccEntry {
     const void *fn;
@@ -102,15 +102,9 @@ long walk_blocks(const void *fn, long waves, long min_waves) {
 }
 
 long group_blocks(const void *fn, long groups) {
+    long cap = kMaxGroupGrid;
     const OccEntry r = residency(fn, kFusedThreads);
-    if (r.per_cu <= 0 || r.cus <= 0) return groups;
-    long per_cu = r.per_cu;
-    // Long problems run one workgroup per CU fewer than the occupancy allows
-    // when that still leaves two or more: on 131,072 tokens x 64 heads 2 per
-    // CU took 601-603 us against 637-641 us at 3, while at 8,192 tokens and
-    // at 48 ragged requests (2.7 and 11 rounds) 3 per CU was 1-4% faster.
-    if (!r.forced && per_cu >= 3 && groups >= kLongRounds * per_cu * r.cus) per_cu -= 1;
-    const long cap = per_cu * r.cus;
+    if (r.forced && r.cus > 0 && r.per_cu * r.cus < cap) cap = r.per_cu * r.cus;
     return cap < groups ? cap : groups;
 }
 

@@ -74,8 +74,14 @@ long device_cus();
 long walk_blocks(const void *fn, long waves, long min_waves);
 
 // Grid of a grid-stride kernel whose workgroups (kFusedThreads threads) walk
-// `groups` work items together: what the device holds at once, one workgroup
-// per CU fewer for long problems (16 or more rounds), at most `groups`.
+// `groups` work items together: one workgroup per group, so that the
+// hardware dispatcher hands each free workgroup slot the next group and no
+// compute unit is left with a fixed share that it finishes late (same bits,
+// 2-8% faster than a grid of what the device holds at once, one workgroup per
+// CU fewer for long problems: 64 heads, 16 x 512 tokens 42.1 -> 41.4 us, 48
+// ragged requests 117.6 -> 107.6, one request of 131,072 tokens 585 -> 571;
+// the split plan's pair of kernels 920 -> 864 us on the last). Walks only past
+// 2^22 groups, or on the grid KDA_TRIL_BLOCKS_PER_CU asks for.
 long group_blocks(const void *fn, long groups);
 
 // Element-type codes of A and X: the kda_dtype values (0 f32, 1 bf16, 2 f16).

@@ -19,8 +19,9 @@
 //     eight heads instead, their rows loaded straight into LDS (the group
 //     kernel below), with the same arithmetic.
 //
-// Both kernels walk their work items (chunk, group of heads) with a grid
-// stride like the 64-token kernel, and compute in FP32 with the same
+// The per-wavefront kernels walk their work items (chunk, group of heads)
+// with a grid stride like the 64-token kernel (the group kernel's grid has
+// one workgroup per item). All compute in FP32 with the same
 // operation order as the 64-token kernel's corresponding blocks, so a 16- or
 // 32-token chunk gives bit for bit the leading block of the 64-token result
 // on the same (zero-padded) rows.
