@@ -140,6 +140,10 @@ kda_status kda_tril_inv_dense(const void *A, kda_dtype a_dtype, void *X, kda_dty
  *                  that reuses one map across layers would keep it; NULL to
  *                  let the kernels resolve chunks from cu_seqlens on the
  *                  device (grid sized by the bound floor(T/64) + num_seqs).
+ *                  The device scan costs each chunk one dependent memory
+ *                  round trip per 64 requests before it, so with hundreds of
+ *                  requests a map is much faster (64 heads, 2,000 requests of
+ *                  1-20 tokens on MI355X: 126 us with a map, 301 us without).
  *   num_chunks     length of chunk_indices (0 when it is NULL).
  */
 kda_status kda_tril_inv_packed(const void *A, kda_dtype a_dtype, void *X, kda_dtype x_dtype,

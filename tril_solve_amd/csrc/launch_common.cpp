@@ -75,6 +75,11 @@ long device_cus() {
     return cus;
 }
 
+bool blocks_forced() {
+    const char *e = getenv("KDA_TRIL_BLOCKS_PER_CU");
+    return e != nullptr && atoi(e) > 0;
+}
+
 long resident_blocks(const void *fn, int threads) {
     const OccEntry r = residency(fn, threads);
     return r.per_cu * r.cus;

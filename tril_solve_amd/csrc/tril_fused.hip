@@ -10,8 +10,8 @@
 // tiles. In the one-wavefront form everything for one chunk-head happens
 // inside one wavefront: the tile goes HBM -> VGPRs, the diagonal inverses go
 // through a small LDS copy, the inverse goes VGPRs -> LDS staging -> HBM as
-// whole rows. Its grid is sized to what the GPU holds at once and every
-// wavefront walks chunk-heads with a stride of the grid size, so consecutive
+// whole rows. Its grid has one wavefront per chunk-head (a grid that is
+// forced smaller walks them with a stride of the grid size), so consecutive
 // wavefronts work on neighbouring heads of the same chunk (adjacent 256-byte
 // rows in HBM).
 //
@@ -400,31 +400,39 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 // ------------------------------------------------------------------ launch
 
 // The layout of the diagonal-block loads (ROWS, see Tile) is chosen per
-// launch. When every item has its own wavefront (one round), latency decides
-// and the row-per-lane loads win (64 matrices: 5.7 against 6.3 us on
-// MI355X). When wavefronts walk several items, the 16-row loads with lane
-// swaps were faster on 16 x 512 tokens (0.9%) and on the 48 ragged requests
-// (1.3-3.5%); on long single requests the two measured within 2% of each
-// other, in either order depending on the machine. Walks over mostly empty
-// chunks (many requests, or dense rows, of a few tokens) run the
-// row-per-lane variant as well, in
-// workgroups of one wavefront: 64 heads, 200 requests of 1-3 tokens 12.6-13.1
-// against 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7 against 9.0-9.8, 400 of
-// 1-10 tokens 27.7-27.9 against 30.2-31.4 (same bits). The ROWS = false
-// variant sizes the grid (its registers allow fewer wavefronts).
+// launch. When every item has its own wavefront in one round, latency
+// decides and the row-per-lane loads win (64 matrices: 5.7 against 6.3 us on
+// MI355X). Past one round, the 16-row loads with lane swaps were faster on 16
+// x 512 tokens (0.9%) and on the 48 ragged requests (1.3-3.5%); on long
+// single requests the two measured within 2% of each other, in either order
+// depending on the machine. Mostly empty chunks (many requests, or dense
+// rows, of a few tokens) take the row-per-lane variant in workgroups of one
+// wavefront there too: 64 heads, 200 requests of 1-3 tokens 12.6-13.1 against
+// 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7 against 9.0-9.8, 400 of 1-10
+// tokens 27.7-27.9 against 30.2-31.4 (same bits). Every launch has one
+// wavefront per item, so the hardware dispatcher hands each free slot the
+// next one; a grid of what the GPU holds at once, each wavefront walking a
+// fixed share, was slower (same bits): 8 heads, 4 requests of 32,768 tokens
+// 78.6 against 74.9 us; 64 heads, 2,000 requests of 1-20 tokens 333.9
+// against 301.9; the VALU merge on 131,072 tokens 758 against 632, on the 48
+// ragged requests 158.3 against 148.1. Wavefronts walk only on a grid that
+// KDA_TRIL_BLOCKS_PER_CU forces.
 template <class KT, class KR>
 static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t stream) {
     const long waves = (long)p.slots * p.heads;
     const long blocks = walk_blocks(reinterpret_cast<const void *>(ktput), waves,
                                     min_chunks(p, kChunk) * p.heads);
     const bool one_round = blocks * kFusedWaves >= waves;
+    const bool walk = blocks_forced();
     if (one_round)  // one item per workgroup of one wavefront
         hipLaunchKernelGGL(krows, dim3((unsigned)waves), dim3(kWave), 0, stream, p);
-    else if (!chunks_mostly_full(p, kChunk))  // the same wavefronts, walking
-        hipLaunchKernelGGL(krows, dim3((unsigned)(blocks * kFusedWaves)), dim3(kWave), 0, stream,
-                           p);
+    else if (!chunks_mostly_full(p, kChunk))  // the same wavefronts
+        hipLaunchKernelGGL(krows, dim3((unsigned)(walk ? blocks * kFusedWaves : waves)),
+                           dim3(kWave), 0, stream, p);
     else
-        hipLaunchKernelGGL(ktput, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, p);
+        hipLaunchKernelGGL(ktput,
+                           dim3((unsigned)(walk ? blocks : (waves + kFusedWaves - 1) / kFusedWaves)),
+                           dim3(kFusedThreads), 0, stream, p);
     return hipGetLastError();
 }
 

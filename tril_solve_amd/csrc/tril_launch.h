@@ -73,6 +73,9 @@ long device_cus();
 // memory system with fewer requests in flight while the others finish.
 long walk_blocks(const void *fn, long waves, long min_waves);
 
+// Whether KDA_TRIL_BLOCKS_PER_CU forces the grid size (read on every call).
+bool blocks_forced();
+
 // Grid of a grid-stride kernel whose workgroups (kFusedThreads threads) walk
 // `groups` work items together: one workgroup per group, so that the
 // hardware dispatcher hands each free workgroup slot the next group and no
