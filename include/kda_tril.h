@@ -38,7 +38,8 @@
  * Errors: plain status codes; nothing is thrown across the ABI. Problems that
  * the host can see (null pointers with nonzero sizes, H <= 0, unknown dtype,
  * forced SPLIT with too little workspace; KDA_ERR_UNSUPPORTED for sizes past
- * the int32 token range or H > 4096) are reported before any launch.
+ * the int32 token range, H > 4096, or chunk slots x H past 2^26 - 4, the
+ * wavefronts one launch can hold) are reported before any launch.
  * Device-side cu_seqlens are not validated (that would need a
  * synchronisation): they must start at 0, be non-decreasing and end at
  * <= total_tokens; kernels clamp every row index to [0, total_tokens) so a

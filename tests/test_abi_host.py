@@ -126,6 +126,10 @@ def test_unsupported_sizes(kt):
     U = kt.KDA_ERR_UNSUPPORTED
     assert _packed(kt, T=2**31) == U
     assert _dense(kt, B=2**20, T=2**12) == U
+    # chunk slots x heads = 2^26 - 1: one wavefront each fits 2^32 threads,
+    # but not once rounded up to whole 4-wavefront workgroups
+    slots = (2**26 - 1) // 3
+    assert _dense(kt, T=64 * slots, H=3, X=1 << 44) == U
 
 
 def test_forced_split_workspace_errors(kt):

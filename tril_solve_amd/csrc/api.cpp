@@ -29,10 +29,12 @@ bool valid_algo(kda_algo a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_FUSED_V
 bool valid_chunk(int32_t c) { return c == 16 || c == 32 || c == 64; }
 size_t dtype_bytes(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
 
-// At most one wavefront of 64 lanes per chunk slot and head; the launch must
-// stay below 2^32 threads.
+// One wavefront of 64 lanes per chunk slot and head, in workgroups of up to
+// four wavefronts: the launch, rounded up to whole workgroups, must stay
+// below 2^32 threads.
 bool grid_fits(int64_t slots, int32_t H) {
-    return slots <= kMaxTokens && slots * (int64_t)H * 64 < (int64_t)UINT32_MAX;
+    const int64_t waves = slots * (int64_t)H;
+    return slots <= kMaxTokens && (waves + 3) / 4 * 256 <= (int64_t)UINT32_MAX;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
