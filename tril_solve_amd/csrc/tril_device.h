@@ -315,8 +315,8 @@ __device__ __forceinline__ Chunk uniform(Chunk c) {
 }
 
 // The lane index made opaque to the optimiser: values derived from it are
-// then recomputed where used instead of being hoisted out of the persistent
-// loop and held in registers for the kernel's lifetime.
+// then recomputed where used instead of being hoisted out of the walk over
+// work items and held in registers for the kernel's lifetime.
 __device__ __forceinline__ int opaque_lane(int lane) {
     asm volatile("" : "+v"(lane));
     return lane;

@@ -70,7 +70,11 @@ long device_cus();
 // holds b workgroups per compute unit, b - 1 is used instead if that leaves
 // fewer idle wavefront slots in the last round and still 16 or more
 // wavefronts per CU: wavefronts with one item fewer than the rest leave the
-// memory system with fewer requests in flight while the others finish.
+// memory system with fewer requests in flight while the others finish. The
+// 16- and 32-token and split per-wavefront kernels launch this grid; the
+// 64-token and build-A launchers use it to tell one-round launches from
+// longer ones and launch it only when KDA_TRIL_BLOCKS_PER_CU is set (else one
+// wavefront per item).
 long walk_blocks(const void *fn, long waves, long min_waves);
 
 // Whether KDA_TRIL_BLOCKS_PER_CU forces the grid size (read on every call).
