@@ -402,14 +402,15 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_fused_valu(Problem p) 
 // The layout of the diagonal-block loads (ROWS, see Tile) is chosen per
 // launch. When every item has its own wavefront in one round, latency
 // decides and the row-per-lane loads win (64 matrices: 5.7 against 6.3 us on
-// MI355X). Past one round, the 16-row loads with lane swaps were faster on 16
-// x 512 tokens (0.9%) and on the 48 ragged requests (1.3-3.5%); on long
-// single requests the two measured within 2% of each other, in either order
-// depending on the machine. Mostly empty chunks (many requests, or dense
-// rows, of a few tokens) take the row-per-lane variant in workgroups of one
-// wavefront there too: 64 heads, 200 requests of 1-3 tokens 12.6-13.1 against
-// 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7 against 9.0-9.8, 400 of 1-10
-// tokens 27.7-27.9 against 30.2-31.4 (same bits). Every launch has one
+// MI355X). Past one round, with one wavefront per item, the 16-row loads
+// with lane swaps in 4-wavefront workgroups are faster (same bits, us): 16 x
+// 512 tokens 44.4 against 51.7, one request of 131,072 tokens 632 against
+// 756, the 48 ragged requests 116.9 against 135.3, 8 heads, 4 requests of
+// 32,768 tokens 75.6 against 86.5 (level at 2 heads). Mostly empty chunks
+// (many requests, or dense rows, of a few tokens) take the row-per-lane
+// variant in workgroups of one wavefront there too: 64 heads, 200 requests of
+// 1-3 tokens 12.6-13.1 against 14.5-15.3 us, 100 of 1-20 tokens 8.2-8.7
+// against 9.0-9.8, 400 of 1-10 tokens 27.7-27.9 against 30.2-31.4 (same bits). Every launch has one
 // wavefront per item, so the hardware dispatcher hands each free slot the
 // next one; a grid of what the GPU holds at once, each wavefront walking a
 // fixed share, was slower (same bits): 8 heads, 4 requests of 32,768 tokens
