@@ -447,7 +447,16 @@ static hipError_t launch_walk(KT ktput, KR krows, const Problem &p, hipStream_t 
 // chooses by the number of rounds, of chunk-heads per CU and of heads.
 enum class Layout { kAuto, kWave, kHeads4, kCols2, kCols2P, kCols4 };
 
-// Heads from which multi-round launches take the 4-head kernel. With few
+// The 4-head kernel takes launches whose chunk-heads (the lower bound: for a
+// packed scan ceil(T / 64) chunks) exceed what the per-wavefront kernel
+// holds at once at its occupancy, from this many heads. Below that bound
+// the per-wavefront kernel with one wavefront per item is faster (64 heads,
+// same bits: 16 requests of 256 tokens 19.7 against 23.8 us, 48 of 64 tokens
+// 15.1 against 17.4); a launch holding 1.2-1.5 times that many chunk-heads
+// measured level (32.4-32.7 us either way), C3 at 1.6 times 41.7 against
+// 43.3. (The bound once came from the walking grid, one workgroup per CU
+// below the occupancy and over the chunk slots, which sent launches of one
+// round to the 4-head kernel.) With few
 // heads the rows of a chunk's heads are close together anyway, so the
 // per-wavefront loads cover nearly adjacent bytes, and groups of four run
 // partly empty when H is not a multiple of four. Measured on single long
@@ -512,12 +521,14 @@ hipError_t launch_fused_mfma(const Problem &p, int a_dt, int x_dt, hipStream_t s
         // (a lower bound: exact for dense inputs and chunk maps)
         const long waves = (long)p.slots * p.heads;
         const long items = min_chunks(p, kChunk) * p.heads;
-        const long blocks = walk_blocks(
-            reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>), waves, items);
+        const long held = resident_blocks(
+                              reinterpret_cast<const void *>(tril_inv_fused_mfma<EI, EO, false>),
+                              kFusedThreads) *
+                          kFusedWaves;
         const Layout lay = fused_layout();
         if (lay == Layout::kHeads4 ||
-            (lay == Layout::kAuto && blocks * kFusedWaves < waves && p.heads >= kHeads4MinHeads &&
-             chunks_mostly_full(p, kChunk))) {
+            (lay == Layout::kAuto && p.heads >= kHeads4MinHeads && chunks_mostly_full(p, kChunk) &&
+             items > held)) {
             const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
             const long g = group_blocks(
                 reinterpret_cast<const void *>(tril_inv_fused_heads4<EI, EO>), groups);
