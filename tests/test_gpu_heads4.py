@@ -1,6 +1,7 @@
 """GPU tests of the solver's 4-head kernels on their edge cases.
 
-Launches that take more than one round of the GPU run the 4-head kernels (a
+Launches of more chunk-heads than the per-wavefront kernels hold at once run
+the 4-head kernels (a
 workgroup owns one chunk and four adjacent heads, their tiles loaded into
 LDS): the fused kernel, and the split plan's diagonal and merge kernels. The
 large workloads of the parity tests reach them with 64 heads.

@@ -294,9 +294,9 @@ def _both_small_layouts(monkeypatch, call):
 
 @pytest.mark.parametrize("H", [1, 2, 3, 7, 8, 9, 13])
 def test_c32_group_kernel_edge_cases(kt, monkeypatch, H):
-    """The 8-head group kernel of the 32-token branch (which multi-round
-    launches with 32 heads or more run; KDA_TRIL_SMALL_LAYOUT=group makes
-    every launch use it):
+    """The 8-head group kernel of the 32-token branch (which launches of
+    more than two groups per CU with 32 heads or more run;
+    KDA_TRIL_SMALL_LAYOUT=group makes every launch use it):
     head counts that leave a group partly empty (a wavefront with one head
     or none), partial chunks and NaN above the diagonal; X bit for bit that
     of the per-wavefront kernel, within tolerance of the oracle, and rows past
@@ -348,7 +348,7 @@ def test_c32_group_kernel_dtypes_and_dense(kt, monkeypatch, a_dtype, x_dtype):
 
 @pytest.mark.parametrize("C", SIZES)
 def test_deterministic_across_grids(kt, monkeypatch, C):
-    """The 16 x 512-token, 64-head batch (multi-round: the 32-token group
+    """The 16 x 512-token, 64-head batch (the 32-token group
     kernel, the 16-token walking kernel) on grids of 1, 2, 3 and 5
     workgroups per CU (KDA_TRIL_BLOCKS_PER_CU, read on every call), 10 calls
     each: X is the same bit for bit as on the default grid."""

@@ -450,11 +450,12 @@ enum class Layout { kAuto, kWave, kHeads4, kCols2, kCols2P, kCols4 };
 // The 4-head kernel takes launches whose chunk-heads (the lower bound: for a
 // packed scan ceil(T / 64) chunks) exceed what the per-wavefront kernel
 // holds at once at its occupancy, from this many heads. Below that bound
-// the per-wavefront kernel with one wavefront per item is faster (64 heads,
-// same bits: 16 requests of 256 tokens 19.7 against 23.8 us, 48 of 64 tokens
-// 15.1 against 17.4); a launch holding 1.2-1.5 times that many chunk-heads
-// measured level (32.4-32.7 us either way), C3 at 1.6 times 41.7 against
-// 43.3. (The bound once came from the walking grid, one workgroup per CU
+// the two are level on cold buffers (64 heads, same bits: 16 requests of 256
+// tokens 23.83 us either way, 48 of 64 tokens 18.40 against 18.35) and the
+// per-wavefront kernel is faster when A is partly in the 256 MB cache, as
+// when it was just written (19.7 against 23.8, 15.1 against 17.4); above it
+// the 4-head kernel wins (1.2-1.5 times as many chunk-heads: 32.6-32.7
+// against 34.5-34.7 us; C3, 1.6 times: 41.7 against 44.1). (The bound once came from the walking grid, one workgroup per CU
 // below the occupancy and over the chunk slots, which sent launches of one
 // round to the 4-head kernel.) With few
 // heads the rows of a chunk's heads are close together anyway, so the

@@ -280,6 +280,15 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32(Problem p) {
 // its heads rotated by two positions (128 bytes) for the same reason.
 
 constexpr int kHeadsGroup32 = 8;
+// Groups (chunks with rows x groups of eight heads, a lower bound) per
+// compute unit above which the group kernel takes over from the
+// per-wavefront kernel. Measured on cold buffers (rotations past 1 GB), 64
+// heads, same bits (us, per-wavefront / group): 16 requests of 128 tokens (2
+// groups per CU) 6.75 / 7.40, of 192 (3) 11.46 / 9.48, of 256 (4) 15.17 /
+// 14.34, 32 of 128 (4) 15.13 / 14.30; 32 heads, 16 of 256 (2) 6.83 / 7.38, of
+// 512 (4) 15.15 / 14.93. (The rule once asked for more items than the walking
+// grid held, which left 3-6 groups per CU on the per-wavefront kernel.)
+constexpr long kGroup32PerCu = 2;
 // Heads from which multi-round launches take the group kernel: with fewer the
 // per-wavefront kernel reads nearly adjacent rows anyway and groups of eight
 // run partly empty. Single long requests of 16,384 chunk-heads, same box (µs,
@@ -432,8 +441,8 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_c32_group(Problem p) {
 // KDA_TRIL_SMALL_LAYOUT (read on every call): "wave" runs the per-wavefront
 // 32-token kernel for every launch, "group" the 8-head group kernel for every
 // launch (the tests use it to reach its edge cases on small problems);
-// anything else, or unset, the group kernel when the per-wavefront launch
-// would take more than one round of the GPU.
+// anything else, or unset, the group kernel from more than two groups per
+// compute unit (32 heads or more, mostly full chunks).
 static int small_layout() {
     const char *e = getenv("KDA_TRIL_SMALL_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return 1;
@@ -455,10 +464,10 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
     return dispatch_dtypes<F32, BF16, F16>(a_dt, x_dt, [&]<class EI, class EO>() {
         if (chunk == 16) return launch_groups(tril_inv_c16<EI, EO>, p, 16, kHeads16, stream);
         if (chunk == 32) {
-            // the ROWS = false variant sizes the grid; one-round launches run
-            // the row-per-lane variant, longer ones the group kernel when
-            // there are enough heads and the chunks are mostly full, else the
-            // ROWS = false variant (the row-per-lane one when the chunks are
+            // the group kernel from more than two groups per CU when there
+            // are enough heads and the chunks are mostly full; else the
+            // ROWS = false variant sizes the grid, one-round launches run the
+            // row-per-lane variant and longer ones the ROWS = false variant (the row-per-lane one when the chunks are
             // mostly empty: 200 requests of 1-3 tokens over 64 heads 7.7-7.9
             // against 8.0-8.3 us; single long requests at 4 and 16 heads
             // 25.7-26.1 against 26.3-26.5 the other way)
@@ -470,8 +479,10 @@ hipError_t launch_small(const Problem &p, int chunk, int a_dt, int x_dt, hipStre
             const bool multi = blocks * kFusedWaves < items;
             const bool full = chunks_mostly_full(p, 32);
             const int lay = small_layout();
-            if (lay == 2 || (lay == 0 && multi && full && p.heads >= kGroup32MinHeads)) {
-                const long g8 = (long)p.slots * ((p.heads + kHeadsGroup32 - 1) / kHeadsGroup32);
+            const long heads8 = (p.heads + kHeadsGroup32 - 1) / kHeadsGroup32;
+            if (lay == 2 || (lay == 0 && full && p.heads >= kGroup32MinHeads &&
+                             min_chunks(p, 32) * heads8 > kGroup32PerCu * device_cus())) {
+                const long g8 = (long)p.slots * heads8;
                 const long gb = group_blocks(
                     reinterpret_cast<const void *>(tril_inv_c32_group<EI, EO>), g8);
                 hipLaunchKernelGGL((tril_inv_c32_group<EI, EO>), dim3((unsigned)gb),
