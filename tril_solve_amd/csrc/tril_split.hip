@@ -205,8 +205,10 @@ __global__ __launch_bounds__(kFusedThreads) void tril_inv_split_merge_heads4(Pro
 
 // KDA_TRIL_SPLIT_LAYOUT (read on every call): "wave" runs the per-wavefront
 // kernels for every launch, "heads4" the 4-head ones for every launch;
-// anything else, or unset, the 4-head ones when the per-wavefront launch
-// would not fit on the device at once and there are two heads or more.
+// anything else, or unset, the 4-head ones from more than two chunk-heads
+// with rows per compute unit when there are two heads or more.
+constexpr long kSplitHeads4PerCu = 2;
+
 static int split_layout() {
     const char *e = getenv("KDA_TRIL_SPLIT_LAYOUT");
     if (e && strcmp(e, "wave") == 0) return 1;
@@ -222,11 +224,14 @@ static hipError_t launch_split_t(const Problem &p, hipStream_t stream) {
     // (A single head leaves three of a group's four wavefronts idle: on a
     // 524,288-token request the per-wavefront kernels took 63-65 µs against
     // 75-76; from two heads on the 4-head ones win, 60 against 63 at H = 2.)
+    // The 4-head kernels take over from more than two chunk-heads per CU,
+    // well before the per-wavefront launch stops fitting on the GPU at once
+    // (cold buffers, 64 heads, same bits, us, per-wavefront / 4-head: 512
+    // chunk-heads 10.12 / 10.47, 1,024 12.57 / 11.98, 2,048 19.36 / 17.44,
+    // 4,096 34.40 / 31.66; 16 heads, 512: 10.31 / 10.53).
     const bool heads4 =
-        lay == 2 ||
-        (lay == 0 && p.heads >= 2 &&
-         blocks > resident_blocks(reinterpret_cast<const void *>(tril_inv_split_merge<EI, EO>),
-                                  kFusedThreads));
+        lay == 2 || (lay == 0 && p.heads >= 2 &&
+                     min_chunks(p, kChunk) * p.heads > kSplitHeads4PerCu * device_cus());
     if (heads4) {
         const long groups = (long)p.slots * ((p.heads + kGroupHeads - 1) / kGroupHeads);
         const long gd = group_blocks(
